@@ -1,0 +1,233 @@
+#!/usr/bin/env python3
+"""Benchmark of one MoE FFN layer forward on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--m M]
+
+A step is one full layer forward (router, gating + top-k, sort by expert,
+[fp8 activation quantisation,] gate/up + SwiGLU, down, combine) over one batch
+of seeded synthetic tokens whose inputs are already resident in HBM.  The
+expert weights are held in several identical copies that the steps rotate
+through, so every step streams its weights from HBM rather than from the
+256 MB last-level cache.
+
+Prints one JSON line: layer tokens/s (``value``), the layer's GB/s and
+TFLOP/s against the HBM and MFMA peaks, a ``roofline`` entry for the
+dominant kernel (its duration measured with HIP events recorded around it on
+the launch stream), and ``cpu_baseline``: the fp64 CPU oracle timed on the
+host cores on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
+METRIC = "MoE layer tokens/s; prefill TFLOP/s vs MFMA peak; decode GB/s vs HBM peak"
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="decode_bf16")
+    ap.add_argument("--m", type=int, default=None, help="tokens (default: the workload's)")
+    ap.add_argument("--path", default="auto")
+    ap.add_argument("--copies", type=int, default=None,
+                    help="weight copies rotated across steps (default: >= 2 GB in total)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample", type=int, default=None,
+                    help="tokens in the CPU-oracle sample")
+    return ap.parse_args()
+
+
+def esz(dtype):
+    return {"f32": 4, "bf16": 2, "fp8": 1}[dtype]
+
+
+def layer_counts(wl, m, D):
+    """Algorithmic flops and bytes of the layer and of each expert kernel.
+
+    D: number of distinct routed experts that received >= 1 token.
+    Weights of every active expert are read once (codes + fp32 block scales
+    for fp8); x is read once, out written once; the sorted intermediates
+    (h, y) count as the producing and consuming kernels' traffic.
+    """
+    H, E, I, Is, k = wl.hidden, wl.experts, wl.inter, wl.shared_inter, wl.topk
+    te = m * k
+    we = esz(wl.dtype)
+    ae = 4 if wl.dtype == "f32" else 2              # x / out / y element bytes
+    sc = (lambda r, c: (r // 128) * (c // 128) * 4) if wl.dtype == "fp8" else (lambda r, c: 0)
+    w13 = D * (2 * I * H * we + sc(2 * I, H)) + (2 * Is * H * we + sc(2 * Is, H) if Is else 0)
+    w2 = D * (H * I * we + sc(H, I)) + (H * Is * we + sc(H, Is) if Is else 0)
+    hb = we if wl.dtype != "f32" else 4
+    h_bytes = (te * I + m * Is) * hb + ((te * I + m * Is) // 128 * 4 if wl.dtype == "fp8" else 0)
+    x_in = m * H * (1 + 4 / 128 if wl.dtype == "fp8" else ae)
+    y_bytes = (te + (m if Is else 0)) * H * ae
+    flops_gateup = 2 * te * 2 * I * H + 2 * m * 2 * Is * H
+    flops_down = 2 * te * H * I + 2 * m * H * Is
+    flops = 2 * m * E * H + flops_gateup + flops_down
+    bytes_layer = w13 + w2 + E * H * ae + m * H * ae * 2
+    return {
+        "flops": flops, "bytes": bytes_layer,
+        "gateup": {"bytes": w13 + x_in + h_bytes, "flops": flops_gateup},
+        "down": {"bytes": w2 + h_bytes + y_bytes, "flops": flops_down},
+    }
+
+
+def cpu_baseline(wl, inp, m, sample):
+    """Time the fp64 oracle on the host for ``sample`` tokens (median of 3)."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_info
+    import oracle.layer as OL
+
+    def np_of(t):
+        if t is None:
+            return None
+        t = t.detach().cpu().contiguous()
+        if t.dtype == torch.bfloat16:
+            return t.view(torch.int16).numpy().view(np.uint16)
+        return t.numpy()
+
+    spec = OL.LayerSpec(hidden=wl.hidden, experts=wl.experts, topk=wl.topk,
+                        inter=wl.inter, shared_inter=wl.shared_inter, dtype=wl.dtype,
+                        gating=wl.gating, routed_scale=wl.routed_scale, block=wl.block)
+    args = dict(x=np_of(inp["x"]), router_w=np_of(inp["router_w"]),
+                w13=np_of(inp["w13"]), w2=np_of(inp["w2"]),
+                w13_scale=np_of(inp["w13_scale"]), w2_scale=np_of(inp["w2_scale"]),
+                bias=np_of(inp["bias"]))
+    if wl.shared_inter:
+        args["shared"] = {k: np_of(inp["shared_" + k]) for k in
+                          ("w13", "w2", "w13_scale", "w2_scale")}
+    tokens = None if sample >= m else list(range(0, m, max(1, m // sample)))[:sample]
+    times, res = [], None
+    for _ in range(3):
+        t0 = time.perf_counter()
+        res = OL.forward(spec, **args, tokens=tokens)
+        times.append(time.perf_counter() - t0)
+    n = len(res["tokens"])
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return {"value": n / statistics.median(times), "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": (f"{n} of {m} tokens ({'all' if tokens is None else 'strided'}); "
+                       "gating and permutation for all tokens, experts and combine for "
+                       "the sample; fp64 numpy, median of 3 runs")}, res
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (--gpus {args.gpus} requested): "
+              "multi-GPU expert parallelism is not part of this build.", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    import synth
+    from mixture_experts_ffn_06_amd import MoeLayer
+
+    wl = synth.WORKLOADS[args.workload]
+    m = args.m or wl.m
+    dev = torch.device("cuda:0")
+    inp = synth.make_inputs(wl, device=dev, m=m)
+    wbytes = sum(v.numel() * v.element_size() for k, v in inp.items()
+                 if v is not None and k.startswith(("w", "shared")))
+    copies = args.copies or max(1, int(np.ceil(2e9 / wbytes)))
+    names = [k for k in inp if k != "x" and inp[k] is not None]
+    layers = []
+    for c in range(copies):
+        w = {k: (inp[k] if c == 0 else inp[k].clone()) for k in names}
+        layers.append(MoeLayer(w, hidden=wl.hidden, num_experts=wl.experts,
+                               inter=wl.inter, topk=wl.topk, max_tokens=m,
+                               shared_inter=wl.shared_inter, gating=wl.gating,
+                               routed_scale=wl.routed_scale, weight_dtype=wl.dtype,
+                               path=args.path))
+    x = inp["x"]
+    act = torch.float32 if wl.dtype == "f32" else torch.bfloat16
+    out = torch.empty((m, wl.hidden), dtype=act, device=dev)
+    idx = torch.empty((m, wl.topk), dtype=torch.int32, device=dev)
+    tw = torch.empty((m, wl.topk), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i, debug=None):
+        layers[i % copies](x, out=out, topk_idx=idx, topk_w=tw, stream=stream, debug=debug)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    # ---- timed region: exactly K steps ----
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = ev0.elapsed_time(ev1) / args.steps
+    ms_per_step = max(wall * 1e3 / args.steps, gpu_ms)
+
+    # ---- per-stage durations: the same steps with HIP events between stages ----
+    from mixture_experts_ffn_06_amd._lib import NUM_STAGES, STAGES
+    stage_ms = np.zeros(NUM_STAGES)
+    for i in range(args.steps):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(NUM_STAGES + 1)]
+        step(i, debug={"events": evs})
+        torch.cuda.synchronize()
+        stage_ms += np.array([evs[j].elapsed_time(evs[j + 1]) for j in range(NUM_STAGES)])
+    stage_ms /= args.steps
+
+    D = int(torch.unique(idx).numel())
+    cnt = layer_counts(wl, m, D)
+    gb = cnt["bytes"] / (ms_per_step * 1e-3) / 1e9
+    tf = cnt["flops"] / (ms_per_step * 1e-3) / 1e12
+    dom = "gateup"
+    dom_ms = float(stage_ms[STAGES.index(dom)])
+    dom_gbps = cnt[dom]["bytes"] / (dom_ms * 1e-3) / 1e9
+    kernel_names = {"small_m": "sm_gateup_kernel", "grouped": "grouped_kernel<gateup>",
+                    "simple": "simple_gateup_kernel"}
+    path = layers[0].plan.path_for(m)
+    result = {
+        "metric": METRIC, "value": m / (ms_per_step * 1e-3), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
+        "config": {"workload": f"{wl.name}: m={m} H={wl.hidden} E={wl.experts} "
+                               f"k={wl.topk} I={wl.inter} I_s={wl.shared_inter} "
+                               f"{wl.dtype} {wl.gating}",
+                   "path": path, "active_experts": D, "weight_copies": copies,
+                   "launch": "eager"},
+        "layer": {"gbps": gb, "hbm_frac": gb / HBM_PEAK_GBPS, "tflops": tf,
+                  "mfma_frac": tf / MFMA_PEAK_TFLOPS[wl.dtype],
+                  "algorithmic_bytes": cnt["bytes"], "algorithmic_flops": cnt["flops"],
+                  "gpu_ms_per_step": gpu_ms},
+        "stages_us": {s: float(stage_ms[j] * 1e3) for j, s in enumerate(STAGES)},
+        "roofline": {"kernel": kernel_names.get(path, path), "bound": "hbm",
+                     "achieved": dom_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": dom_gbps / HBM_PEAK_GBPS, "traffic": None,
+                     "bytes_per_launch": cnt[dom]["bytes"], "us_per_launch": dom_ms * 1e3},
+    }
+    if not args.no_cpu_baseline:
+        sample = args.cpu_sample or min(m, 64)
+        cb, ref = cpu_baseline(wl, inp, m, sample)
+        result["cpu_baseline"] = cb
+        o = out.float().cpu().numpy().astype(np.float64)[ref["tokens"]]
+        r = ref["out64"]
+        result["parity"] = {"tokens": len(ref["tokens"]),
+                            "rel_l2": float(np.linalg.norm(o - r) / np.linalg.norm(r)),
+                            "topk_idx_equal": float(np.mean(
+                                idx.cpu().numpy() == ref["idx"]))}
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

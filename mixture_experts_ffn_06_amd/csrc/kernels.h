@@ -1,0 +1,97 @@
+// Internal launch interface between the C-ABI layer (moe_api.cpp) and the
+// kernels.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Shape and options of one forward call.
+struct Dims {
+  int m;        // tokens
+  int H;        // hidden
+  int E;        // routed experts
+  int I;        // routed intermediate
+  int Is;       // shared intermediate (0 = none)
+  int k;        // top-k
+  int te;       // m * k
+  int wdt;      // weight storage: kF32 / kBF16 / kFP8
+  int gating;   // 0 softmax, 1 sigmoid
+  int renorm;   // 1: renormalise the selected weights
+  float scale;  // routed scaling factor
+  int bm;       // M tile of the grouped GEMM (rows of one tile)
+};
+
+// Layer inputs (device pointers, caller-owned).
+struct Inputs {
+  const void *x;           // [m,H] f32 or bf16
+  const void *router_w;    // [E,H]
+  const void *w13;         // [E,2I,H]
+  const void *w2;          // [E,H,I]
+  const float *w13_scale;  // [E,2I/128,H/128] (fp8)
+  const float *w2_scale;   // [E,H/128,I/128]  (fp8)
+  const float *bias;       // [E] or null
+  const void *sw13;        // shared [2Is,H]
+  const void *sw2;         // shared [H,Is]
+  const float *sw13_scale; // [2Is/128,H/128]
+  const float *sw2_scale;  // [H/128,Is/128]
+};
+
+// Device regions carved from the caller's workspace.
+struct Work {
+  float *logits;        // [m,E]
+  int *counts;          // [E]
+  int *offsets;         // [E+1]
+  int *sorted_pair;     // [te]
+  int *slot_of_pair;    // [te]
+  int *blk;             // [G,E] per-chunk counts, then chunk bases
+  int *lrank;           // [te] rank of a pair among same-expert pairs of its chunk
+  unsigned *ticket;     // chunks finished (reset to 0 by the last chunk)
+  int2 *tiles;          // [max_tiles] (group, first row) of every M tile
+  int *ntiles;          // [1] number of M tiles
+  int *active;          // [E] experts with >= 1 pair, ascending
+  int *nactive;         // [1]
+  uint8_t *xq;          // [m,H] fp8 codes of x
+  float *sx;            // [m,H/128]
+  void *h;              // [te,I]  routed SwiGLU output (sorted rows)
+  float *h_scale;       // [te,I/128]
+  void *h_sh;           // [m,Is]  shared SwiGLU output
+  float *h_sh_scale;    // [m,Is/128]
+  void *y;              // [te,H]  routed down output (sorted rows)
+  void *y_sh;           // [m,H]   shared down output
+};
+
+// permute.hip
+constexpr int kPermuteChunk = 1024;
+int permute_chunks(int te);
+hipError_t launch_permute(const Dims &d, const int *topk_idx, const Work &w,
+                          int max_tiles, hipStream_t s);
+
+// router.hip
+hipError_t launch_router(const Dims &d, const Inputs &in, const Work &w,
+                         hipStream_t s);
+hipError_t launch_topk(const Dims &d, const Inputs &in, const Work &w,
+                       int *topk_idx, float *topk_w, hipStream_t s);
+
+// quant.hip
+hipError_t launch_quant_x(const Dims &d, const Inputs &in, const Work &w,
+                          hipStream_t s);
+
+// Expert paths: gate/up (+ SwiGLU) and down, routed and shared rows.
+// simple.hip (fp32 VALU, any storage format)
+hipError_t launch_simple_gateup(const Dims &d, const Inputs &in, const Work &w, hipStream_t s);
+hipError_t launch_simple_down(const Dims &d, const Inputs &in, const Work &w, hipStream_t s);
+// grouped.hip (MFMA grouped GEMM, bf16 / fp8)
+hipError_t launch_grouped_gateup(const Dims &d, const Inputs &in, const Work &w, hipStream_t s);
+hipError_t launch_grouped_down(const Dims &d, const Inputs &in, const Work &w, hipStream_t s);
+// small_m.hip (weight streaming for m <= 16, bf16)
+hipError_t launch_small_m_gateup(const Dims &d, const Inputs &in, const Work &w, hipStream_t s);
+hipError_t launch_small_m_down(const Dims &d, const Inputs &in, const Work &w, hipStream_t s);
+
+// combine.hip
+hipError_t launch_combine(const Dims &d, const Work &w, const int *topk_idx,
+                          const float *topk_w, void *out, hipStream_t s);
+
+}  // namespace moe

@@ -131,9 +131,10 @@ def dequant_blocks(codes: np.ndarray, scales: np.ndarray, block: int = 128) -> n
     ``codes [R, C]`` with ``scales [R/block_r, C/block]`` where the row block
     is ``R // scales.shape[0]`` (128 for weights, 1 for activation rows).
     """
-    codes = np.asarray(codes)
+    codes = np.asarray(codes, dtype=np.uint8)
     R, C = codes.shape
     sr, sc = scales.shape
     br, bc = R // sr, C // sc
-    vals = e4m3_decode(codes).reshape(sr, br, sc, bc)
+    table = e4m3_decode(np.arange(256, dtype=np.uint8))   # value of every code
+    vals = table[codes].reshape(sr, br, sc, bc)
     return (vals * np.asarray(scales, np.float64)[:, None, :, None]).reshape(R, C)

@@ -25,6 +25,10 @@ notes of the repository):
 * SwiGLU is ``silu(w1 x) * (w3 x)`` with no clamp; the expert intermediate is
   rounded to the GEMM operand format (bf16, or fp8 per row per 128 columns)
   before the down product;
+* each expert's down output is stored in bf16 before the unpermute and
+  weighted reduce (page 3: the grouped prefill bodies all write the same
+  sorted BF16 ``expert_down_out``), for the shared expert too; the fp32
+  layer keeps it in fp32;
 * the shared expert is added with weight 1 (page 2, ``MoeV41::forward``:
   routed and shared rows are summed into one fp32 accumulator, cleared first);
 * the output is rounded once, from the fp64 sum, to the activation format.
@@ -185,18 +189,27 @@ def round_intermediate(a: np.ndarray, dtype: str, block: int):
     return vals, codes, scales
 
 
+def round_down_output(y: np.ndarray, dtype: str) -> np.ndarray:
+    """Storage of an expert's down output before the combine: bf16 (fp32
+    for the fp32 layer)."""
+    if dtype == "f32":
+        return y.astype(np.float32).astype(np.float64)
+    return bf16_round(y)
+
+
 def expert_mlp(a_rows: np.ndarray, w13: np.ndarray, w2: np.ndarray,
                inter: int, dtype: str, block: int):
     """SwiGLU expert on rows ``a_rows [n, H]`` with exact fp64 weights.
 
     ``w13 [2I, H]`` holds w1 (gate) in rows [0, I) and w3 (up) in [I, 2I);
-    ``w2 [H, I]``.  Returns ``(y [n, H], h values [n, I], h codes, h scales)``.
+    ``w2 [H, I]``.  Returns ``(y [n, H] as stored, h values [n, I], h codes,
+    h scales)``.
     """
     g = a_rows @ w13[:inter].T
     u = a_rows @ w13[inter:].T
     h = silu(g) * u
     hv, hc, hs = round_intermediate(h, dtype, block)
-    return hv @ w2.T, hv, hc, hs
+    return round_down_output(hv @ w2.T, dtype), hv, hc, hs
 
 
 # ------------------------------------------------------------------ all ---

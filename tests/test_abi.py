@@ -1,0 +1,109 @@
+"""The C ABI without a GPU: exports, plan validation and argument checks.
+
+Only calls that fail validation run here -- they return before anything
+touches the GPU (the header guarantees that an error enqueues nothing).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mixture_experts_ffn_06_amd as moe
+from mixture_experts_ffn_06_amd._lib import EXPORTS, MoeConfig, MoeShared, lib
+
+HEADER = os.path.join(os.path.dirname(__file__), "..", "include", "moe.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^[A-Za-z_][\w \*]*?\b(moe_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_library_exports_every_declared_function():
+    names = _declared()
+    assert set(names) == set(EXPORTS)
+    L = lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def _cfg(**kw):
+    base = dict(hidden=256, num_experts=8, inter=128, topk=2, max_tokens=64,
+                shared_inter=0, gating="softmax", weight_dtype="bf16")
+    base.update(kw)
+    return base
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(topk=0), 1), (dict(topk=9), 1), (dict(num_experts=2000, topk=2), 1),
+    (dict(hidden=0), 1), (dict(hidden=100), 2),
+    (dict(weight_dtype="fp8", inter=96), 2), (dict(weight_dtype="fp8", hidden=320), 2),
+    (dict(weight_dtype="fp8", path="small_m"), 2), (dict(weight_dtype="f32", path="grouped"), 2),
+    (dict(weight_dtype="bf16", inter=48), 2),
+])
+def test_plan_rejects_bad_configs(kw, status):
+    with pytest.raises(moe.MoeError) as ei:
+        moe.MoePlan(**_cfg(**kw))
+    assert ei.value.status == status
+
+
+def test_plan_accepts_and_reports_paths_and_workspace():
+    p = moe.MoePlan(**_cfg())
+    assert p.path_for(1) == "small_m" and p.path_for(16) == "small_m"
+    assert p.path_for(17) == "grouped"
+    assert p.workspace_bytes(0) >= 0
+    assert p.workspace_bytes(64) > p.workspace_bytes(8) > 0
+    assert moe.MoePlan(**_cfg(weight_dtype="f32", hidden=64, inter=32)).path_for(4) == "simple"
+    assert moe.MoePlan(**_cfg(weight_dtype="fp8")).path_for(4) == "grouped"
+    assert lib().moe_workspace_bytes(None, 4) == 0
+
+
+FAKE = 1 << 20   # aligned, never dereferenced: validation fails first
+
+
+def _fwd(plan, m=4, ws_bytes=1 << 40, **over):
+    args = dict(x=FAKE, router_w=FAKE, w13=FAKE, w2=FAKE, out=FAKE, topk_idx=FAKE,
+                topk_w=FAKE, workspace=FAKE, shared=None, bias=None,
+                w13_scale=None, w2_scale=None)
+    args.update(over)
+    return plan.forward(args.pop("x"), args.pop("router_w"), args.pop("w13"),
+                        args.pop("w2"), args.pop("out"), args.pop("topk_idx"),
+                        args.pop("topk_w"), args.pop("workspace"), m=m,
+                        stream=0, workspace_bytes=ws_bytes, check=False, **args)
+
+
+def test_forward_validation_errors_return_before_any_launch():
+    p = moe.MoePlan(**_cfg())
+    assert _fwd(p, m=65) == 1                       # m > max_tokens
+    assert _fwd(p, m=-1) == 1
+    assert _fwd(p, x=None) == 1                     # null pointer
+    assert _fwd(p, out=FAKE + 8) == 1               # misaligned
+    assert _fwd(p, workspace=FAKE + 16) == 1        # workspace not 256-aligned
+    assert _fwd(p, ws_bytes=16) == 3                # workspace too small
+    assert _fwd(p, w13_scale=FAKE) == 1             # scales on bf16 weights
+    assert _fwd(p, bias=FAKE) == 2                  # bias with softmax gating
+    assert _fwd(p, shared={"w13": FAKE, "w2": FAKE}) == 1   # plan has no shared expert
+    assert _fwd(p, m=0) == 0                        # empty batch: nothing to do
+    f = moe.MoePlan(**_cfg(weight_dtype="fp8"))
+    assert _fwd(f) == 1                             # fp8 needs scales
+    s = moe.MoePlan(**_cfg(shared_inter=128))
+    assert _fwd(s) == 1                             # shared expert missing
+    assert _fwd(s, shared={"w13": FAKE, "w2": None}) == 1
+    r = lib().moe_forward(None, 4, *([None] * 4), None, 2, *([None] * 7), 0, None)
+    assert r == 1
+
+
+def test_topk_argument_must_match_plan():
+    p = moe.MoePlan(**_cfg())
+    L = lib()
+    st = L.moe_forward(p.handle, 4, FAKE, FAKE, FAKE, FAKE, None, 3, FAKE, FAKE, FAKE,
+                       None, None, None, FAKE, 1 << 40, None)
+    assert st == 1
+
+
+def test_strerror_texts():
+    assert moe.strerror(0) == "ok"
+    assert "workspace" in moe.strerror(3)
+    assert moe.strerror(99) == "unknown status"

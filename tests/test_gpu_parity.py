@@ -1,0 +1,172 @@
+"""GPU parity: the HIP layer (through the C ABI) against the fp64 oracle.
+
+Every workload runs on seeded synthetic inputs; each case prints its name
+before it touches the GPU.  Full-size workloads compare every token where the
+oracle is quick (decode, prefill) and a fixed token sample otherwise (the
+large fp8 shapes); reduced shapes that still span several M tiles, partial N
+tiles and ragged token counts compare every element on every path.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from mixture_experts_ffn_06_amd import MoeLayer
+from tests.conftest import to_np
+from tests.parity import check_layer, debug_buffers
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def make_layer(wl, inp, path="auto", max_tokens=None):
+    w = {k: v for k, v in inp.items() if k != "x" and v is not None}
+    return MoeLayer(w, hidden=wl.hidden, num_experts=wl.experts, inter=wl.inter,
+                    topk=wl.topk, max_tokens=max_tokens or inp["x"].shape[0],
+                    shared_inter=wl.shared_inter, gating=wl.gating,
+                    routed_scale=wl.routed_scale, weight_dtype=wl.dtype, path=path)
+
+
+def run_case(wl, path="auto", m=None, tokens=None, lazy=False, inp=None):
+    _say(f"case {wl.name} m={m or wl.m} path={path} tokens={'all' if tokens is None else len(tokens)}")
+    if inp is None:
+        inp = synth.make_inputs(wl, device=DEV, m=m)
+    mm = inp["x"].shape[0]
+    layer = make_layer(wl, inp, path)
+    if path != "auto":
+        assert layer.plan.path_for(mm) == path
+    dbg = debug_buffers(wl, mm, DEV)
+    out, idx, w = layer(inp["x"], debug=dbg)
+    torch.cuda.synchronize()
+    rep = check_layer(wl, inp, out, idx, w, tokens=tokens, debug=dbg, lazy=lazy)
+    _say(f"  -> {rep}")
+    assert rep.ok(), rep.failures
+    return rep, layer, inp, (out, idx, w, dbg)
+
+
+# ------------------------------------------------------------ workloads ---
+
+def test_tiny_f32():
+    run_case(synth.WORKLOADS["tiny_f32"])
+
+
+@pytest.mark.parametrize("path", ["small_m", "grouped", "simple"])
+@pytest.mark.parametrize("m", [1, 4, 16])
+def test_decode_bf16(m, path):
+    run_case(synth.WORKLOADS["decode_bf16"], path=path, m=m)
+
+
+def test_prefill_bf16_all_tokens():
+    rep, *_ = run_case(synth.WORKLOADS["prefill_bf16"], path="grouped")
+    assert rep.tokens_checked == 1024
+
+
+def _sample(m, n=6, seed=0):
+    rng = np.random.default_rng(seed)
+    return sorted({0, m - 1, *rng.choice(m, size=n, replace=False).tolist()})
+
+
+def test_large_fp8_sampled():
+    wl = synth.WORKLOADS["large_fp8"]
+    run_case(wl, path="grouped", tokens=_sample(wl.m), lazy=True)
+
+
+def test_skew_fp8_sampled():
+    wl = synth.WORKLOADS["skew_fp8"]
+    rep, layer, inp, (out, idx, w, dbg) = run_case(wl, path="grouped",
+                                                    tokens=_sample(wl.m, seed=1), lazy=True)
+    counts = to_np(dbg["counts"])
+    assert int((counts == 0).sum()) == 20
+    assert counts.max() / counts.sum() > 0.10
+
+
+# ------------------------------------------- reduced shapes, all elements ---
+
+RAGGED_FP8 = synth.Workload("ragged_fp8", m=300, hidden=512, experts=16, topk=4,
+                            inter=256, shared_inter=384, dtype="fp8",
+                            gating="sigmoid", routed_scale=2.5, seed=31,
+                            zipf_alpha=0.3, zipf_head=0.2)
+RAGGED_BF16 = synth.Workload("ragged_bf16", m=200, hidden=288, experts=8, topk=3,
+                             inter=96, shared_inter=160, dtype="bf16",
+                             gating="softmax", routed_scale=1.0, seed=32)
+SIGMOID_BF16 = synth.Workload("sigmoid_bf16", m=77, hidden=256, experts=32, topk=6,
+                              inter=128, shared_inter=0, dtype="bf16",
+                              gating="sigmoid", routed_scale=2.5, seed=33,
+                              zipf_alpha=0.2, zipf_head=0.1)
+
+
+@pytest.mark.parametrize("path", ["grouped", "simple"])
+def test_ragged_fp8_all(path):
+    run_case(RAGGED_FP8, path=path)
+
+
+@pytest.mark.parametrize("path", ["grouped", "simple"])
+def test_ragged_bf16_all(path):
+    run_case(RAGGED_BF16, path=path)
+
+
+@pytest.mark.parametrize("m", [1, 7, 13, 16])
+def test_small_m_with_shared_expert(m):
+    run_case(RAGGED_BF16, path="small_m", m=m)
+
+
+@pytest.mark.parametrize("path", ["grouped", "small_m"])
+def test_sigmoid_bias_bf16(path):
+    run_case(SIGMOID_BF16, path=path, m=16 if path == "small_m" else None)
+
+
+def test_k_equals_E():
+    wl = synth.Workload("k_eq_E", m=40, hidden=128, experts=4, topk=4, inter=64,
+                        shared_inter=0, dtype="bf16", gating="softmax",
+                        routed_scale=1.0, seed=34)
+    run_case(wl, path="grouped")
+
+
+def test_one_expert_top1():
+    wl = synth.Workload("one", m=130, hidden=256, experts=1, topk=1, inter=128,
+                        shared_inter=128, dtype="fp8", gating="softmax",
+                        routed_scale=1.0, seed=35)
+    run_case(wl, path="grouped")
+
+
+def test_empty_experts_many_tiles():
+    """Few tokens over many experts: most groups are empty."""
+    wl = synth.Workload("sparse", m=20, hidden=256, experts=256, topk=2, inter=128,
+                        shared_inter=128, dtype="fp8", gating="sigmoid",
+                        routed_scale=1.0, seed=36)
+    rep, *_, (out, idx, w, dbg) = run_case(wl, path="grouped")
+    assert int((to_np(dbg["counts"]) == 0).sum()) >= 256 - 40
+
+
+# ------------------------------------------------------------ behaviour ---
+
+def test_m_zero_is_a_noop():
+    wl = RAGGED_BF16
+    inp = synth.make_inputs(wl, device=DEV)
+    layer = make_layer(wl, inp)
+    out = torch.full((1, wl.hidden), 7.0, dtype=torch.bfloat16, device=DEV)
+    _say("case m=0")
+    layer.plan.forward(inp["x"], inp["router_w"], inp["w13"], inp["w2"], out,
+                       torch.empty(1, wl.topk, dtype=torch.int32, device=DEV),
+                       torch.empty(1, wl.topk, dtype=torch.float32, device=DEV),
+                       layer.workspace, shared=layer.shared, m=0)
+    torch.cuda.synchronize()
+    assert torch.all(out == 7.0)
+
+
+@pytest.mark.parametrize("wl,path", [(RAGGED_FP8, "grouped"), (RAGGED_BF16, "grouped"),
+                                     (RAGGED_BF16, "small_m")])
+def test_repeat_calls_are_bit_identical_on_a_dirty_workspace(wl, path):
+    inp = synth.make_inputs(wl, device=DEV, m=16 if path == "small_m" else None)
+    layer = make_layer(wl, inp, path)
+    _say(f"case determinism {wl.name} {path}")
+    o1, i1, w1 = [t.clone() for t in layer(inp["x"])]
+    layer.workspace.fill_(0xA5)
+    o2, i2, w2 = layer(inp["x"])
+    torch.cuda.synchronize()
+    assert torch.equal(i1, i2) and torch.equal(w1, w2)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))

@@ -199,7 +199,8 @@ def test_one_expert_top1_is_swiglu_mlp():
     x = inp["x"].double()
     w13, w2 = inp["w13"][0].double(), inp["w2"][0].double()
     ref = (torch.nn.functional.silu(x @ w13[:32].T) * (x @ w13[32:].T)) @ w2.T
-    assert np.max(np.abs(r["out64"] - ref.numpy())) < 1e-13
+    # the fp32 layer stores each expert's down output in fp32
+    assert np.max(np.abs(r["out64"] - ref.numpy())) < 1e-6 * np.abs(ref.numpy()).max()
     assert np.all(r["w"] == 1.0)
 
 
@@ -214,7 +215,7 @@ def test_shared_only_contribution_and_unit_weight():
     x = inp["x"].double()
     s13, s2 = inp["shared_w13"].double(), inp["shared_w2"].double()
     ref = (torch.nn.functional.silu(x @ s13[:64].T) * (x @ s13[64:].T)) @ s2.T
-    assert np.max(np.abs(r["out64"] - ref.numpy())) < 1e-13
+    assert np.max(np.abs(r["out64"] - ref.numpy())) < 1e-6 * np.abs(ref.numpy()).max()
 
 
 # ---------------------------------------------------------- symmetries ---
