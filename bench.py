@@ -46,6 +46,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=None,
                     help="tokens in the CPU-oracle sample")
+    ap.add_argument("--copy-mb", type=int, default=0,
+                    help="before the timed region, run one plain device copy of this many MiB "
+                         "(a known-size reference for HBM byte counters)")
     return ap.parse_args()
 
 
@@ -160,6 +163,13 @@ def main():
     def step(i, debug=None):
         layers[i % copies](x, out=out, topk_idx=idx, topk_w=tw, stream=stream, debug=debug)
 
+    if args.copy_mb:
+        src = torch.ones(args.copy_mb << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()

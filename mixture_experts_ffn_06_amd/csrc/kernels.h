@@ -21,7 +21,6 @@ struct Dims {
   int gating;   // 0 softmax, 1 sigmoid
   int renorm;   // 1: renormalise the selected weights
   float scale;  // routed scaling factor
-  int bm;       // M tile of the grouped GEMM (rows of one tile)
 };
 
 // Layer inputs (device pointers, caller-owned).
@@ -46,11 +45,7 @@ struct Work {
   int *offsets;         // [E+1]
   int *sorted_pair;     // [te]
   int *slot_of_pair;    // [te]
-  int *blk;             // [G,E] per-chunk counts, then chunk bases
-  int *lrank;           // [te] rank of a pair among same-expert pairs of its chunk
-  unsigned *ticket;     // chunks finished (reset to 0 by the last chunk)
-  int2 *tiles;          // [max_tiles] (group, first row) of every M tile
-  int *ntiles;          // [1] number of M tiles
+  int *lrank;           // [te] rank of a pair among same-expert pairs of its run
   int *active;          // [E] experts with >= 1 pair, ascending
   int *nactive;         // [1]
   uint8_t *xq;          // [m,H] fp8 codes of x
@@ -64,10 +59,8 @@ struct Work {
 };
 
 // permute.hip
-constexpr int kPermuteChunk = 1024;
-int permute_chunks(int te);
 hipError_t launch_permute(const Dims &d, const int *topk_idx, const Work &w,
-                          int max_tiles, hipStream_t s);
+                          hipStream_t s);
 
 // router.hip
 hipError_t launch_router(const Dims &d, const Inputs &in, const Work &w,

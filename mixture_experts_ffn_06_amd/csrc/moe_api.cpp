@@ -19,7 +19,6 @@
 
 struct moe_plan_s {
   moe_config_t cfg;
-  int bm;          // grouped GEMM M tile
 };
 
 namespace {
@@ -47,13 +46,12 @@ int resolve_path(const moe_config_t &c, int m) {
 // Byte sizes of every workspace region for m tokens.
 struct Layout {
   enum {
-    kLogits, kCounts, kOffsets, kSorted, kSlot, kBlk, kLrank, kTicket, kTiles,
-    kNtiles, kActive, kNactive, kXq, kSx, kH, kHs, kHsh, kHshs, kY, kYsh, kN
+    kLogits, kCounts, kOffsets, kSorted, kSlot, kLrank, kActive, kNactive, kXq,
+    kSx, kH, kHs, kHsh, kHshs, kY, kYsh, kN
   };
   size_t size[kN];
   size_t off[kN];
   size_t total;
-  int max_tiles;
 };
 
 Layout layout(const moe_plan_s &p, int m) {
@@ -63,20 +61,13 @@ Layout layout(const moe_plan_s &p, int m) {
   const bool fp8 = c.weight_dtype == MOE_FP8_E4M3;
   const size_t hb = c.weight_dtype == MOE_F32 ? 4 : (fp8 ? 1 : 2);
   const size_t yb = c.weight_dtype == MOE_F32 ? 4 : 2;
-  const size_t G = moe::permute_chunks(static_cast<int>(te));
   Layout L;
-  L.max_tiles = static_cast<int>((te + p.bm - 1) / p.bm + (te < E ? te : E) +
-                                 (Is > 0 ? (m + p.bm - 1) / p.bm : 0));
   L.size[Layout::kLogits] = m * E * 4;
   L.size[Layout::kCounts] = E * 4;
   L.size[Layout::kOffsets] = (E + 1) * 4;
   L.size[Layout::kSorted] = te * 4;
   L.size[Layout::kSlot] = te * 4;
-  L.size[Layout::kBlk] = G * E * 4;
   L.size[Layout::kLrank] = te * 4;
-  L.size[Layout::kTicket] = 4;
-  L.size[Layout::kTiles] = static_cast<size_t>(L.max_tiles) * 8;
-  L.size[Layout::kNtiles] = 4;
   L.size[Layout::kActive] = E * 4;
   L.size[Layout::kNactive] = 4;
   L.size[Layout::kXq] = fp8 ? m * H : 0;
@@ -105,11 +96,7 @@ moe::Work carve(const Layout &L, void *ws) {
   w.offsets = static_cast<int *>(at(Layout::kOffsets));
   w.sorted_pair = static_cast<int *>(at(Layout::kSorted));
   w.slot_of_pair = static_cast<int *>(at(Layout::kSlot));
-  w.blk = static_cast<int *>(at(Layout::kBlk));
   w.lrank = static_cast<int *>(at(Layout::kLrank));
-  w.ticket = static_cast<unsigned *>(at(Layout::kTicket));
-  w.tiles = static_cast<int2 *>(at(Layout::kTiles));
-  w.ntiles = static_cast<int *>(at(Layout::kNtiles));
   w.active = static_cast<int *>(at(Layout::kActive));
   w.nactive = static_cast<int *>(at(Layout::kNactive));
   w.xq = static_cast<uint8_t *>(at(Layout::kXq));
@@ -186,7 +173,6 @@ int run_forward(moe_plan_t plan, int32_t m, const void *x, const void *router_w,
   d.Is = c.shared_inter; d.k = c.topk; d.te = m * c.topk;
   d.wdt = c.weight_dtype == MOE_F32 ? moe::kF32 : (fp8 ? moe::kFP8 : moe::kBF16);
   d.gating = c.gating; d.renorm = c.renormalize ? 1 : 0; d.scale = c.routed_scale;
-  d.bm = plan->bm;
   moe::Inputs in;
   in.x = x; in.router_w = router_w; in.w13 = w13; in.w2 = w2;
   in.w13_scale = w13_scale; in.w2_scale = w2_scale; in.bias = bias;
@@ -215,7 +201,7 @@ int run_forward(moe_plan_t plan, int32_t m, const void *x, const void *router_w,
   const bool ok =
       stage(MOE_STAGE_ROUTER, "router", [&] { return moe::launch_router(d, in, w, s); }) &&
       stage(MOE_STAGE_TOPK, "topk", [&] { return moe::launch_topk(d, in, w, topk_idx, topk_w, s); }) &&
-      stage(MOE_STAGE_PERMUTE, "permute", [&] { return moe::launch_permute(d, topk_idx, w, L.max_tiles, s); }) &&
+      stage(MOE_STAGE_PERMUTE, "permute", [&] { return moe::launch_permute(d, topk_idx, w, s); }) &&
       stage(MOE_STAGE_QUANT, "quant_x", [&] { return fp8 ? moe::launch_quant_x(d, in, w, s) : hipSuccess; }) &&
       stage(MOE_STAGE_GATEUP, "gate/up", [&] {
         switch (path) {
@@ -270,7 +256,6 @@ int moe_plan(const moe_config_t *cfg, moe_plan_t *plan_out) {
   moe_plan_s *p = new (std::nothrow) moe_plan_s;
   if (!p) return MOE_ERR_INVALID_ARG;
   p->cfg = *cfg;
-  p->bm = 128;
   *plan_out = p;
   return MOE_OK;
 }

@@ -1,5 +1,5 @@
 // Sort (token, slot) pairs by expert: histogram -> exclusive scan -> stable
-// scatter, plus the M-tile list of the grouped GEMM.
+// scatter.
 //
 // forward_prefill.rs (page 3, step 3 "Sort tokens by expert") produces
 // sorted token ids, expert offsets and a token-to-slot map from the top-k
@@ -9,24 +9,22 @@
 // expert's segment is its rank among the earlier pairs (ascending
 // p = t*k + j) with the same expert, so the result is one fixed permutation.
 //
-// One launch.  Every block ranks one chunk of kPermuteChunk pairs: per wave a
-// same-expert lane mask is built from one ballot per expert-id bit, the rank
-// is a popcount of the lower lanes, and per-wave counts are prefix-summed
-// over the chunk's waves in LDS.  The block then publishes its per-expert
-// counts and takes a ticket; the last block to finish scans counts over
-// chunks and experts, scatters every pair, and writes the tile list.
+// One block of 16 waves.  Wave w owns a contiguous run of pairs and walks it
+// 64 pairs at a time: a same-expert lane mask from one ballot per expert-id
+// bit gives each lane its rank among equal experts of lower lanes, and a
+// per-wave running count per expert (LDS, wave-private) turns it into the
+// pair's rank inside the wave's run.  Per-wave counts are then scanned over
+// waves and experts (expert offsets), and a second walk scatters every pair.
+// Everything stays inside one block: no grid-wide hand-off, no atomics.
 #include "common.h"
 #include "kernels.h"
 
 namespace moe {
 
-constexpr int kPermThreads = kPermuteChunk;          // one pair per thread
-constexpr int kPermWaves = kPermThreads / kWave;     // 16
-constexpr int kScanLds = 6144;                       // ints for chunk bases
+constexpr int kPermThreads = 1024;
+constexpr int kPermWaves = kPermThreads / kWave;   // 16
 
-int permute_chunks(int te) { return (te + kPermuteChunk - 1) / kPermuteChunk; }
-
-// Block-wide exclusive scan of one int per thread (1024 threads).
+// Block-wide exclusive scan of one int per thread.
 __device__ int block_exclusive_scan(int v, int *tmp /*[kPermWaves]*/, int *total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int incl = v;
@@ -49,126 +47,101 @@ __device__ int block_exclusive_scan(int v, int *tmp /*[kPermWaves]*/, int *total
   return base + incl - v;
 }
 
-__global__ __launch_bounds__(kPermThreads) void permute_kernel(
-    const int *__restrict__ topk_idx, int te, int E, int G, int bm,
-    int m_shared, int *__restrict__ counts, int *__restrict__ offsets,
-    int *__restrict__ sorted_pair, int *__restrict__ slot_of_pair,
-    int *__restrict__ blk, int *__restrict__ lrank, unsigned *ticket,
-    int2 *__restrict__ tiles, int *__restrict__ ntiles,
-    int *__restrict__ active, int *__restrict__ nactive) {
-  __shared__ uint16_t wcnt[kPermWaves * 1024];   // per-wave counts, E <= 1024
-  __shared__ int scan_tmp[kPermWaves];
-  __shared__ int base_lds[kScanLds];
-  __shared__ int is_last;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-
-  // ---- phase 1: rank pairs inside this chunk ----
-  for (int i = tid; i < kPermWaves * E; i += kPermThreads) wcnt[i] = 0;
-  __syncthreads();
-  const int p = blockIdx.x * kPermuteChunk + tid;
-  const bool valid = p < te;
-  const int e = valid ? topk_idx[p] : 0;
+// Mask of the lanes whose expert equals this lane's (among `valid` lanes).
+__device__ __forceinline__ uint64_t same_expert_mask(int e, bool valid, int E) {
   uint64_t same = __ballot(valid);
   for (int b = 0; (1 << b) < E; ++b) {
     const bool bit = (e >> b) & 1;
     const uint64_t bb = __ballot(valid && bit);
     same &= bit ? bb : ~bb;
   }
-  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  const int rank = __popcll(same & below);
-  const uint64_t above = (lane == 63) ? 0ull : (~0ull << (lane + 1));
-  if (valid && (same & above) == 0) wcnt[wave * E + e] = static_cast<uint16_t>(rank + 1);
+  return same;
+}
+
+__global__ __launch_bounds__(kPermThreads) void permute_kernel(
+    const int *__restrict__ topk_idx, int te, int E,
+    int *__restrict__ counts, int *__restrict__ offsets,
+    int *__restrict__ sorted_pair, int *__restrict__ slot_of_pair,
+    int *__restrict__ lrank, int *__restrict__ active, int *__restrict__ nactive) {
+  extern __shared__ int wcnt[];          // [kPermWaves][E]
+  __shared__ int scan_tmp[kPermWaves];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int i = tid; i < kPermWaves * E; i += kPermThreads) wcnt[i] = 0;
   __syncthreads();
-  for (int x = tid; x < E; x += kPermThreads) {
-    int run = 0;
-    for (int wv = 0; wv < kPermWaves; ++wv) {
-      const int c = wcnt[wv * E + x];
-      wcnt[wv * E + x] = static_cast<uint16_t>(run);
+
+  // ---- pass 1: rank of each pair inside its wave's run ----
+  const int per = (te + kPermWaves * 64 - 1) / (kPermWaves * 64) * 64;
+  const int p0 = wave * per, p1 = min(te, p0 + per);
+  int *mine = wcnt + wave * E;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const uint64_t above = (lane == 63) ? 0ull : (~0ull << (lane + 1));
+  int e_next = (p0 + lane < p1) ? topk_idx[p0 + lane] : 0;
+  for (int base = p0; base < p1; base += 64) {
+    const int p = base + lane;
+    const bool valid = p < p1;
+    const int e = e_next;
+    e_next = (p + 64 < p1) ? topk_idx[p + 64] : 0;   // prefetch the next group
+    const uint64_t same = same_expert_mask(e, valid, E);
+    const int cur = valid ? mine[e] : 0;
+    const int r = cur + __popcll(same & below);
+    if (valid) lrank[p] = r;
+    if (valid && (same & above) == 0) mine[e] = r + 1;   // last lane of its group
+  }
+  __syncthreads();
+
+  // ---- expert totals, offsets, per-wave bases ----
+  constexpr int EPT = 1024 / kPermThreads;   // experts per thread (E <= 1024)
+  (void)EPT;
+  const int x = tid;                          // one expert per thread
+  int tot = 0;
+  if (x < E)
+    for (int w = 0; w < kPermWaves; ++w) tot += wcnt[w * E + x];
+  int all_pairs, all_active;
+  const int off = block_exclusive_scan(x < E ? tot : 0, scan_tmp, &all_pairs);
+  const int aoff = block_exclusive_scan(x < E && tot > 0 ? 1 : 0, scan_tmp, &all_active);
+  if (x < E) {
+    counts[x] = tot;
+    offsets[x] = off;
+    if (tot > 0) active[aoff] = x;
+    int run = off;
+    for (int w = 0; w < kPermWaves; ++w) {
+      const int c = wcnt[w * E + x];
+      wcnt[w * E + x] = run;
       run += c;
     }
-    blk[static_cast<size_t>(blockIdx.x) * E + x] = run;
-  }
-  __syncthreads();
-  if (valid) lrank[p] = wcnt[wave * E + e] + rank;
-
-  // ---- hand-off: the last chunk to finish does the global part ----
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    const unsigned prev = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_ACQ_REL,
-                                                 __HIP_MEMORY_SCOPE_AGENT);
-    is_last = prev == static_cast<unsigned>(G - 1);
-  }
-  __syncthreads();
-  if (!is_last) return;
-  __threadfence();
-
-  // ---- phase 2: per-expert totals, chunk bases (relative), expert scan ----
-  // blk[g][x] <- sum_{g' < g} blk[g'][x]; processed in slabs of chunks so the
-  // loads of one slab are independent.
-  int tot = 0;  // thread x < E: running total of expert x
-  const int slab = kScanLds / E;  // chunks per slab (>= 6 for E <= 1024)
-  for (int g0 = 0; g0 < G; g0 += slab) {
-    const int gn = min(slab, G - g0);
-    for (int i = tid; i < gn * E; i += kPermThreads)
-      base_lds[i] = blk[static_cast<size_t>(g0) * E + i];
-    __syncthreads();
-    for (int x = tid; x < E; x += kPermThreads) {
-      for (int g = 0; g < gn; ++g) {
-        const int c = base_lds[g * E + x];
-        base_lds[g * E + x] = tot;
-        tot += c;
-      }
-    }
-    __syncthreads();
-    for (int i = tid; i < gn * E; i += kPermThreads)
-      blk[static_cast<size_t>(g0) * E + i] = base_lds[i];
-    __syncthreads();
-  }
-  // exclusive scans over experts (E <= 1024: one expert per thread)
-  const int cnt = tid < E ? tot : 0;
-  int all_pairs, all_tiles, all_active;
-  const int off = block_exclusive_scan(cnt, scan_tmp, &all_pairs);
-  const int nt = (cnt + bm - 1) / bm;
-  const int toff = block_exclusive_scan(nt, scan_tmp, &all_tiles);
-  const int aoff = block_exclusive_scan(cnt > 0 ? 1 : 0, scan_tmp, &all_active);
-  if (tid < E) {
-    counts[tid] = cnt;
-    offsets[tid] = off;
-    base_lds[tid] = off;   // reuse: expert offsets for the scatter
-    if (cnt > 0) active[aoff] = tid;
-    for (int i = 0; i < nt; ++i) tiles[toff + i] = make_int2(tid, i * bm);
   }
   if (tid == 0) {
     offsets[E] = all_pairs;
-    const int sh_tiles = (m_shared + bm - 1) / bm;
-    for (int i = 0; i < sh_tiles; ++i) tiles[all_tiles + i] = make_int2(E, i * bm);
-    *ntiles = all_tiles + sh_tiles;
     *nactive = all_active;
   }
   __syncthreads();
-  __threadfence();
 
-  // ---- phase 3: scatter every pair ----
-  for (int q = tid; q < te; q += kPermThreads) {
-    const int eq = topk_idx[q];
-    const int g = q / kPermuteChunk;
-    const int pos = base_lds[eq] + blk[static_cast<size_t>(g) * E + eq] + lrank[q];
-    sorted_pair[pos] = q;
-    slot_of_pair[q] = pos;
+  // ---- pass 2: scatter (each thread rereads the ranks it wrote) ----
+  for (int base = p0; base < p1; base += 64) {
+    const int p = base + lane;
+    if (p < p1) {
+      const int e = topk_idx[p];
+      const int pos = mine[e] + lrank[p];
+      sorted_pair[pos] = p;
+      slot_of_pair[p] = pos;
+    }
   }
-  if (tid == 0) *ticket = 0u;
 }
 
 hipError_t launch_permute(const Dims &d, const int *topk_idx, const Work &w,
-                          int max_tiles, hipStream_t s) {
-  (void)max_tiles;
-  const int G = permute_chunks(d.te);
-  const int m_shared = d.Is > 0 ? d.m : 0;
-  hipLaunchKernelGGL(permute_kernel, dim3(G), dim3(kPermThreads), 0, s,
-                     topk_idx, d.te, d.E, G, d.bm, m_shared, w.counts,
-                     w.offsets, w.sorted_pair, w.slot_of_pair, w.blk, w.lrank,
-                     w.ticket, w.tiles, w.ntiles, w.active, w.nactive);
+                          hipStream_t s) {
+  const size_t lds = static_cast<size_t>(kPermWaves) * d.E * sizeof(int);
+  static bool attr = false;
+  if (!attr) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(permute_kernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       kPermWaves * 1024 * static_cast<int>(sizeof(int)));
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
+  hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(kPermThreads), lds, s, topk_idx,
+                     d.te, d.E, w.counts, w.offsets, w.sorted_pair, w.slot_of_pair,
+                     w.lrank, w.active, w.nactive);
   return hipGetLastError();
 }
 

@@ -47,64 +47,103 @@ __global__ __launch_bounds__(256) void router_valu_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// MFMA router for bf16 and m > 16: a block computes 64 tokens x 64 experts;
-// wave w owns tokens 16w..16w+15 and all four 16-expert column blocks, with
-// operands read straight from global memory (the expert rows are shared by
-// the four waves through L1).  fp32 accumulation, K in 32-wide steps.
+// MFMA router for bf16: a block computes 16*MBW tokens x 16*NBW experts with
+// its four waves splitting H; each wave streams its K range of the token and
+// expert rows straight into MFMA operands (16x16x32 bf16, fp32 accumulate)
+// and the four partial tiles are summed through LDS in a fixed order.  Small
+// tiles keep enough blocks in flight at decode sizes; larger ones cut the
+// re-reads of x and Wr at prefill sizes.
+template <int MBW, int NBW>
 __global__ __launch_bounds__(256) void router_mfma_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ wr,
     float *__restrict__ logits, int m, int E, int H) {
+  __shared__ f32x4_t part[3][MBW * NBW][kWave];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int t0 = blockIdx.y * 64 + wave * 16;
-  const int e0 = blockIdx.x * 64;
-  if (t0 >= m) return;
+  const int t0 = blockIdx.y * 16 * MBW, e0 = blockIdx.x * 16 * NBW;
   const int kofs = (lane >> 4) * 8;
-  const uint16_t *ap = x + static_cast<size_t>(min(t0 + (lane & 15), m - 1)) * H + kofs;
-  const uint16_t *bp[4];
+  const uint16_t *ap[MBW];
+  const uint16_t *bp[NBW];
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb)
-    bp[nb] = wr + static_cast<size_t>(min(e0 + nb * 16 + (lane & 15), E - 1)) * H + kofs;
-  f32x4_t acc[4];
+  for (int i = 0; i < MBW; ++i)
+    ap[i] = x + static_cast<size_t>(min(t0 + 16 * i + (lane & 15), m - 1)) * H + kofs;
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) acc[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-  for (int k = 0; k < H; k += 32) {
-    const bf16x8_t a = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(ap + k));
+  for (int j = 0; j < NBW; ++j)
+    bp[j] = wr + static_cast<size_t>(min(e0 + 16 * j + (lane & 15), E - 1)) * H + kofs;
+  f32x4_t acc[MBW][NBW];
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      const bf16x8_t b = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(bp[nb] + k));
-      acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[nb], 0, 0, 0);
+  for (int i = 0; i < MBW; ++i)
+#pragma unroll
+    for (int j = 0; j < NBW; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const int steps = H / 32;
+  const int s0 = steps * wave / 4, s1 = steps * (wave + 1) / 4;
+  constexpr int BATCH = 4;
+  for (int s = s0; s < s1; s += BATCH) {
+    uint4 av[BATCH][MBW], bv[BATCH][NBW];
+#pragma unroll
+    for (int q = 0; q < BATCH; ++q) {
+      const bool in = s + q < s1;
+      const int o = (s + q) * 32;
+#pragma unroll
+      for (int i = 0; i < MBW; ++i)
+        av[q][i] = in ? *reinterpret_cast<const uint4 *>(ap[i] + o) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int j = 0; j < NBW; ++j)
+        bv[q][j] = in ? *reinterpret_cast<const uint4 *>(bp[j] + o) : make_uint4(0, 0, 0, 0);
     }
+#pragma unroll
+    for (int q = 0; q < BATCH; ++q)
+#pragma unroll
+      for (int i = 0; i < MBW; ++i)
+#pragma unroll
+        for (int j = 0; j < NBW; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8_t, av[q][i]), __builtin_bit_cast(bf16x8_t, bv[q][j]),
+              acc[i][j], 0, 0, 0);
   }
+  if (wave > 0) {
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) {
-    const int e = e0 + nb * 16 + (lane & 15);
+    for (int i = 0; i < MBW; ++i)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = t0 + (lane >> 4) * 4 + i;
-      if (t < m && e < E) logits[static_cast<size_t>(t) * E + e] = acc[nb][i];
+      for (int j = 0; j < NBW; ++j) part[wave - 1][i * NBW + j][lane] = acc[i][j];
+  }
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int i = 0; i < MBW; ++i)
+#pragma unroll
+    for (int j = 0; j < NBW; ++j) {
+      f32x4_t v = acc[i][j];
+#pragma unroll
+      for (int w = 0; w < 3; ++w) v += part[w][i * NBW + j][lane];
+      const int e = e0 + 16 * j + (lane & 15);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = t0 + 16 * i + (lane >> 4) * 4 + r;
+        if (t < m && e < E) logits[static_cast<size_t>(t) * E + e] = v[r];
+      }
     }
-  }
+}
+
+template <int MBW, int NBW>
+static hipError_t launch_router_mfma(const Dims &d, const Inputs &in, const Work &w,
+                                     hipStream_t s) {
+  const dim3 grid((d.E + 16 * NBW - 1) / (16 * NBW), (d.m + 16 * MBW - 1) / (16 * MBW));
+  hipLaunchKernelGGL((router_mfma_kernel<MBW, NBW>), grid, dim3(256), 0, s,
+                     static_cast<const uint16_t *>(in.x),
+                     static_cast<const uint16_t *>(in.router_w), w.logits, d.m, d.E, d.H);
+  return hipGetLastError();
 }
 
 hipError_t launch_router(const Dims &d, const Inputs &in, const Work &w,
                          hipStream_t s) {
-  if (d.wdt != kF32 && d.m > 16) {
-    const dim3 grid((d.E + 63) / 64, (d.m + 63) / 64);
-    hipLaunchKernelGGL(router_mfma_kernel, grid, dim3(256), 0, s,
-                       static_cast<const uint16_t *>(in.x),
-                       static_cast<const uint16_t *>(in.router_w), w.logits,
-                       d.m, d.E, d.H);
-    return hipGetLastError();
+  if (d.wdt != kF32) {
+    if (d.m <= 64) return launch_router_mfma<1, 1>(d, in, w, s);
+    return launch_router_mfma<2, 4>(d, in, w, s);
   }
   dim3 grid((d.E + kRouterWaves - 1) / kRouterWaves,
             (d.m + kRouterTok - 1) / kRouterTok);
-  if (d.wdt == kF32)
-    hipLaunchKernelGGL(router_valu_kernel<kF32>, grid, dim3(256), 0, s, in.x,
-                       in.router_w, w.logits, d.m, d.E, d.H);
-  else
-    hipLaunchKernelGGL(router_valu_kernel<kBF16>, grid, dim3(256), 0, s, in.x,
-                       in.router_w, w.logits, d.m, d.E, d.H);
+  hipLaunchKernelGGL(router_valu_kernel<kF32>, grid, dim3(256), 0, s, in.x,
+                     in.router_w, w.logits, d.m, d.E, d.H);
   return hipGetLastError();
 }
 
@@ -121,13 +160,9 @@ template <int EPL>
 __global__ __launch_bounds__(256) void topk_kernel(
     const float *__restrict__ logits, int m, int E, int k, int gating,
     int renorm, float scale, const float *__restrict__ bias,
-    int *__restrict__ topk_idx, float *__restrict__ topk_w,
-    unsigned *__restrict__ ticket) {
+    int *__restrict__ topk_idx, float *__restrict__ topk_w) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * kTopkWaves + (threadIdx.x >> 6);
-  // The permutation kernel that follows counts finished chunks on `ticket`;
-  // it must start from zero on every call.
-  if (blockIdx.x == 0 && threadIdx.x == 0) *ticket = 0u;
   if (t >= m) return;
   const float *lrow = logits + static_cast<size_t>(t) * E;
   float l[EPL], c[EPL];
@@ -205,7 +240,7 @@ hipError_t launch_topk(const Dims &d, const Inputs &in, const Work &w,
   if (epl <= N) {                                                             \
     hipLaunchKernelGGL(topk_kernel<N>, grid, dim3(256), 0, s, w.logits, d.m,  \
                        d.E, d.k, d.gating, d.renorm, d.scale, in.bias,        \
-                       topk_idx, topk_w, w.ticket);                           \
+                       topk_idx, topk_w);                                     \
     return hipGetLastError();                                                 \
   }
   MOE_TOPK_CASE(1)
