@@ -136,12 +136,15 @@ typedef struct {
  * Errors: MOE_ERR_INVALID_ARG for non-positive sizes, topk outside
  * [1, min(E,32)], E > 1024, unknown enums; MOE_ERR_UNSUPPORTED for fp8 with
  * H, I or I_s not multiples of 128, bf16/fp8 with H, I or I_s not multiples
- * of 32, or SMALL_M forced with fp8/fp32 weights. */
+ * of 32, SMALL_M forced with fp8/fp32 weights, or sizes whose operands
+ * reach 2 GiB (max_tokens * topk * max(H, I, I_s) elements, or one expert's
+ * 2 * max(I, I_s) * H weight elements, at 2 bytes per bf16/fp8 element and 4
+ * per fp32: the expert kernels use 32-bit byte offsets). */
 int moe_plan(const moe_config_t *cfg, moe_plan_t *plan_out);
 
 /* Bytes of device workspace that moe_forward needs for m tokens (0 on a
- * NULL plan).  The workspace holds logits, the permutation, the tile list,
- * quantised activations and the sorted intermediates. */
+ * NULL plan).  The workspace holds logits, the permutation, the list of
+ * experts with rows, quantised activations and the sorted intermediates. */
 size_t moe_workspace_bytes(moe_plan_t plan, int32_t m);
 
 /* Forward of the layer for m tokens (page 2, MoeV41::forward: x, m and a

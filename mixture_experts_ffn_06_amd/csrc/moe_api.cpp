@@ -7,6 +7,7 @@
 //   quantisation] -> experts (gate/up + SwiGLU, down; routed and shared)
 //   -> unpermute + weighted reduce + shared blend.
 // No host synchronisation, no allocation, no host<->device copies.
+#include <algorithm>
 #include <hip/hip_runtime.h>
 
 #include <cstdio>
@@ -130,6 +131,14 @@ int check_cfg(const moe_config_t &c) {
   if (c.weight_dtype == MOE_F32 && c.path != MOE_PATH_AUTO && c.path != MOE_PATH_SIMPLE)
     return MOE_ERR_UNSUPPORTED;
   if (c.path == MOE_PATH_SMALL_M && c.weight_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  // the expert kernels address each operand (token rows, the sorted h / y
+  // rows, one expert's weight matrix) with 32-bit byte offsets
+  const int64_t esz = c.weight_dtype == MOE_F32 ? 4 : 2;
+  const int64_t widest = std::max<int64_t>({c.hidden, c.inter, c.shared_inter});
+  const int64_t lim = int64_t(1) << 31;
+  if (int64_t(c.max_tokens) * c.topk * widest * esz >= lim ||
+      int64_t(2) * std::max(c.inter, c.shared_inter) * c.hidden * esz >= lim)
+    return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
