@@ -41,6 +41,7 @@ struct Inputs {
 // Device regions carved from the caller's workspace.
 struct Work {
   float *logits;        // [m,E]
+  float *rpart;         // [kRouterMaxSplits][m,E] router partial tiles (m <= 16)
   int *counts;          // [E]
   int *offsets;         // [E+1]
   int *sorted_pair;     // [te]
@@ -63,6 +64,14 @@ hipError_t launch_permute(const Dims &d, const int *topk_idx, const Work &w,
                           hipStream_t s);
 
 // router.hip
+// m <= 16 (route_fused_ok): the router writes kRouterMaxSplits-bounded K-split
+// partial tiles to Work::rpart, and one kernel sums them, runs gating + top-k
+// and the sort by expert
+constexpr int kRouterMaxSplits = 8;
+bool route_fused_ok(const Dims &d);
+int router_splits(const Dims &d);
+hipError_t launch_topk_permute(const Dims &d, const Inputs &in, const Work &w, int *topk_idx,
+                               float *topk_w, hipStream_t s);
 hipError_t launch_router(const Dims &d, const Inputs &in, const Work &w,
                          hipStream_t s);
 hipError_t launch_topk(const Dims &d, const Inputs &in, const Work &w,

@@ -47,7 +47,7 @@ int resolve_path(const moe_config_t &c, int m) {
 // Byte sizes of every workspace region for m tokens.
 struct Layout {
   enum {
-    kLogits, kCounts, kOffsets, kSorted, kSlot, kLrank, kActive, kNactive, kXq,
+    kLogits, kRpart, kCounts, kOffsets, kSorted, kSlot, kLrank, kActive, kNactive, kXq,
     kSx, kH, kHs, kHsh, kHshs, kY, kYsh, kN
   };
   size_t size[kN];
@@ -64,6 +64,7 @@ Layout layout(const moe_plan_s &p, int m) {
   const size_t yb = c.weight_dtype == MOE_F32 ? 4 : 2;
   Layout L;
   L.size[Layout::kLogits] = m * E * 4;
+  L.size[Layout::kRpart] = m <= 16 ? static_cast<size_t>(moe::kRouterMaxSplits) * m * E * 4 : 0;
   L.size[Layout::kCounts] = E * 4;
   L.size[Layout::kOffsets] = (E + 1) * 4;
   L.size[Layout::kSorted] = te * 4;
@@ -93,6 +94,7 @@ moe::Work carve(const Layout &L, void *ws) {
   auto at = [&](int i) { return static_cast<void *>(b + L.off[i]); };
   moe::Work w;
   w.logits = static_cast<float *>(at(Layout::kLogits));
+  w.rpart = static_cast<float *>(at(Layout::kRpart));
   w.counts = static_cast<int *>(at(Layout::kCounts));
   w.offsets = static_cast<int *>(at(Layout::kOffsets));
   w.sorted_pair = static_cast<int *>(at(Layout::kSorted));
@@ -201,6 +203,7 @@ int run_forward(moe_plan_t plan, int32_t m, const void *x, const void *router_w,
   };
   hipError_t e;
   const char *what = "";
+  const bool fused = moe::route_fused_ok(d);
   auto stage = [&](int i, const char *name, auto &&launch) -> bool {
     what = name;
     if ((e = mark(i)) != hipSuccess) return false;
@@ -208,9 +211,15 @@ int run_forward(moe_plan_t plan, int32_t m, const void *x, const void *router_w,
     return e == hipSuccess;
   };
   const bool ok =
+      // m <= 16: top-k and sort in one kernel (the permute stage is empty)
       stage(MOE_STAGE_ROUTER, "router", [&] { return moe::launch_router(d, in, w, s); }) &&
-      stage(MOE_STAGE_TOPK, "topk", [&] { return moe::launch_topk(d, in, w, topk_idx, topk_w, s); }) &&
-      stage(MOE_STAGE_PERMUTE, "permute", [&] { return moe::launch_permute(d, topk_idx, w, s); }) &&
+      stage(MOE_STAGE_TOPK, "topk", [&] {
+        return fused ? moe::launch_topk_permute(d, in, w, topk_idx, topk_w, s)
+                     : moe::launch_topk(d, in, w, topk_idx, topk_w, s);
+      }) &&
+      stage(MOE_STAGE_PERMUTE, "permute", [&] {
+        return fused ? hipSuccess : moe::launch_permute(d, topk_idx, w, s);
+      }) &&
       stage(MOE_STAGE_QUANT, "quant_x", [&] { return fp8 ? moe::launch_quant_x(d, in, w, s) : hipSuccess; }) &&
       stage(MOE_STAGE_GATEUP, "gate/up", [&] {
         switch (path) {

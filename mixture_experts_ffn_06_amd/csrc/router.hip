@@ -12,6 +12,7 @@
 // routed scaling factor.
 #include "common.h"
 #include "kernels.h"
+#include "routing.h"
 
 namespace moe {
 
@@ -53,13 +54,17 @@ __global__ __launch_bounds__(256) void router_valu_kernel(
 // and the four partial tiles are summed through LDS in a fixed order.  Small
 // tiles keep enough blocks in flight at decode sizes; larger ones cut the
 // re-reads of x and Wr at prefill sizes.
-template <int MBW, int NBW>
+//
+// With SPLIT (m <= 16 * MBW): blockIdx.y picks one of gridDim.y K ranges and
+// the block writes its partial tile to logits + blockIdx.y * m * E.
+template <int MBW, int NBW, bool SPLIT>
 __global__ __launch_bounds__(256) void router_mfma_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ wr,
     float *__restrict__ logits, int m, int E, int H) {
   __shared__ f32x4_t part[3][MBW * NBW][kWave];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int t0 = blockIdx.y * 16 * MBW, e0 = blockIdx.x * 16 * NBW;
+  const int t0 = SPLIT ? 0 : blockIdx.y * 16 * MBW, e0 = blockIdx.x * 16 * NBW;
+  if (SPLIT) logits += static_cast<size_t>(blockIdx.y) * m * E;
   const int kofs = (lane >> 4) * 8;
   const uint16_t *ap[MBW];
   const uint16_t *bp[NBW];
@@ -75,7 +80,8 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(
 #pragma unroll
     for (int j = 0; j < NBW; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const int steps = H / 32;
-  const int s0 = steps * wave / 4, s1 = steps * (wave + 1) / 4;
+  const int parts = SPLIT ? 4 * gridDim.y : 4, part_id = SPLIT ? 4 * blockIdx.y + wave : wave;
+  const int s0 = steps * part_id / parts, s1 = steps * (part_id + 1) / parts;
   constexpr int BATCH = 4;
   for (int s = s0; s < s1; s += BATCH) {
     uint4 av[BATCH][MBW], bv[BATCH][NBW];
@@ -128,7 +134,7 @@ template <int MBW, int NBW>
 static hipError_t launch_router_mfma(const Dims &d, const Inputs &in, const Work &w,
                                      hipStream_t s) {
   const dim3 grid((d.E + 16 * NBW - 1) / (16 * NBW), (d.m + 16 * MBW - 1) / (16 * MBW));
-  hipLaunchKernelGGL((router_mfma_kernel<MBW, NBW>), grid, dim3(256), 0, s,
+  hipLaunchKernelGGL((router_mfma_kernel<MBW, NBW, false>), grid, dim3(256), 0, s,
                      static_cast<const uint16_t *>(in.x),
                      static_cast<const uint16_t *>(in.router_w), w.logits, d.m, d.E, d.H);
   return hipGetLastError();
@@ -137,6 +143,13 @@ static hipError_t launch_router_mfma(const Dims &d, const Inputs &in, const Work
 hipError_t launch_router(const Dims &d, const Inputs &in, const Work &w,
                          hipStream_t s) {
   if (d.wdt != kF32) {
+    if (route_fused_ok(d)) {   // partial tiles, summed by topk_permute_kernel
+      const dim3 grid((d.E + 15) / 16, router_splits(d));
+      hipLaunchKernelGGL((router_mfma_kernel<1, 1, true>), grid, dim3(256), 0, s,
+                         static_cast<const uint16_t *>(in.x),
+                         static_cast<const uint16_t *>(in.router_w), w.rpart, d.m, d.E, d.H);
+      return hipGetLastError();
+    }
     if (d.m <= 64) return launch_router_mfma<1, 1>(d, in, w, s);
     return launch_router_mfma<2, 4>(d, in, w, s);
   }
@@ -148,88 +161,97 @@ hipError_t launch_router(const Dims &d, const Inputs &in, const Work &w,
 }
 
 // ---------------------------------------------------------------------------
-// Gating + top-k: one wave per token.  Lane l holds experts l, l+64, ...
-// Selection repeats k times: every lane offers its best untaken expert, a
-// butterfly reduction picks the larger score (equal scores: lower index).
-// Softmax ranks by the logit itself (same order as the softmax probability,
-// without its rounding); sigmoid ranks by sigmoid(l) + bias.
+// Decode-sized batches (m <= 16): the router product runs on at least
+// kRouterBlocksTarget blocks (split over K as well as over experts when E is
+// small); blocks write partial tiles.  One block of 16 waves then sums the
+// partials in split order, runs gating + top-k (wave t: token t) and the sort
+// by expert, with the logits and indices handed between the steps in LDS: two
+// launches instead of three.  (One CU pulls only a small share of HBM
+// bandwidth, so the partials that single block reads are kept few.)
+constexpr int kFusedThreads = 1024;
+constexpr int kRouterBlocksTarget = 8;
+
+bool route_fused_ok(const Dims &d) { return d.wdt != kF32 && d.m <= 16; }
+
+int router_splits(const Dims &d) {
+  const int eb = (d.E + 15) / 16;
+  int ks = kRouterBlocksTarget / eb;
+  ks = ks < 1 ? 1 : (ks > kRouterMaxSplits ? kRouterMaxSplits : ks);
+  while (ks > 1 && d.H / 32 < 4 * ks) ks /= 2;   // >= one 32-wide step per wave
+  return ks;
+}
+
+template <int EPL>
+__global__ __launch_bounds__(kFusedThreads) void topk_permute_kernel(Dims d, Inputs in, Work w, int ks,
+                                                                     int *topk_idx, float *topk_w) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  __shared__ int scan_tmp[kPermWaves];
+  const int wave = threadIdx.x >> 6;
+  const int m = d.m, E = d.E;
+  float *lg = reinterpret_cast<float *>(smem);                // [m][E]
+  int *idx_s = reinterpret_cast<int *>(lg + m * E);           // [m * k]
+  int *wcnt = idx_s + ((m * d.k + 3) & ~3);                   // [16][E]
+  // ---- logits: partial tiles summed in split order ----
+  for (int i = threadIdx.x; i < m * E; i += kFusedThreads) {
+    float v = w.rpart[i];
+    for (int q = 1; q < ks; ++q) v += w.rpart[static_cast<size_t>(q) * m * E + i];
+    lg[i] = v;
+    w.logits[i] = v;
+  }
+  __syncthreads();
+  // ---- gating + top-k: wave t takes token t ----
+  if (wave < m)
+    topk_token<EPL>(lg + wave * E, E, d.k, d.gating, d.renorm, d.scale, in.bias,
+                    topk_idx + static_cast<size_t>(wave) * d.k, topk_w + static_cast<size_t>(wave) * d.k,
+                    idx_s + wave * d.k);
+  __syncthreads();
+  // ---- stable sort by expert ----
+  permute_block(idx_s, d.te, E, wcnt, scan_tmp, w.counts, w.offsets, w.sorted_pair, w.slot_of_pair,
+                w.lrank, w.active, w.nactive);
+}
+
+hipError_t launch_topk_permute(const Dims &d, const Inputs &in, const Work &w, int *topk_idx,
+                               float *topk_w, hipStream_t s) {
+  const size_t lds = static_cast<size_t>(d.m) * d.E * 4 + static_cast<size_t>((d.m * d.k + 3) & ~3) * 4 +
+                     static_cast<size_t>(kPermWaves) * d.E * 4;
+  const int epl = (d.E + kWave - 1) / kWave;
+  const int ks = router_splits(d);
+#define MOE_FUSED_CASE(N)                                                                      \
+  if (epl <= N) {                                                                              \
+    static bool attr = false;                                                                  \
+    if (!attr) {                                                                               \
+      const hipError_t e = hipFuncSetAttribute(                                                \
+          reinterpret_cast<const void *>(topk_permute_kernel<N>),                              \
+          hipFuncAttributeMaxDynamicSharedMemorySize, 144 << 10);                              \
+      if (e != hipSuccess) return e;                                                           \
+      attr = true;                                                                             \
+    }                                                                                          \
+    hipLaunchKernelGGL(topk_permute_kernel<N>, dim3(1), dim3(kFusedThreads), lds, s, d, in, w, \
+                       ks, topk_idx, topk_w);                                                  \
+    return hipGetLastError();                                                                  \
+  }
+  MOE_FUSED_CASE(1)
+  MOE_FUSED_CASE(2)
+  MOE_FUSED_CASE(4)
+  MOE_FUSED_CASE(8)
+  MOE_FUSED_CASE(16)
+#undef MOE_FUSED_CASE
+  return hipErrorInvalidValue;
+}
+
+// ---------------------------------------------------------------------------
+// Gating + top-k: one wave per token (topk_token in routing.h).
 constexpr int kTopkWaves = 4;
-constexpr int kMaxEPerLane = 16;  // E <= 1024
 
 template <int EPL>
 __global__ __launch_bounds__(256) void topk_kernel(
     const float *__restrict__ logits, int m, int E, int k, int gating,
     int renorm, float scale, const float *__restrict__ bias,
     int *__restrict__ topk_idx, float *__restrict__ topk_w) {
-  const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * kTopkWaves + (threadIdx.x >> 6);
   if (t >= m) return;
-  const float *lrow = logits + static_cast<size_t>(t) * E;
-  float l[EPL], c[EPL];
-  unsigned taken = 0;
-#pragma unroll
-  for (int i = 0; i < EPL; ++i) {
-    const int e = lane + kWave * i;
-    l[i] = e < E ? lrow[e] : 0.f;
-    if (gating == 0) {
-      c[i] = l[i];
-    } else {
-      c[i] = 1.0f / (1.0f + expf(-l[i]));
-      if (bias) c[i] += e < E ? bias[e] : 0.f;
-    }
-    if (e >= E) taken |= 1u << i;
-  }
-  int my_e = -1;        // lane j < k: expert chosen in round j
-  float my_l = 0.f;     // its logit
-  for (int j = 0; j < k; ++j) {
-    float bv = -INFINITY;
-    int be = 0x7fffffff;
-    float bl = 0.f;
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-      if (!(taken & (1u << i))) {
-        const int e = lane + kWave * i;
-        if (c[i] > bv || (c[i] == bv && e < be)) { bv = c[i]; be = e; bl = l[i]; }
-      }
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float ov = __shfl_xor(bv, o);
-      const int oe = __shfl_xor(be, o);
-      const float ol = __shfl_xor(bl, o);
-      if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; bl = ol; }
-    }
-    if ((be & 63) == lane) taken |= 1u << (be >> 6);
-    if (lane == j) { my_e = be; my_l = bl; }
-  }
-  // Gate weights of the selected experts.
-  float wj = 0.f;
-  if (gating == 0) {
-    const float l0 = __shfl(my_l, 0);  // largest selected logit
-    if (renorm) {
-      const float ex = lane < k ? expf(my_l - l0) : 0.f;
-      wj = ex / wave_sum(ex);
-    } else {
-      float lmax = -INFINITY;
-#pragma unroll
-      for (int i = 0; i < EPL; ++i)
-        if (lane + kWave * i < E) lmax = fmaxf(lmax, l[i]);
-      lmax = wave_max(lmax);
-      float z = 0.f;
-#pragma unroll
-      for (int i = 0; i < EPL; ++i)
-        if (lane + kWave * i < E) z += expf(l[i] - lmax);
-      z = wave_sum(z);
-      wj = expf(my_l - lmax) / z;
-    }
-  } else {
-    const float sj = lane < k ? 1.0f / (1.0f + expf(-my_l)) : 0.f;
-    wj = renorm ? sj / wave_sum(sj) : sj;
-  }
-  if (lane < k) {
-    topk_idx[static_cast<size_t>(t) * k + lane] = my_e;
-    topk_w[static_cast<size_t>(t) * k + lane] = wj * scale;
-  }
+  topk_token<EPL>(logits + static_cast<size_t>(t) * E, E, k, gating, renorm, scale, bias,
+                  topk_idx + static_cast<size_t>(t) * k, topk_w + static_cast<size_t>(t) * k, nullptr);
 }
 
 hipError_t launch_topk(const Dims &d, const Inputs &in, const Work &w,

@@ -1,0 +1,201 @@
+// Gating + top-k and the stable sort by expert as device functions, shared by
+// their own kernels and by the fused single-block routing kernel.
+#pragma once
+#include "common.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------------------
+// Gating + top-k of one token by one wave (router.hip describes the gating).
+// Lane l holds experts l, l+64, ...  Selection repeats k times: every lane
+// offers its best untaken expert, a butterfly reduction picks the larger
+// score (equal scores: lower index).  Softmax ranks by the logit itself (same
+// order as the softmax probability, without its rounding); sigmoid ranks by
+// sigmoid(l) + bias.  lrow may point to global memory or LDS; idx_copy, if
+// not null, receives the k indices as well.
+constexpr int kMaxEPerLane = 16;  // E <= 1024
+
+template <int EPL>
+__device__ __forceinline__ void topk_token(const float *lrow, int E, int k, int gating,
+                                           int renorm, float scale, const float *bias,
+                                           int *idx_out, float *w_out, int *idx_copy) {
+  const int lane = threadIdx.x & 63;
+  float l[EPL], c[EPL];
+  unsigned taken = 0;
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int e = lane + kWave * i;
+    l[i] = e < E ? lrow[e] : 0.f;
+    if (gating == 0) {
+      c[i] = l[i];
+    } else {
+      c[i] = 1.0f / (1.0f + expf(-l[i]));
+      if (bias) c[i] += e < E ? bias[e] : 0.f;
+    }
+    if (e >= E) taken |= 1u << i;
+  }
+  int my_e = -1;        // lane j < k: expert chosen in round j
+  float my_l = 0.f;     // its logit
+  for (int j = 0; j < k; ++j) {
+    float bv = -INFINITY;
+    int be = 0x7fffffff;
+    float bl = 0.f;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      if (!(taken & (1u << i))) {
+        const int e = lane + kWave * i;
+        if (c[i] > bv || (c[i] == bv && e < be)) { bv = c[i]; be = e; bl = l[i]; }
+      }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const float ov = __shfl_xor(bv, o);
+      const int oe = __shfl_xor(be, o);
+      const float ol = __shfl_xor(bl, o);
+      if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; bl = ol; }
+    }
+    if ((be & 63) == lane) taken |= 1u << (be >> 6);
+    if (lane == j) { my_e = be; my_l = bl; }
+  }
+  // Gate weights of the selected experts.
+  float wj = 0.f;
+  if (gating == 0) {
+    const float l0 = __shfl(my_l, 0);  // largest selected logit
+    if (renorm) {
+      const float ex = lane < k ? expf(my_l - l0) : 0.f;
+      wj = ex / wave_sum(ex);
+    } else {
+      float lmax = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < EPL; ++i)
+        if (lane + kWave * i < E) lmax = fmaxf(lmax, l[i]);
+      lmax = wave_max(lmax);
+      float z = 0.f;
+#pragma unroll
+      for (int i = 0; i < EPL; ++i)
+        if (lane + kWave * i < E) z += expf(l[i] - lmax);
+      z = wave_sum(z);
+      wj = expf(my_l - lmax) / z;
+    }
+  } else {
+    const float sj = lane < k ? 1.0f / (1.0f + expf(-my_l)) : 0.f;
+    wj = renorm ? sj / wave_sum(sj) : sj;
+  }
+  if (lane < k) {
+    idx_out[lane] = my_e;
+    w_out[lane] = wj * scale;
+    if (idx_copy) idx_copy[lane] = my_e;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Stable sort of the te = m*k (token, slot) pairs by expert (permute.hip
+// describes the method) by one block of kPermThreads threads.  topk_idx may
+// point to global memory or LDS; wcnt is LDS of kPermWaves * E ints and
+// scan_tmp LDS of kPermWaves ints.
+constexpr int kPermThreads = 1024;
+constexpr int kPermWaves = kPermThreads / kWave;   // 16
+
+// Block-wide exclusive scan of one int per thread.
+__device__ __forceinline__ int block_exclusive_scan(int v, int *tmp /*[kPermWaves]*/, int *total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(incl, o);
+    if (lane >= o) incl += u;
+  }
+  if (lane == 63) tmp[wave] = incl;
+  __syncthreads();
+  int base = 0, all = 0;
+#pragma unroll
+  for (int i = 0; i < kPermWaves; ++i) {
+    const int c = tmp[i];
+    base += i < wave ? c : 0;
+    all += c;
+  }
+  __syncthreads();
+  *total = all;
+  return base + incl - v;
+}
+
+// Mask of the lanes whose expert equals this lane's (among `valid` lanes).
+__device__ __forceinline__ uint64_t same_expert_mask(int e, bool valid, int E) {
+  uint64_t same = __ballot(valid);
+  for (int b = 0; (1 << b) < E; ++b) {
+    const bool bit = (e >> b) & 1;
+    const uint64_t bb = __ballot(valid && bit);
+    same &= bit ? bb : ~bb;
+  }
+  return same;
+}
+
+__device__ __forceinline__ void permute_block(
+    const int *topk_idx, int te, int E, int *wcnt, int *scan_tmp,
+    int *__restrict__ counts, int *__restrict__ offsets,
+    int *__restrict__ sorted_pair, int *__restrict__ slot_of_pair,
+    int *__restrict__ lrank, int *__restrict__ active, int *__restrict__ nactive) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int i = tid; i < kPermWaves * E; i += kPermThreads) wcnt[i] = 0;
+  __syncthreads();
+
+  // ---- pass 1: rank of each pair inside its wave's run ----
+  const int per = (te + kPermWaves * 64 - 1) / (kPermWaves * 64) * 64;
+  const int p0 = wave * per, p1 = min(te, p0 + per);
+  int *mine = wcnt + wave * E;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const uint64_t above = (lane == 63) ? 0ull : (~0ull << (lane + 1));
+  int e_next = (p0 + lane < p1) ? topk_idx[p0 + lane] : 0;
+  for (int base = p0; base < p1; base += 64) {
+    const int p = base + lane;
+    const bool valid = p < p1;
+    const int e = e_next;
+    e_next = (p + 64 < p1) ? topk_idx[p + 64] : 0;   // prefetch the next group
+    const uint64_t same = same_expert_mask(e, valid, E);
+    const int cur = valid ? mine[e] : 0;
+    const int r = cur + __popcll(same & below);
+    if (valid) lrank[p] = r;
+    if (valid && (same & above) == 0) mine[e] = r + 1;   // last lane of its group
+  }
+  __syncthreads();
+
+  // ---- expert totals, offsets, per-wave bases ----
+  constexpr int EPT = 1024 / kPermThreads;   // experts per thread (E <= 1024)
+  (void)EPT;
+  const int x = tid;                          // one expert per thread
+  int tot = 0;
+  if (x < E)
+    for (int w = 0; w < kPermWaves; ++w) tot += wcnt[w * E + x];
+  int all_pairs, all_active;
+  const int off = block_exclusive_scan(x < E ? tot : 0, scan_tmp, &all_pairs);
+  const int aoff = block_exclusive_scan(x < E && tot > 0 ? 1 : 0, scan_tmp, &all_active);
+  if (x < E) {
+    counts[x] = tot;
+    offsets[x] = off;
+    if (tot > 0) active[aoff] = x;
+    int run = off;
+    for (int w = 0; w < kPermWaves; ++w) {
+      const int c = wcnt[w * E + x];
+      wcnt[w * E + x] = run;
+      run += c;
+    }
+  }
+  if (tid == 0) {
+    offsets[E] = all_pairs;
+    *nactive = all_active;
+  }
+  __syncthreads();
+
+  // ---- pass 2: scatter (each thread rereads the ranks it wrote) ----
+  for (int base = p0; base < p1; base += 64) {
+    const int p = base + lane;
+    if (p < p1) {
+      const int e = topk_idx[p];
+      const int pos = mine[e] + lrank[p];
+      sorted_pair[pos] = p;
+      slot_of_pair[p] = pos;
+    }
+  }
+}
+
+}  // namespace moe

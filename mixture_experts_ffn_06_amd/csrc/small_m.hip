@@ -7,161 +7,305 @@
 // selected experts; forward_layer.rs, page 4: one dispatch covers all
 // selected experts of a decode step).
 //
-// gate/up: block = (active expert d, 16 h columns).  Its four waves split H;
-// each wave streams the 16 w1 rows and the 16 matching w3 rows of its K range
-// straight into MFMA B registers (16 B per lane, all loads of a batch in
-// flight together), with the expert's <= 16 token rows as the M side of a
-// 16x16x32 bf16 MFMA.  The four partial sums meet in LDS, and wave 0 forms
-// SiLU(g) * u and writes the bf16 h rows.
-// down: block = (active expert d, 16 output columns), the same split-K
-// scheme over I, writing bf16 y rows.  A shared expert is one more slot
-// (after the active routed experts) whose rows are the m tokens.
+// Work item = (slot, column group): a slot is a routed expert with >= 1 row
+// (or the shared expert, whose rows are the m tokens); a column group is
+// NBLK weight blocks of 16 rows (gate/up: NBLK/2 blocks of w1 and the
+// matching NBLK/2 of w3; down: NBLK blocks of w2).  One wave (or KS waves
+// splitting K, their partial sums met in LDS) owns an item.
+//
+// HBM efficiency decides this kernel, and the MFMA operand layout (a load
+// instruction touching 16 weight rows, 64 bytes each) streams markedly slower
+// than row-contiguous loads.  So the weights move in stages of RUN bytes per
+// row: each direct global->LDS load covers 1024/RUN whole rows of RUN
+// contiguous bytes, into a per-wave ring of DEPTH stages, and the MFMA B
+// fragments are read back from LDS (16-byte pieces XOR-swizzled per row so
+// those reads are bank-conflict free).  The slot's <= 16 token rows (A, read
+// from L2) go straight to registers, one stage ahead like the weights.  The
+// grid is sized so that every item is resident at once.
 #include "common.h"
 #include "kernels.h"
+#include "lds.h"
 
 namespace moe {
 
-constexpr int kSmWaves = 4;
-constexpr int kSmBatch = 8;   // K steps (of 32) whose loads are issued together
+constexpr int kSmBlockWaves = 4;
 
-// Partial product of one wave over K steps [s0, s1): acc += A . B^T for one
-// 16x16 block.  a_row / b_row point at the lane's row, K offset included.
-__device__ __forceinline__ void sm_stream(const uint16_t *a_row, bool a_ok,
-                                          const uint16_t *b_row0,
-                                          const uint16_t *b_row1, int s0,
-                                          int s1, f32x4_t &acc0, f32x4_t &acc1) {
-  for (int s = s0; s < s1; s += kSmBatch) {
-    uint4 av[kSmBatch], bv0[kSmBatch], bv1[kSmBatch];
-#pragma unroll
-    for (int i = 0; i < kSmBatch; ++i) {
-      const bool in = s + i < s1;
-      const int o = (s + i) * 32;
-      bv0[i] = in ? *reinterpret_cast<const uint4 *>(b_row0 + o) : make_uint4(0, 0, 0, 0);
-      if (b_row1) bv1[i] = in ? *reinterpret_cast<const uint4 *>(b_row1 + o) : make_uint4(0, 0, 0, 0);
-      av[i] = (in && a_ok) ? *reinterpret_cast<const uint4 *>(a_row + o) : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < kSmBatch; ++i) {
-      const bf16x8_t a = __builtin_bit_cast(bf16x8_t, av[i]);
-      acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8_t, bv0[i]), acc0, 0, 0, 0);
-      if (b_row1)
-        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8_t, bv1[i]), acc1, 0, 0, 0);
-    }
-  }
-}
+enum : int { kSmGateUp = 0, kSmDown = 1 };
 
-// One slot of the small-m grid: a routed expert with >= 1 row, or the shared
-// expert.  Returns false for slots past the last one.
-struct SmSlot {
-  bool shared;
-  int e, seg0, rows, inter;
+template <int NBLK, int RUN, int DEPTH>
+struct SmCfg {
+  static constexpr int NPR = RUN / 16;            // 16-byte pieces per row per stage
+  static constexpr int RPI = 64 / NPR;            // rows per load instruction
+  static constexpr int NI = NBLK * 16 / RPI;      // load instructions per stage
+  static constexpr int SSTEPS = RUN / 64;         // 32-wide bf16 MFMA steps per stage
+  static constexpr int STAGE = NBLK * 16 * RUN;   // bytes per stage
+  static constexpr int WAVE_LDS = DEPTH * STAGE;
+  static constexpr int LDS = kSmBlockWaves * WAVE_LDS;
+  static_assert(RUN == 64 || RUN == 128 || RUN == 256, "swizzle covers 64- to 256-byte runs");
+  static_assert(DEPTH == 2, "one stage in flight");
+  static_assert(NI + SSTEPS < 64, "vmcnt range");
+  static_assert(WAVE_LDS >= NBLK * kWave * 16, "partial sums fit the ring");
 };
 
-__device__ __forceinline__ bool sm_slot(const Dims &d, const Work &w, int slot, SmSlot &o) {
-  const int na = *w.nactive;
-  if (slot < na) {
-    o.shared = false;
-    o.e = w.active[slot];
-    o.seg0 = w.offsets[o.e];
-    o.rows = w.offsets[o.e + 1] - o.seg0;   // <= m <= 16
-    o.inter = d.I;
-    return true;
-  }
-  if (slot == na && d.Is > 0) {
-    o.shared = true;
-    o.e = d.E;
-    o.seg0 = 0;
-    o.rows = d.m;
-    o.inter = d.Is;
-    return true;
-  }
-  return false;
+// Position of logical 16-byte piece p of row r inside the row's run: the
+// 16 rows of a block read the same logical piece in one MFMA step, and the
+// XOR puts them in 16 distinct 16-byte bank groups of each 256-byte window.
+template <int RUN>
+__device__ __forceinline__ int sm_swz(int p, int r) {
+  return p ^ ((r / (256 / RUN)) % (RUN / 16));
 }
 
-__global__ __launch_bounds__(256) void sm_gateup_kernel(Dims d, Inputs in, Work w) {
-  __shared__ f32x4_t part[kSmWaves][2][kWave];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  SmSlot sl;
-  if (!sm_slot(d, w, blockIdx.x, sl)) return;
-  const int c0 = blockIdx.y * 16;
-  if (c0 >= sl.inter) return;
-  const int seg0 = sl.seg0, rows = sl.rows;
-  const int r = lane & 15;
-  const int kofs = (lane >> 4) * 8;
-  const bool a_ok = r < rows;
-  const int tok = !a_ok ? 0 : (sl.shared ? r : w.sorted_pair[seg0 + r] / d.k);
-  const uint16_t *a_row = static_cast<const uint16_t *>(in.x) + static_cast<size_t>(tok) * d.H + kofs;
-  const uint16_t *W = sl.shared ? static_cast<const uint16_t *>(in.sw13)
-                                : static_cast<const uint16_t *>(in.w13) + static_cast<size_t>(sl.e) * 2 * d.I * d.H;
-  const uint16_t *bg = W + static_cast<size_t>(c0 + r) * d.H + kofs;
-  const uint16_t *bu = W + static_cast<size_t>(sl.inter + c0 + r) * d.H + kofs;
-  const int steps = d.H / 32;
-  const int s0 = steps * wave / kSmWaves, s1 = steps * (wave + 1) / kSmWaves;
-  f32x4_t g = {0.f, 0.f, 0.f, 0.f}, u = {0.f, 0.f, 0.f, 0.f};
-  sm_stream(a_row, a_ok, bg, bu, s0, s1, g, u);
-  part[wave][0][lane] = g;
-  part[wave][1][lane] = u;
-  __syncthreads();
-  if (wave != 0) return;
+template <int MODE, int NBLK, int RUN, int DEPTH>
+__global__ __launch_bounds__(kSmBlockWaves * kWave) void sm_kernel(Dims d, Inputs in, Work w, int ks) {
+  using C = SmCfg<NBLK, RUN, DEPTH>;
+  constexpr int CW = MODE == kSmGateUp ? 16 * NBLK / 2 : 16 * NBLK;   // output columns per item
+  extern __shared__ __align__(1024) uint8_t lds[];
+  const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6);
+  uint8_t *ring = lds + wave * C::WAVE_LDS;
+  const int item = uniform(blockIdx.x * (kSmBlockWaves / ks) + wave / ks);
+  const int kp = uniform(wave % ks);
+
+  // ---- the item: slot and column group ----
+  const int na = uniform(*w.nactive);
+  const int ncol_r = MODE == kSmGateUp ? d.I : d.H;
+  const int ipr = (ncol_r + CW - 1) / CW;                  // items per routed slot
+  const int ips = d.Is > 0 ? ((MODE == kSmGateUp ? d.Is : d.H) + CW - 1) / CW : 0;
+  const bool live = item < na * ipr + ips;
+
+  f32x4_t acc[NBLK];
 #pragma unroll
-  for (int wv = 1; wv < kSmWaves; ++wv) {
-    g += part[wv][0][lane];
-    u += part[wv][1][lane];
+  for (int j = 0; j < NBLK; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  int seg0 = 0, rows = 0, inter = 0, c0 = 0, ncol = 0;
+  bool shared = false;
+  if (live) {
+    int e, cg;
+    if (item < na * ipr) {
+      const int slot = item / ipr;
+      cg = item - slot * ipr;
+      e = uniform(w.active[slot]);
+      seg0 = uniform(w.offsets[e]);
+      rows = uniform(w.offsets[e + 1]) - seg0;   // <= m <= 16
+      inter = d.I;
+    } else {
+      shared = true;
+      e = d.E;
+      cg = item - na * ipr;
+      rows = d.m;
+      inter = d.Is;
+    }
+    c0 = cg * CW;
+    ncol = MODE == kSmGateUp ? inter : d.H;
+    const int K = MODE == kSmGateUp ? d.H : inter;
+    const int kbytes = K * 2;
+
+    // Operand bases (wave-uniform) and 32-bit byte offsets from them (the
+    // plan keeps every operand below 2 GiB).
+    const int r = lane & 15;
+    const int ar = min(r, rows - 1);   // rows past the slot's end repeat its last row
+    const uint8_t *Ab, *Wb;
+    uint32_t aoff;
+    if (MODE == kSmGateUp) {
+      const int tok = shared ? ar : w.sorted_pair[seg0 + ar] / d.k;
+      Ab = static_cast<const uint8_t *>(in.x);
+      aoff = static_cast<uint32_t>(tok) * kbytes;
+      Wb = shared ? static_cast<const uint8_t *>(in.sw13)
+                  : static_cast<const uint8_t *>(in.w13) + static_cast<size_t>(e) * 2 * d.I * d.H * 2;
+    } else {
+      Ab = static_cast<const uint8_t *>(shared ? w.h_sh : w.h);
+      aoff = static_cast<uint32_t>(seg0 + ar) * kbytes;
+      Wb = shared ? static_cast<const uint8_t *>(in.sw2)
+                  : static_cast<const uint8_t *>(in.w2) + static_cast<size_t>(e) * d.H * d.I * 2;
+    }
+    aoff += (lane >> 4) * 16;   // the lane's 8 K elements of each step
+    // First weight row of block j (blocks past the last column read row 0
+    // and store nothing).
+    auto wrow = [&](int j) -> int {
+      if (MODE == kSmGateUp) {
+        const int c = c0 + 16 * (j % (NBLK / 2));
+        return c < ncol ? (j < NBLK / 2 ? c : inter + c) : 0;
+      }
+      const int c = c0 + 16 * j;
+      return c < ncol ? c : 0;
+    };
+    // Load instruction q covers block q / (16/RPI), rows (q % (16/RPI)) * RPI
+    // + lane / NPR; the lane fetches logical piece sm_swz(lane % NPR, row) of
+    // its row, so LDS position lane % NPR holds that piece.
+    uint32_t qoff[C::NI];
+#pragma unroll
+    for (int q = 0; q < C::NI; ++q) {
+      const int j = q / (16 / C::RPI);
+      const int row = (q % (16 / C::RPI)) * C::RPI + lane / C::NPR;
+      qoff[q] = static_cast<uint32_t>(wrow(j) + row) * kbytes + sm_swz<RUN>(lane % C::NPR, row) * 16;
+    }
+
+    // ---- K range of this wave, in stages of RUN bytes per row ----
+    const int nst_all = kbytes / RUN;
+    const int st0 = uniform(nst_all * kp / ks), st1 = uniform(nst_all * (kp + 1) / ks);
+    uint4 aA[C::SSTEPS], aB[C::SSTEPS];
+    // Loads of stage st into ring slot sl (K bytes are a multiple of RUN:
+    // every stage is whole).
+    auto issue = [&](int st, int sl, uint4 (&A)[C::SSTEPS]) {
+      const uint32_t kb = static_cast<uint32_t>(st) * RUN;
+      uint8_t *slot = ring + sl * C::STAGE;
+#pragma unroll
+      for (int q = 0; q < C::NI; ++q) dma16_to_lds(Wb + (qoff[q] + kb), slot + q * 1024);
+#pragma unroll
+      for (int i = 0; i < C::SSTEPS; ++i) A[i] = *reinterpret_cast<const uint4 *>(Ab + (aoff + kb) + i * 64);
+    };
+    // lane reads row r, logical piece 4 i + lane / 16 of step i
+    const int g = lane >> 4;
+    auto compute = [&](int st, int sl, const uint4 (&A)[C::SSTEPS]) {
+      const uint8_t *slot = ring + sl * C::STAGE;
+#pragma unroll
+      for (int i = 0; i < C::SSTEPS; ++i) {
+        const uint32_t rb = lds_off(slot + r * RUN + sm_swz<RUN>(4 * i + g, r) * 16);
+        u32x4_t b[NBLK];
+        if constexpr (NBLK == 2) {
+          lds_read2<0, 16 * RUN>(rb, rb, b[0], b[1]);
+        } else {
+          static_assert(NBLK == 4, "2 or 4 blocks");
+          lds_read4<0, 16 * RUN, 32 * RUN, 48 * RUN>(rb, rb, rb, rb, b[0], b[1], b[2], b[3]);
+        }
+        const bf16x8_t a = __builtin_bit_cast(bf16x8_t, A[i]);
+#pragma unroll
+        for (int j = 0; j < NBLK; ++j)
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8_t, b[j]), acc[j], 0, 0, 0);
+      }
+    };
+    // Ring of two slots, walked two stages per iteration so that each
+    // register buffer has a fixed slot; every wait counts exactly the LPS
+    // operations of the stage issued after the one it waits for.  The
+    // issue after the last stage repeats it into the idle slot (never read).
+    constexpr int LPS = C::NI + C::SSTEPS;   // vector-memory ops per stage
+    const int n = st1 - st0;
+    if (n > 0) {
+      issue(st0, 0, aA);
+      int st = st0;
+      for (int p = 0; p < n / 2; ++p, st += 2) {
+        issue(st + 1, 1, aB);
+        wait_vm<LPS>();
+        compute(st, 0, aA);
+        issue(min(st + 2, st1 - 1), 0, aA);
+        wait_vm<LPS>();
+        compute(st + 1, 1, aB);
+      }
+      wait_vm<0>();
+      if (n & 1) compute(st, 0, aA);
+    }
   }
-  uint16_t *h = static_cast<uint16_t *>(sl.shared ? w.h_sh : w.h) + static_cast<size_t>(seg0) * sl.inter;
+
+  // ---- partial sums of the KS waves of an item meet in LDS (each wave's
+  // own ring: all of its loads have landed) ----
+  if (ks > 1) {
+    f32x4_t *part = reinterpret_cast<f32x4_t *>(ring);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = (lane >> 4) * 4 + i;
-    if (row < rows) h[static_cast<size_t>(row) * sl.inter + c0 + (lane & 15)] = f32_to_bf16(silu(g[i]) * u[i]);
+    for (int j = 0; j < NBLK; ++j) part[j * kWave + lane] = acc[j];
+    __syncthreads();
+    if (kp != 0) return;
+    for (int q = 1; q < ks; ++q) {
+      const f32x4_t *other = reinterpret_cast<const f32x4_t *>(lds + (wave + q) * C::WAVE_LDS);
+#pragma unroll
+      for (int j = 0; j < NBLK; ++j) acc[j] += other[j * kWave + lane];
+    }
+  }
+  if (!live) return;
+
+  // ---- epilogue: lane holds rows 4*(lane/16) + i, column lane % 16 ----
+  const int cl = lane & 15;
+  if (MODE == kSmGateUp) {
+    uint16_t *h = static_cast<uint16_t *>(shared ? w.h_sh : w.h) + static_cast<size_t>(seg0) * inter;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = (lane >> 4) * 4 + i;
+      if (row < rows) {
+#pragma unroll
+        for (int j = 0; j < NBLK / 2; ++j)
+          if (c0 + 16 * j < ncol)
+            h[static_cast<size_t>(row) * inter + c0 + 16 * j + cl] =
+                f32_to_bf16(silu(acc[j][i]) * acc[j + NBLK / 2][i]);
+      }
+    }
+  } else {
+    uint16_t *y = static_cast<uint16_t *>(shared ? w.y_sh : w.y) + static_cast<size_t>(seg0) * d.H;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = (lane >> 4) * 4 + i;
+      if (row < rows) {
+#pragma unroll
+        for (int j = 0; j < NBLK; ++j)
+          if (c0 + 16 * j < ncol)
+            y[static_cast<size_t>(row) * d.H + c0 + 16 * j + cl] = f32_to_bf16(acc[j][i]);
+      }
+    }
   }
 }
 
-__global__ __launch_bounds__(256) void sm_down_kernel(Dims d, Inputs in, Work w) {
-  __shared__ f32x4_t part[kSmWaves][kWave];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  SmSlot sl;
-  if (!sm_slot(d, w, blockIdx.x, sl)) return;
-  const int seg0 = sl.seg0, rows = sl.rows, K = sl.inter;
-  const int n0 = blockIdx.y * 16;
-  const int r = lane & 15;
-  const int kofs = (lane >> 4) * 8;
-  const bool a_ok = r < rows;
-  const uint16_t *a_row = static_cast<const uint16_t *>(sl.shared ? w.h_sh : w.h) +
-                          static_cast<size_t>(seg0 + (a_ok ? r : 0)) * K + kofs;
-  const uint16_t *b = (sl.shared ? static_cast<const uint16_t *>(in.sw2)
-                                 : static_cast<const uint16_t *>(in.w2) + static_cast<size_t>(sl.e) * d.H * d.I) +
-                      static_cast<size_t>(n0 + r) * K + kofs;
-  const int steps = K / 32;
-  const int s0 = steps * wave / kSmWaves, s1 = steps * (wave + 1) / kSmWaves;
-  f32x4_t acc = {0.f, 0.f, 0.f, 0.f}, unused = {0.f, 0.f, 0.f, 0.f};
-  sm_stream(a_row, a_ok, b, nullptr, s0, s1, acc, unused);
-  part[wave][lane] = acc;
-  __syncthreads();
-  if (wave != 0) return;
-#pragma unroll
-  for (int wv = 1; wv < kSmWaves; ++wv) acc += part[wv][lane];
-  uint16_t *y = static_cast<uint16_t *>(sl.shared ? w.y_sh : w.y) + static_cast<size_t>(seg0) * d.H;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = (lane >> 4) * 4 + i;
-    if (row < rows) y[static_cast<size_t>(row) * d.H + n0 + (lane & 15)] = f32_to_bf16(acc[i]);
+static int sm_cus() {
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      cus = 256;
   }
+  return cus;
 }
 
-// H, I multiples of 32 and m <= 16 are checked by the caller.
-static int sm_slots(const Dims &d) { return (d.te < d.E ? d.te : d.E) + (d.Is > 0 ? 1 : 0); }
+// Grid for the largest possible item count (the number of slots is only
+// known on the device: items past it exit at once).  KS, the waves per
+// item, is the largest of 1, 2, 4 that keeps every item resident at once.
+template <int MODE, int NBLK, int RUN, int DEPTH>
+static hipError_t sm_launch(const Dims &d, const Inputs &in, const Work &w, hipStream_t s) {
+  using C = SmCfg<NBLK, RUN, DEPTH>;
+  constexpr int CW = MODE == kSmGateUp ? 16 * NBLK / 2 : 16 * NBLK;
+  auto kern = sm_kernel<MODE, NBLK, RUN, DEPTH>;
+  static int blocks_per_cu = 0;
+  if (blocks_per_cu == 0) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
+    if (e != hipSuccess) return e;
+    int nb = 0;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kern, kSmBlockWaves * kWave, C::LDS);
+    if (e != hipSuccess) return e;
+    if (nb < 1) return hipErrorInvalidConfiguration;
+    blocks_per_cu = nb;
+  }
+  const int slots = d.te < d.E ? d.te : d.E;
+  const int ncol_r = MODE == kSmGateUp ? d.I : d.H;
+  const int ipr = (ncol_r + CW - 1) / CW;
+  const int ips = d.Is > 0 ? ((MODE == kSmGateUp ? d.Is : d.H) + CW - 1) / CW : 0;
+  const long items = static_cast<long>(slots) * ipr + ips;
+  const long cap = static_cast<long>(sm_cus()) * blocks_per_cu * kSmBlockWaves;
+  int ks = 1;
+  while (ks < kSmBlockWaves && items * ks * 2 <= cap) ks *= 2;
+  const long per_block = kSmBlockWaves / ks;
+  const long grid = (items + per_block - 1) / per_block;
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(kSmBlockWaves * kWave), C::LDS, s,
+                     d, in, w, ks);
+  return hipGetLastError();
+}
+
+// H, I multiples of 32 and m <= 16 are checked by the caller.  A stage moves
+// RUN contiguous bytes of each row: 256 when K is a multiple of 128 (longer
+// runs stream faster), else 128 or 64.
+template <int MODE, int NBLK>
+static hipError_t sm_dispatch(const Dims &d, const Inputs &in, const Work &w, hipStream_t s, int kgcd) {
+  if (kgcd % 128 == 0) return sm_launch<MODE, NBLK, 256, 2>(d, in, w, s);
+  if (kgcd % 64 == 0) return sm_launch<MODE, NBLK, 128, 2>(d, in, w, s);
+  return sm_launch<MODE, NBLK, 64, 2>(d, in, w, s);
+}
 
 hipError_t launch_small_m_gateup(const Dims &d, const Inputs &in, const Work &w,
                                  hipStream_t s) {
-  const int imax = d.Is > d.I ? d.Is : d.I;
-  hipLaunchKernelGGL(sm_gateup_kernel, dim3(sm_slots(d), imax / 16), dim3(256), 0, s, d, in, w);
-  return hipGetLastError();
+  return sm_dispatch<kSmGateUp, 2>(d, in, w, s, d.H);   // 16 h columns per item
 }
 
 hipError_t launch_small_m_down(const Dims &d, const Inputs &in, const Work &w,
                                hipStream_t s) {
-  hipLaunchKernelGGL(sm_down_kernel, dim3(sm_slots(d), d.H / 16), dim3(256), 0, s, d, in, w);
-  return hipGetLastError();
+  // K is I for routed slots and I_s for the shared one: stages fit both
+  const int kg = d.Is > 0 ? (d.I % 128 == 0 && d.Is % 128 == 0 ? 128 : (d.I % 64 == 0 && d.Is % 64 == 0 ? 64 : 32))
+                          : d.I;
+  return sm_dispatch<kSmDown, 2>(d, in, w, s, kg);      // 32 output columns per item
 }
 
 }  // namespace moe
