@@ -13,8 +13,10 @@ through, so every step streams its weights from HBM rather than from the
 Prints one JSON line: layer tokens/s (``value``), the layer's GB/s and
 TFLOP/s against the HBM and MFMA peaks, a ``roofline`` entry for the
 dominant kernel (its duration measured with HIP events recorded around it on
-the launch stream), and ``cpu_baseline``: the fp64 CPU oracle timed on the
-host cores on a bounded sample of the same workload.
+the launch stream inside the timed steps; its HBM traffic from the rocprofv3
+byte counters recorded in profiles/hbm_traffic.json, null once the kernel's
+sources differ from the ones counted), and ``cpu_baseline``: the fp64 CPU
+oracle timed on the host cores on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -46,6 +48,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=None,
                     help="tokens in the CPU-oracle sample")
+    ap.add_argument("--kernel-events", choices=("timed", "off"), default="timed",
+                    help="timed: record HIP events around the dominant kernel inside the timed "
+                         "steps (its duration for the roofline); off: time it in a separate loop")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="before the timed region, run one plain device copy of this many MiB "
                          "(a known-size reference for HBM byte counters)")
@@ -54,6 +59,33 @@ def parse():
 
 def esz(dtype):
     return {"f32": 4, "bf16": 2, "fp8": 1}[dtype]
+
+
+# Source files of each expert-kernel family: HBM byte counters recorded in
+# profiles/hbm_traffic.json stand only while these files are unchanged.
+KERNEL_SOURCES = {"small_m": ("small_m.hip", "lds.h", "common.h", "kernels.h"),
+                  "grouped": ("grouped.hip", "lds.h", "common.h", "kernels.h")}
+
+
+def recorded_traffic(workload, m, stage, path):
+    """HBM bytes per launch (read + write) of a kernel, from the rocprofv3
+    FETCH_SIZE / WRITE_SIZE runs summarised in profiles/, or None when there is
+    no record for it or its sources changed since the counters were taken."""
+    import hashlib
+    files = KERNEL_SOURCES.get(path)
+    rec_path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    if not files or not os.path.exists(rec_path):
+        return None
+    rec = json.load(open(rec_path)).get(f"{workload}|m={m}|{stage}")
+    if rec is None:
+        return None
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "mixture_experts_ffn_06_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    if h.hexdigest() != rec["source_sha256"]:
+        return None
+    return rec["read_bytes"] + rec["write_bytes"]
 
 
 def layer_counts(wl, m, D):
@@ -170,8 +202,23 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    from mixture_experts_ffn_06_amd._lib import NUM_STAGES, STAGES, _event_handle
+    dom = "gateup"
+    di = STAGES.index(dom)
+
+    def dom_events():
+        """Events recorded by the library on the launch stream just before the
+        dominant kernel and just before the next stage."""
+        evs = [None] * (NUM_STAGES + 1)
+        evs[di] = torch.cuda.Event(enable_timing=True)
+        evs[di + 1] = torch.cuda.Event(enable_timing=True)
+        for ev in (evs[di], evs[di + 1]):
+            _event_handle(ev)          # create the HIP events outside the timed region
+        return evs
+
     for i in range(args.warmup):
         step(i)
+    kev = [dom_events() for _ in range(args.steps)] if args.kernel_events == "timed" else None
     torch.cuda.synchronize()
     # ---- timed region: exactly K steps ----
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -179,15 +226,16 @@ def main():
     t0 = time.perf_counter()
     ev0.record(stream)
     for i in range(args.steps):
-        step(i)
+        step(i, debug=None if kev is None else {"events": kev[i]})
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     gpu_ms = ev0.elapsed_time(ev1) / args.steps
     ms_per_step = max(wall * 1e3 / args.steps, gpu_ms)
+    dom_timed_ms = (float(np.mean([e[di].elapsed_time(e[di + 1]) for e in kev]))
+                    if kev is not None else None)
 
     # ---- per-stage durations: the same steps with HIP events between stages ----
-    from mixture_experts_ffn_06_amd._lib import NUM_STAGES, STAGES
     stage_ms = np.zeros(NUM_STAGES)
     for i in range(args.steps):
         evs = [torch.cuda.Event(enable_timing=True) for _ in range(NUM_STAGES + 1)]
@@ -200,8 +248,7 @@ def main():
     cnt = layer_counts(wl, m, D)
     gb = cnt["bytes"] / (ms_per_step * 1e-3) / 1e9
     tf = cnt["flops"] / (ms_per_step * 1e-3) / 1e12
-    dom = "gateup"
-    dom_ms = float(stage_ms[STAGES.index(dom)])
+    dom_ms = dom_timed_ms if dom_timed_ms is not None else float(stage_ms[di])
     dom_gbps = cnt[dom]["bytes"] / (dom_ms * 1e-3) / 1e9
     kernel_names = {"small_m": "sm_gateup_kernel", "grouped": "grouped_kernel<gateup>",
                     "simple": "simple_gateup_kernel"}
@@ -223,7 +270,9 @@ def main():
         "stages_us": {s: float(stage_ms[j] * 1e3) for j, s in enumerate(STAGES)},
         "roofline": {"kernel": kernel_names.get(path, path), "bound": "hbm",
                      "achieved": dom_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": dom_gbps / HBM_PEAK_GBPS, "traffic": None,
+                     "frac": dom_gbps / HBM_PEAK_GBPS,
+                     "traffic": recorded_traffic(wl.name, m, dom, path),
+                     "traffic_unit": "HBM bytes per launch, read + written (rocprofv3 counters)",
                      "bytes_per_launch": cnt[dom]["bytes"], "us_per_launch": dom_ms * 1e3},
     }
     if not args.no_cpu_baseline:
