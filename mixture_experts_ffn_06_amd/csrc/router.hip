@@ -186,6 +186,7 @@ __global__ __launch_bounds__(kFusedThreads) void topk_permute_kernel(Dims d, Inp
                                                                      int *topk_idx, float *topk_w) {
   extern __shared__ __align__(16) uint8_t smem[];
   __shared__ int scan_tmp[kPermWaves];
+  __shared__ uint32_t sk[kFusedThreads / kWave][kTopkScratch];
   const int wave = threadIdx.x >> 6;
   const int m = d.m, E = d.E;
   float *lg = reinterpret_cast<float *>(smem);                // [m][E]
@@ -203,7 +204,7 @@ __global__ __launch_bounds__(kFusedThreads) void topk_permute_kernel(Dims d, Inp
   if (wave < m)
     topk_token<EPL>(lg + wave * E, E, d.k, d.gating, d.renorm, d.scale, in.bias,
                     topk_idx + static_cast<size_t>(wave) * d.k, topk_w + static_cast<size_t>(wave) * d.k,
-                    idx_s + wave * d.k);
+                    idx_s + wave * d.k, sk[wave]);
   __syncthreads();
   // ---- stable sort by expert ----
   permute_block(idx_s, d.te, E, wcnt, scan_tmp, w.counts, w.offsets, w.sorted_pair, w.slot_of_pair,
@@ -248,10 +249,12 @@ __global__ __launch_bounds__(256) void topk_kernel(
     const float *__restrict__ logits, int m, int E, int k, int gating,
     int renorm, float scale, const float *__restrict__ bias,
     int *__restrict__ topk_idx, float *__restrict__ topk_w) {
+  __shared__ uint32_t sk[kTopkWaves][kTopkScratch];
   const int t = blockIdx.x * kTopkWaves + (threadIdx.x >> 6);
   if (t >= m) return;
   topk_token<EPL>(logits + static_cast<size_t>(t) * E, E, k, gating, renorm, scale, bias,
-                  topk_idx + static_cast<size_t>(t) * k, topk_w + static_cast<size_t>(t) * k, nullptr);
+                  topk_idx + static_cast<size_t>(t) * k, topk_w + static_cast<size_t>(t) * k, nullptr,
+                  sk[threadIdx.x >> 6]);
 }
 
 hipError_t launch_topk(const Dims &d, const Inputs &in, const Work &w,

@@ -7,56 +7,104 @@ namespace moe {
 
 // ---------------------------------------------------------------------------
 // Gating + top-k of one token by one wave (router.hip describes the gating).
-// Lane l holds experts l, l+64, ...  Selection repeats k times: every lane
-// offers its best untaken expert, a butterfly reduction picks the larger
-// score (equal scores: lower index).  Softmax ranks by the logit itself (same
+// Lane l holds experts l, l+64, ...  Softmax ranks by the logit itself (same
 // order as the softmax probability, without its rounding); sigmoid ranks by
-// sigmoid(l) + bias.  lrow may point to global memory or LDS; idx_copy, if
-// not null, receives the k indices as well.
+// sigmoid(l) + bias.  Equal scores: lower expert index first.
+//
+// Selection without cross-lane shuffles: scores become order-preserving
+// 32-bit keys, and the k-th largest key T is found bit by bit from the top
+// (keep a bit if at least k keys reach the prefix; each count is a ballot
+// and a popcount).  Keys above T are selected, then keys equal to T in
+// ascending expert order until k are taken.  The k selected (key, expert,
+// logit) go to LDS; lane j < k counts the selected entries that precede its
+// own (larger key, or equal key and lower index), which is its output
+// position, and the entries are re-read in that order.
+//
+// lrow may point to global memory or LDS; sk is LDS of kTopkScratch words
+// owned by the wave; idx_copy, if not null, receives the k indices too.
 constexpr int kMaxEPerLane = 16;  // E <= 1024
+constexpr int kTopkScratch = 3 * 32;
+
+// Unsigned key with the order of the float (-0 taken as +0, so equal scores
+// stay equal and fall back to the index order).
+__device__ __forceinline__ uint32_t order_key(float f) {
+  const uint32_t u = __float_as_uint(f + 0.0f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
 
 template <int EPL>
 __device__ __forceinline__ void topk_token(const float *lrow, int E, int k, int gating,
                                            int renorm, float scale, const float *bias,
-                                           int *idx_out, float *w_out, int *idx_copy) {
+                                           int *idx_out, float *w_out, int *idx_copy,
+                                           uint32_t *sk) {
   const int lane = threadIdx.x & 63;
-  float l[EPL], c[EPL];
-  unsigned taken = 0;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  float l[EPL];
+  uint32_t key[EPL];
+  bool valid[EPL];
 #pragma unroll
   for (int i = 0; i < EPL; ++i) {
     const int e = lane + kWave * i;
-    l[i] = e < E ? lrow[e] : 0.f;
-    if (gating == 0) {
-      c[i] = l[i];
-    } else {
-      c[i] = 1.0f / (1.0f + expf(-l[i]));
-      if (bias) c[i] += e < E ? bias[e] : 0.f;
+    valid[i] = e < E;
+    l[i] = valid[i] ? lrow[e] : 0.f;
+    float c = l[i];
+    if (gating != 0) {
+      c = 1.0f / (1.0f + expf(-l[i]));
+      if (bias) c += valid[i] ? bias[e] : 0.f;
     }
-    if (e >= E) taken |= 1u << i;
+    key[i] = valid[i] ? order_key(c) : 0u;
   }
-  int my_e = -1;        // lane j < k: expert chosen in round j
-  float my_l = 0.f;     // its logit
-  for (int j = 0; j < k; ++j) {
-    float bv = -INFINITY;
-    int be = 0x7fffffff;
-    float bl = 0.f;
+  // T = the largest value with at least k keys >= T (the k-th largest key)
+  uint32_t T = 0;
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t t = T | (1u << b);
+    int cnt = 0;
 #pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-      if (!(taken & (1u << i))) {
-        const int e = lane + kWave * i;
-        if (c[i] > bv || (c[i] == bv && e < be)) { bv = c[i]; be = e; bl = l[i]; }
-      }
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float ov = __shfl_xor(bv, o);
-      const int oe = __shfl_xor(be, o);
-      const float ol = __shfl_xor(bl, o);
-      if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; bl = ol; }
-    }
-    if ((be & 63) == lane) taken |= 1u << (be >> 6);
-    if (lane == j) { my_e = be; my_l = bl; }
+    for (int i = 0; i < EPL; ++i) cnt += __popcll(__ballot(valid[i] && key[i] >= t));
+    if (cnt >= k) T = t;
   }
+  int need = k;
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) need -= __popcll(__ballot(valid[i] && key[i] > T));
+  // selection, then compaction into LDS in ascending expert order
+  int base = 0;
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const uint64_t eq = __ballot(valid[i] && key[i] == T);
+    const bool take_eq = ((eq >> lane) & 1ull) && __popcll(eq & below) < need;
+    need -= min(need, __popcll(eq));
+    const bool sel = (valid[i] && key[i] > T) || take_eq;
+    const uint64_t sm = __ballot(sel);
+    if (sel) {
+      const int pos = base + __popcll(sm & below);
+      sk[pos] = key[i];
+      sk[32 + pos] = static_cast<uint32_t>(lane + kWave * i);
+      sk[64 + pos] = __float_as_uint(l[i]);
+    }
+    base += __popcll(sm);
+  }
+  __builtin_amdgcn_wave_barrier();
+  // output position of entry j = number of entries ranked before it
+  uint32_t my_key = 0, my_idx = 0, my_lbits = 0;
+  int rank = 0;
+  if (lane < k) {
+    my_key = sk[lane];
+    my_idx = sk[32 + lane];
+    my_lbits = sk[64 + lane];
+    for (int j = 0; j < k; ++j) {
+      const uint32_t ok = sk[j], oi = sk[32 + j];
+      rank += (ok > my_key || (ok == my_key && oi < my_idx)) ? 1 : 0;
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+  if (lane < k) {
+    sk[rank] = my_idx;
+    sk[32 + rank] = my_lbits;
+  }
+  __builtin_amdgcn_wave_barrier();
+  // lane j < k: expert chosen j-th, and its logit
+  const int my_e = lane < k ? static_cast<int>(sk[lane]) : -1;
+  const float my_l = lane < k ? __uint_as_float(sk[32 + lane]) : 0.f;
   // Gate weights of the selected experts.
   float wj = 0.f;
   if (gating == 0) {
@@ -68,12 +116,12 @@ __device__ __forceinline__ void topk_token(const float *lrow, int E, int k, int 
       float lmax = -INFINITY;
 #pragma unroll
       for (int i = 0; i < EPL; ++i)
-        if (lane + kWave * i < E) lmax = fmaxf(lmax, l[i]);
+        if (valid[i]) lmax = fmaxf(lmax, l[i]);
       lmax = wave_max(lmax);
       float z = 0.f;
 #pragma unroll
       for (int i = 0; i < EPL; ++i)
-        if (lane + kWave * i < E) z += expf(l[i] - lmax);
+        if (valid[i]) z += expf(l[i] - lmax);
       z = wave_sum(z);
       wj = expf(my_l - lmax) / z;
     }
