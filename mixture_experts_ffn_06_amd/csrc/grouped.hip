@@ -44,10 +44,11 @@ __device__ __forceinline__ i32x8_t as_i32x8(u32x4_t a, u32x4_t b) {
 }
 
 // Tile geometry.  WM x WN waves; a wave owns MBW 16-row m-blocks and NB
-// 16-row weight blocks.  K advances in stages of STAGE_K elements (bf16: MFMA
-// steps of 32; fp8: one 16x16x128 step = one scale block).  A "step block" is
-// 16 rows x one MFMA step of K (bf16 1 KB, fp8 2 KB), moved by one (bf16) or
-// two (fp8, 8 rows each) 1 KB load instructions.
+// 16-row weight blocks.  K advances in stages of STAGE_K elements = 128 bytes
+// of every row (bf16: two MFMA steps of 32; fp8: one 16x16x128 step = one
+// scale block).  A "stage block" is 16 rows x 128 bytes, moved by two 1 KB
+// load instructions of 8 whole 128-byte row runs each (row-contiguous runs
+// stream from HBM faster than the 64-byte pieces of the MFMA layout).
 template <int DT, int MODE, int NB, int WN, int WM, int MBW, int DEPTH, int STAGE_K>
 struct GCfg {
   static constexpr int NW = WN * WM;
@@ -57,14 +58,14 @@ struct GCfg {
   static constexpr int ESZ = DT == kBF16 ? 2 : 1;
   static constexpr int KSTEP = DT == kBF16 ? 32 : 128;
   static constexpr int SK = STAGE_K;                  // K elements per stage
-  static constexpr int STEPS = STAGE_K / KSTEP;
-  static constexpr int BV = DT == kBF16 ? 1 : 2;      // 1 KB chunks per step block
-  static constexpr int RB = KSTEP * ESZ;              // bytes of a row in one step
-  static constexpr int CPR = RB / 16;                 // 16-byte pieces per such row
-  static constexpr int RPI = 16 / BV;                 // rows per load instruction
-  static constexpr int SWZ_DIV = 16 / CPR;
-  static constexpr int A_CH = MB * STEPS * BV;        // chunks per stage: A ...
-  static constexpr int B_CH = WN * NB * STEPS * BV;   // ... and B
+  static constexpr int STEPS = STAGE_K / KSTEP;     // MFMA steps per stage
+  static constexpr int RB = STAGE_K * ESZ;            // bytes of a row in one stage
+  static constexpr int BV = 16 * RB / 1024;           // 1 KB chunks per 16-row block
+  static constexpr int CPR = RB / 16;                 // 16-byte pieces per row
+  static constexpr int RPI = 1024 / RB;               // rows per load instruction
+  static constexpr int SWZ_DIV = 256 / RB;            // rows per 256-byte bank window
+  static constexpr int A_CH = MB * BV;                // chunks per stage: A ...
+  static constexpr int B_CH = WN * NB * BV;           // ... and B
   static constexpr int CPW = (A_CH + B_CH) / NW;      // chunks loaded per wave
   static constexpr bool SCALED = DT == kFP8;
   static constexpr int LPS = CPW + (SCALED ? 1 : 0);  // loads per stage per wave
@@ -80,6 +81,7 @@ struct GCfg {
   static constexpr int WCOLS = MODE == kGateUp ? 16 * NB / 2 : 16 * NB;
   static constexpr int NCOLS = WN * WCOLS;
   static_assert(STAGE_K % KSTEP == 0, "stage = whole MFMA steps");
+  static_assert(RB == 128, "stage rows of 128 bytes (swizzle, chunk and read layout)");
   static_assert((A_CH + B_CH) % NW == 0, "chunks spread evenly over the waves");
   static_assert(LPS * (DEPTH - 1) < 64, "vmcnt range");
   static_assert(!SCALED || (ROW_WAVES < NW && WN * NB <= 64), "fp8 scale areas");
@@ -229,23 +231,23 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void grouped_kernel(GroupedArgs a)
     };
 
     // ---- this wave's share of every stage's chunks ----
-    // Chunk c < A_CH: A step block (mb, s), instruction i; otherwise B step
-    // block (cg, j, s), instruction i.  dst = c * 1 KB in the stage.  The
-    // lane's source is (c < A_CH ? Ab : Wb) + coff[q] + the stage's K offset.
+    // Chunk c < A_CH: A stage block mb, instruction i; otherwise B stage
+    // block (cg, j), instruction i.  dst = c * 1 KB in the stage.  The lane's
+    // source is (c < A_CH ? Ab : Wb) + coff[q] + the stage's K offset.
     uint32_t coff[C::CPW];
+    int cpc[DT == kBF16 ? C::CPW : 1];   // bf16: the lane's piece offset inside the stage
 #pragma unroll
     for (int q = 0; q < C::CPW; ++q) {
       const int c = wave * C::CPW + q;
       const int i = c % C::BV;
-      const int rl = i * C::RPI + lrow;               // row inside the step block
+      const int rl = i * C::RPI + lrow;               // row inside the stage block
       const int pc = (lpiece ^ swz(rl)) * 16;         // this lane's piece, swizzled
+      if constexpr (DT == kBF16) cpc[q] = pc;
       if (c < C::A_CH) {
-        const int s = (c / C::BV) % C::STEPS, mb = c / (C::BV * C::STEPS);
-        coff[q] = a_off(mb * 16 + rl) + pc + s * C::RB;
+        coff[q] = a_off((c / C::BV) * 16 + rl) + pc;
       } else {
-        const int cb = c - C::A_CH;
-        const int s = (cb / C::BV) % C::STEPS, blk = cb / (C::BV * C::STEPS);
-        coff[q] = static_cast<uint32_t>(wrow_of(blk / NB, blk % NB) + rl) * kbytes + pc + s * C::RB;
+        const int blk = (c - C::A_CH) / C::BV;
+        coff[q] = static_cast<uint32_t>(wrow_of(blk / NB, blk % NB) + rl) * kbytes + pc;
       }
     }
     // fp8 scales: waves < ROW_WAVES fetch row scales (lane l: row 64w + l),
@@ -277,11 +279,12 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void grouped_kernel(GroupedArgs a)
       for (int q = 0; q < C::CPW; ++q) {
         const int c = wave * C::CPW + q;
         const uint8_t *base = c < C::A_CH ? Ab : Wb;
-        // a partial last stage (bf16) loads its missing steps from K = 0:
-        // valid memory, and compute skips those steps
-        const int s = ((c < C::A_CH ? c : c - C::A_CH) / C::BV) % C::STEPS;
-        const uint32_t k = (st * C::SK + s * C::KSTEP < K) ? kb : kb - (st * C::SK) * C::ESZ - s * C::RB;
-        dma16_to_lds(base + (coff[q] + k), sl + c * 1024);
+        // a partial last stage (bf16, K % 64 = 32) loads the pieces past the
+        // row end from K = 0: valid memory, and compute skips that step
+        uint32_t off = coff[q] + kb;
+        if constexpr (DT == kBF16)   // fp8 K is a multiple of the stage
+          if (kb + cpc[q] >= static_cast<uint32_t>(kbytes)) off = coff[q] - cpc[q];
+        dma16_to_lds(base + off, sl + c * 1024);
       }
       if constexpr (C::SCALED) dma4_to_lds(sbase + (soff + st), sl + C::A_BYTES + C::B_BYTES + wave * 256);
     };
@@ -295,59 +298,101 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void grouped_kernel(GroupedArgs a)
     const int mb0 = wm * MBW;                 // this wave's first m-block
     const bool rows_on = mb0 < nmb;           // any of its rows exist
 
-    // lane L reads row L % 16, pieces of K slice L / 16, at their swizzled
-    // positions: off0 / off1 for its first / last 16-byte piece
+    // lane L reads row L % 16 of a stage block, K slice L / 16 of each MFMA
+    // step, at the swizzled positions of its 16-byte pieces: bf16 step s is
+    // logical piece 4 s + L / 16 (loff[s]); fp8 (one step) pieces 2 (L / 16)
+    // and 2 (L / 16) + 1 (loff[0], loff[1]).
     const int rr16 = lane & 15, kg = lane >> 4;
-    const int off0 = rr16 * C::RB + (((C::BV * kg) ^ swz(rr16)) * 16);
-    const int off1 = rr16 * C::RB + (((C::BV * kg + C::BV - 1) ^ swz(rr16)) * 16);
+    constexpr int NOFF = DT == kBF16 ? C::STEPS : 2;
+    uint32_t loff[NOFF];
+#pragma unroll
+    for (int s = 0; s < NOFF; ++s) {
+      const int piece = DT == kBF16 ? 4 * s + kg : 2 * kg + s;
+      loff[s] = rr16 * C::RB + ((piece ^ swz(rr16)) * 16);
+    }
 
-    auto compute = [&](int st) {
-      const uint8_t *sl = lds + (st % DEPTH) * C::STAGE_BYTES;
-      // step block (mb, s) of A and (cg, j, s) of B
-      const uint32_t la0 = lds_off(sl + (mb0 * C::STEPS) * C::BV * 1024 + off0);
-      const uint32_t lb0 = lds_off(sl + C::A_BYTES + (wn * NB * C::STEPS) * C::BV * 1024 + off0);
+    // ---- stage operands: LDS -> registers, issued one stage ahead ----
+    // bf16: a[s * MBW + mb], b[s * NB + j] (one 16-byte piece per lane each);
+    // fp8: a[2 mb + h], b[2 j + h] (the lane's two pieces of a 128-wide step).
+    constexpr int NA = DT == kBF16 ? C::STEPS * MBW : 2 * MBW;
+    constexpr int NBR = DT == kBF16 ? C::STEPS * NB : 2 * NB;
+    struct Regs {
+      u32x4_t a[NA];
+      u32x4_t b[NBR];
+    };
+    constexpr int BLK = 16 * C::RB;   // bytes of a stage block
+    auto read_stage = [&](int slot, Regs &R) {
+      const uint32_t la = lds_off(lds + slot * C::STAGE_BYTES + mb0 * BLK);
+      const uint32_t lb = lds_off(lds + slot * C::STAGE_BYTES + C::A_BYTES + wn * NB * BLK);
+      // bf16 a[s * MBW + mb] / b[s * NB + j]: piece loff[s] of block mb / j;
+      // fp8 a[2 mb + h] / b[2 j + h]: piece loff[h]
+      static_for<0, NA>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        constexpr int o = DT == kBF16 ? i / MBW : i % 2, blk = DT == kBF16 ? i % MBW : i / 2;
+        lds_issue<blk * BLK>(la + loff[o], R.a[i]);
+      });
+      static_for<0, NBR>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        constexpr int o = DT == kBF16 ? i / NB : i % 2, blk = DT == kBF16 ? i % NB : i / 2;
+        lds_issue<blk * BLK>(lb + loff[o], R.b[i]);
+      });
+    };
+    // Wait for the issued reads; the empty statements then "redefine" every
+    // operand register, so no use of one can be scheduled before the wait.
+    auto lds_wait = [&](Regs &R) {
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      static_for<0, NA>([&](auto ic) { lds_tie(R.a[decltype(ic)::value]); });
+      static_for<0, NBR>([&](auto ic) { lds_tie(R.b[decltype(ic)::value]); });
+    };
+
+    auto compute = [&](int st, const Regs &R) {
       if constexpr (DT == kBF16) {
-        static_assert(MBW == 4 && NB == 4, "bf16 stage read layout");
-        constexpr int AS = C::STEPS * 1024;   // between m-blocks / weight blocks
 #pragma unroll
         for (int s = 0; s < C::STEPS; ++s) {
-          if (st * C::SK + s * C::KSTEP < K && rows_on) {
-            u32x4_t b0, b1, b2, b3, a0, a1, a2, a3;
-            const uint32_t lb = lb0 + s * 1024, la = la0 + s * 1024;
-            lds_read4<0, AS, 2 * AS, 3 * AS>(lb, lb, lb, lb, b0, b1, b2, b3);
-            lds_read4<0, AS, 2 * AS, 3 * AS>(la, la, la, la, a0, a1, a2, a3);
-            const bf16x8_t bv[4] = {__builtin_bit_cast(bf16x8_t, b0), __builtin_bit_cast(bf16x8_t, b1),
-                                    __builtin_bit_cast(bf16x8_t, b2), __builtin_bit_cast(bf16x8_t, b3)};
-            const bf16x8_t av[4] = {__builtin_bit_cast(bf16x8_t, a0), __builtin_bit_cast(bf16x8_t, a1),
-                                    __builtin_bit_cast(bf16x8_t, a2), __builtin_bit_cast(bf16x8_t, a3)};
+          if (st * C::SK + s * C::KSTEP < K) {
 #pragma unroll
             for (int mb = 0; mb < MBW; ++mb)
 #pragma unroll
-                for (int j = 0; j < NB; ++j)
-                  acc[mb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[mb], bv[j], acc[mb][j], 0, 0, 0);
+              for (int j = 0; j < NB; ++j)
+                acc[mb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8_t, R.a[s * MBW + mb]),
+                    __builtin_bit_cast(bf16x8_t, R.b[s * NB + j]), acc[mb][j], 0, 0, 0);
           }
         }
-      } else {
-        // one 128-wide K block per stage: partial MFMA from zero, then
-        // acc += partial * (A row scale * weight block scale)
-        static_assert(MBW == 4 && (NB == 4 || NB == 8), "fp8 stage read layout");
-        if (!rows_on) return;
-        const uint32_t d1 = off1 - off0;   // second piece of the lane's 32 bytes
-        const uint8_t *ssc = sl + C::A_BYTES + C::B_BYTES;
-        u32x4_t aq[8], sv[4];
-        lds_read4<0, 0, 2048, 2048>(la0, la0 + d1, la0, la0 + d1, aq[0], aq[1], aq[2], aq[3]);
-        lds_read4<4096, 4096, 6144, 6144>(la0, la0 + d1, la0, la0 + d1, aq[4], aq[5], aq[6], aq[7]);
-        // row scales of rows (mb0 + mb)*16 + 4*kg + i: contiguous floats
+      }
+    };
+    // fp8 scales of stage st: row scales of rows (mb0 + mb)*16 + 4*kg + i
+    // (contiguous floats) and the weight-block scales of this column group
+    auto read_scales = [&](int st, u32x4_t (&sv)[4], u32x4_t (&sw)[2]) {
+      if constexpr (C::SCALED) {
+        const uint8_t *ssc = lds + (st % DEPTH) * C::STAGE_BYTES + C::A_BYTES + C::B_BYTES;
         const uint32_t lsr = lds_off(ssc + ((mb0 * 16) + 4 * kg) * 4);
         lds_read4<0, 64, 128, 192>(lsr, lsr, lsr, lsr, sv[0], sv[1], sv[2], sv[3]);
-        // weight blocks four at a time, with their block scales (area ROW_WAVES)
+        const uint32_t lsw = lds_off(ssc + C::ROW_WAVES * 256 + wn * NB * 4);
+        if constexpr (NB == 4) lds_read1(lsw, sw[0]);
+        else lds_read2<0, 16>(lsw, lsw, sw[0], sw[1]);
+      }
+    };
+
+    // fp8 stage st, operands read and multiplied in two halves of the weight
+    // blocks (8 blocks of operands do not fit next to 128 accumulators)
+    auto compute_fp8 = [&](int st) {
+      if constexpr (C::SCALED) {
+        const uint8_t *sl = lds + (st % DEPTH) * C::STAGE_BYTES;
+        const uint32_t la0 = lds_off(sl + mb0 * BLK) + loff[0];
+        const uint32_t lb0 = lds_off(sl + C::A_BYTES + wn * NB * BLK) + loff[0];
+        const uint32_t d1 = loff[1] - loff[0];   // the lane's second piece
+        u32x4_t aq[8];
+        lds_read4<0, 0, 2048, 2048>(la0, la0 + d1, la0, la0 + d1, aq[0], aq[1], aq[2], aq[3]);
+        lds_read4<4096, 4096, 6144, 6144>(la0, la0 + d1, la0, la0 + d1, aq[4], aq[5], aq[6], aq[7]);
+        u32x4_t sv[4], sw[2];
+        read_scales(st, sv, sw);
 #pragma unroll
         for (int j0 = 0; j0 < NB; j0 += 4) {
-          u32x4_t bq[8], sw;
+          u32x4_t bq[8];
           const uint32_t lb = lb0 + j0 * 2048;
           lds_read4<0, 0, 2048, 2048>(lb, lb + d1, lb, lb + d1, bq[0], bq[1], bq[2], bq[3]);
           lds_read4<4096, 4096, 6144, 6144>(lb, lb + d1, lb, lb + d1, bq[4], bq[5], bq[6], bq[7]);
-          lds_read1(lds_off(ssc + C::ROW_WAVES * 256 + (wn * NB + j0) * 4), sw);
 #pragma unroll
           for (int mb = 0; mb < MBW; ++mb) {
             const i32x8_t av = as_i32x8(aq[2 * mb], aq[2 * mb + 1]);
@@ -356,7 +401,7 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void grouped_kernel(GroupedArgs a)
               const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
               const f32x4_t p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                   av, as_i32x8(bq[2 * j], bq[2 * j + 1]), z, 0, 0, 0, 127, 0, 127);
-              const float ws = __uint_as_float(sw[j]);
+              const float ws = __uint_as_float(sw[(j0 + j) / 4][(j0 + j) % 4]);
 #pragma unroll
               for (int i = 0; i < 4; ++i)
                 acc[mb][j0 + j][i] = fmaf(p[i], __uint_as_float(sv[mb][i]) * ws, acc[mb][j0 + j][i]);
@@ -366,22 +411,67 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void grouped_kernel(GroupedArgs a)
       }
     };
 
-    // ---- K loop: DEPTH-stage ring of LDS slots filled by direct loads ----
     __syncthreads();   // the previous unit is done with every slot
+    if constexpr (DT == kBF16) {
+      // ---- bf16: single-barrier ring of DEPTH = 3 LDS slots ----
+      // Step st issues the loads of stage st + 2 (into the slot of stage
+      // st - 1, whose LDS reads every wave finished in step st - 2), waits
+      // for its own loads of stage st + 1, passes the barrier (stage st + 1
+      // has landed for all waves), issues the LDS reads of stage st + 1,
+      // multiplies stage st from registers, then waits for those reads: the
+      // reads of one stage overlap the MFMAs of the previous one.
+      static_assert(DEPTH == 3, "single-barrier ring");
+      Regs RA, RB;
+      auto step = [&](int st, Regs &cur, Regs &next) {
+        if (st + 2 < nstage) {
+          issue(st + 2);
+          wait_vm<C::LPS>();
+        } else {
+          wait_vm<0>();
+        }
+        ring_barrier();
+        if (rows_on) {
+          if (st + 1 < nstage) read_stage((st + 1) % DEPTH, next);
+          __builtin_amdgcn_sched_barrier(0);
+          compute(st, cur);
+          __builtin_amdgcn_sched_barrier(0);
+          if (st + 1 < nstage) lds_wait(next);
+        }
+      };
+      issue(0);
+      if (nstage > 1) {
+        issue(1);
+        wait_vm<C::LPS>();
+      } else {
+        wait_vm<0>();
+      }
+      ring_barrier();   // stage 0 landed
+      if (rows_on) {
+        read_stage(0, RA);
+        lds_wait(RA);
+      }
+      for (int st = 0; st < nstage; st += 2) {
+        step(st, RA, RB);
+        if (st + 1 >= nstage) break;
+        step(st + 1, RB, RA);
+      }
+    } else {
+      // ---- fp8: DEPTH-slot ring, barrier before reuse and after landing ----
 #pragma unroll
-    for (int st = 0; st < DEPTH - 1; ++st)
-      if (st < nstage) issue(st);
-    for (int st = 0; st < nstage; ++st) {
-      if (st > 0) ring_barrier();    // slot (st - 1) % DEPTH is free again
-      const int ahead = st + DEPTH - 1;
-      if (ahead < nstage) issue(ahead);
-      // stages issued after `st`: min(DEPTH - 1, nstage - 1 - st)
-      const int later = min(DEPTH - 1, nstage - 1 - st);
-      if (DEPTH == 3 && later >= 2) wait_vm<(DEPTH - 1) * C::LPS>();
-      else if (later >= 1) wait_vm<C::LPS>();
-      else wait_vm<0>();
-      ring_barrier();                // every wave's loads of stage st landed
-      compute(st);
+      for (int st = 0; st < DEPTH - 1; ++st)
+        if (st < nstage) issue(st);
+      for (int st = 0; st < nstage; ++st) {
+        if (st > 0) ring_barrier();    // slot (st - 1) % DEPTH is free again
+        const int ahead = st + DEPTH - 1;
+        if (ahead < nstage) issue(ahead);
+        // stages issued after `st`: min(DEPTH - 1, nstage - 1 - st)
+        const int later = min(DEPTH - 1, nstage - 1 - st);
+        if (DEPTH == 3 && later >= 2) wait_vm<(DEPTH - 1) * C::LPS>();
+        else if (later >= 1) wait_vm<C::LPS>();
+        else wait_vm<0>();
+        ring_barrier();                // every wave's loads of stage st landed
+        if (rows_on) compute_fp8(st);
+      }
     }
     __syncthreads();
 
@@ -504,17 +594,18 @@ static hipError_t launch_one(GroupedArgs ga, hipStream_t s) {
   return hipGetLastError();
 }
 
-// 256-row tiles when experts average more than 96 rows, 128-row tiles
-// otherwise (fewer idle rows per tile).
+// Large tiles when experts average more than 96 rows, small ones otherwise
+// (fewer idle rows per tile).
 static bool big_tiles(const Dims &d) { return d.te > 96 * d.E; }
 
 hipError_t launch_grouped_gateup(const Dims &d, const Inputs &in,
                                  const Work &w, hipStream_t s) {
   const GroupedArgs ga{d, in, w, 0, 0};
   if (d.wdt == kBF16) {
-    // 64 h columns (4 weight blocks per wave: 2 gate + 2 up), K stages of 64
+    // 256-row tiles (64 h columns, 2 x 4 waves) when experts average more
+    // than 96 rows, else 96-row tiles (128 h columns, 4 column waves)
     if (big_tiles(d)) return launch_one<kBF16, kGateUp, 4, 2, 4, 4, 3, 64>(ga, s);
-    return launch_one<kBF16, kGateUp, 4, 2, 2, 4, 3, 64>(ga, s);
+    return launch_one<kBF16, kGateUp, 4, 4, 1, 6, 3, 64>(ga, s);
   }
   // fp8: 128 h columns = one h scale group (2 column waves x 4 gate + 4 up
   // blocks)
@@ -526,8 +617,8 @@ hipError_t launch_grouped_down(const Dims &d, const Inputs &in, const Work &w,
                                hipStream_t s) {
   const GroupedArgs ga{d, in, w, 0, 0};
   if (d.wdt == kBF16) {
-    if (big_tiles(d)) return launch_one<kBF16, kDown, 4, 2, 4, 4, 3, 64>(ga, s);
-    return launch_one<kBF16, kDown, 4, 2, 2, 4, 3, 64>(ga, s);
+    if (big_tiles(d)) return launch_one<kBF16, kDown, 4, 2, 2, 4, 3, 64>(ga, s);
+    return launch_one<kBF16, kDown, 4, 4, 1, 6, 3, 64>(ga, s);
   }
   if (big_tiles(d)) return launch_one<kFP8, kDown, 4, 2, 4, 4, 3, 128>(ga, s);
   return launch_one<kFP8, kDown, 4, 2, 2, 4, 3, 128>(ga, s);

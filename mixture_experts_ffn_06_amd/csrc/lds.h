@@ -2,6 +2,7 @@
 // compiler's wait tracking (shared by the grouped and small-m expert kernels).
 #pragma once
 #include "common.h"
+#include <type_traits>
 
 namespace moe {
 
@@ -48,6 +49,24 @@ __device__ __forceinline__ void ring_barrier() {
 // and ends with the wait for them, so no use of a result can be scheduled
 // before its data has arrived.
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// Issue one 16-byte read at p + O without waiting for it: the result is in
+// v only after an s_waitcnt lgkmcnt, and lds_tie(v) after that wait keeps
+// every use of v behind it.
+template <int O>
+__device__ __forceinline__ void lds_issue(uint32_t p, u32x4_t &v) {
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(p), "i"(O));
+}
+__device__ __forceinline__ void lds_tie(u32x4_t &v) { asm volatile("" : "+v"(v)); }
+
+// Compile-time loop: f(integral_constant<int, I>) for I in [B, E).
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
 
 __device__ __forceinline__ uint32_t lds_off(const void *p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
