@@ -250,6 +250,10 @@ def main():
     tf = cnt["flops"] / (ms_per_step * 1e-3) / 1e12
     dom_ms = dom_timed_ms if dom_timed_ms is not None else float(stage_ms[di])
     dom_gbps = cnt[dom]["bytes"] / (dom_ms * 1e-3) / 1e9
+    dom_tflops = cnt[dom]["flops"] / (dom_ms * 1e-3) / 1e12
+    # the kernel's bound: whichever of its bytes and flops takes longer at peak
+    mfma_peak = MFMA_PEAK_TFLOPS[wl.dtype]
+    mfma_bound = cnt[dom]["flops"] / (mfma_peak * 1e12) > cnt[dom]["bytes"] / (HBM_PEAK_GBPS * 1e9)
     kernel_names = {"small_m": "sm_gateup_kernel", "grouped": "grouped_kernel<gateup>",
                     "simple": "simple_gateup_kernel"}
     path = layers[0].plan.path_for(m)
@@ -268,9 +272,12 @@ def main():
                   "algorithmic_bytes": cnt["bytes"], "algorithmic_flops": cnt["flops"],
                   "gpu_ms_per_step": gpu_ms},
         "stages_us": {s: float(stage_ms[j] * 1e3) for j, s in enumerate(STAGES)},
-        "roofline": {"kernel": kernel_names.get(path, path), "bound": "hbm",
-                     "achieved": dom_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": dom_gbps / HBM_PEAK_GBPS,
+        "roofline": {"kernel": kernel_names.get(path, path),
+                     "bound": "mfma" if mfma_bound else "hbm",
+                     "achieved": dom_tflops if mfma_bound else dom_gbps,
+                     "peak": mfma_peak if mfma_bound else HBM_PEAK_GBPS,
+                     "unit": "TFLOP/s" if mfma_bound else "GB/s",
+                     "frac": dom_tflops / mfma_peak if mfma_bound else dom_gbps / HBM_PEAK_GBPS,
                      "traffic": recorded_traffic(wl.name, m, dom, path),
                      "traffic_unit": "HBM bytes per launch, read + written (rocprofv3 counters)",
                      "bytes_per_launch": cnt[dom]["bytes"], "us_per_launch": dom_ms * 1e3},

@@ -49,6 +49,7 @@ struct Work {
   int *lrank;           // [te] rank of a pair among same-expert pairs of its run
   int *active;          // [E] experts with >= 1 pair, ascending
   int *nactive;         // [1]
+  int *perm_blk;        // [chunks][E] per-chunk counts, then starts (many pairs)
   uint8_t *xq;          // [m,H] fp8 codes of x
   float *sx;            // [m,H/128]
   void *h;              // [te,I]  routed SwiGLU output (sorted rows)
@@ -59,7 +60,11 @@ struct Work {
   void *y_sh;           // [m,H]   shared down output
 };
 
-// permute.hip
+// permute.hip: one block below kPermMultiMin pairs, else chunks of
+// kPermChunk pairs (needs Work::perm_blk of permute_chunks(d) * E ints)
+constexpr int kPermChunk = 4096;
+constexpr int kPermMultiMin = 8192;
+int permute_chunks(const Dims &d);
 hipError_t launch_permute(const Dims &d, const int *topk_idx, const Work &w,
                           hipStream_t s);
 

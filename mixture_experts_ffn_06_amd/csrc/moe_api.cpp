@@ -47,7 +47,7 @@ int resolve_path(const moe_config_t &c, int m) {
 // Byte sizes of every workspace region for m tokens.
 struct Layout {
   enum {
-    kLogits, kRpart, kCounts, kOffsets, kSorted, kSlot, kLrank, kActive, kNactive, kXq,
+    kLogits, kRpart, kCounts, kOffsets, kSorted, kSlot, kLrank, kActive, kNactive, kPermBlk, kXq,
     kSx, kH, kHs, kHsh, kHshs, kY, kYsh, kN
   };
   size_t size[kN];
@@ -72,6 +72,8 @@ Layout layout(const moe_plan_s &p, int m) {
   L.size[Layout::kLrank] = te * 4;
   L.size[Layout::kActive] = E * 4;
   L.size[Layout::kNactive] = 4;
+  L.size[Layout::kPermBlk] = te >= static_cast<size_t>(moe::kPermMultiMin)
+                                 ? (te + moe::kPermChunk - 1) / moe::kPermChunk * E * 4 : 0;
   L.size[Layout::kXq] = fp8 ? m * H : 0;
   L.size[Layout::kSx] = fp8 ? m * (H / 128) * 4 : 0;
   L.size[Layout::kH] = te * I * hb;
@@ -102,6 +104,7 @@ moe::Work carve(const Layout &L, void *ws) {
   w.lrank = static_cast<int *>(at(Layout::kLrank));
   w.active = static_cast<int *>(at(Layout::kActive));
   w.nactive = static_cast<int *>(at(Layout::kNactive));
+  w.perm_blk = static_cast<int *>(at(Layout::kPermBlk));
   w.xq = static_cast<uint8_t *>(at(Layout::kXq));
   w.sx = static_cast<float *>(at(Layout::kSx));
   w.h = at(Layout::kH);

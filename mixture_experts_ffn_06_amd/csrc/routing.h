@@ -178,18 +178,18 @@ __device__ __forceinline__ uint64_t same_expert_mask(int e, bool valid, int E) {
   return same;
 }
 
-__device__ __forceinline__ void permute_block(
-    const int *topk_idx, int te, int E, int *wcnt, int *scan_tmp,
-    int *__restrict__ counts, int *__restrict__ offsets,
-    int *__restrict__ sorted_pair, int *__restrict__ slot_of_pair,
-    int *__restrict__ lrank, int *__restrict__ active, int *__restrict__ nactive) {
+// Pass 1 over the pairs [c0, c1): each wave takes a contiguous run and walks
+// it 64 pairs at a time; a pair's rank among the earlier pairs of the same
+// expert in its wave's run goes to lrank[p], the run's count per expert to
+// wcnt[wave][e] (wcnt is zeroed here).
+__device__ __forceinline__ void chunk_ranks(const int *topk_idx, int c0, int c1, int E, int *wcnt,
+                                            int *__restrict__ lrank) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   for (int i = tid; i < kPermWaves * E; i += kPermThreads) wcnt[i] = 0;
   __syncthreads();
-
-  // ---- pass 1: rank of each pair inside its wave's run ----
-  const int per = (te + kPermWaves * 64 - 1) / (kPermWaves * 64) * 64;
-  const int p0 = wave * per, p1 = min(te, p0 + per);
+  const int n = c1 - c0;
+  const int per = (n + kPermWaves * 64 - 1) / (kPermWaves * 64) * 64;
+  const int p0 = c0 + wave * per, p1 = min(c1, p0 + per);
   int *mine = wcnt + wave * E;
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   const uint64_t above = (lane == 63) ? 0ull : (~0ull << (lane + 1));
@@ -206,35 +206,32 @@ __device__ __forceinline__ void permute_block(
     if (valid && (same & above) == 0) mine[e] = r + 1;   // last lane of its group
   }
   __syncthreads();
+}
 
-  // ---- expert totals, offsets, per-wave bases ----
-  constexpr int EPT = 1024 / kPermThreads;   // experts per thread (E <= 1024)
-  (void)EPT;
-  const int x = tid;                          // one expert per thread
-  int tot = 0;
-  if (x < E)
-    for (int w = 0; w < kPermWaves; ++w) tot += wcnt[w * E + x];
-  int all_pairs, all_active;
-  const int off = block_exclusive_scan(x < E ? tot : 0, scan_tmp, &all_pairs);
-  const int aoff = block_exclusive_scan(x < E && tot > 0 ? 1 : 0, scan_tmp, &all_active);
+// Turns the per-wave counts of chunk_ranks into start positions, the runs of
+// each expert following base[e] in wave order (thread x: expert x).
+__device__ __forceinline__ void chunk_bases(int E, int *wcnt, int base_x) {
+  const int x = threadIdx.x;
   if (x < E) {
-    counts[x] = tot;
-    offsets[x] = off;
-    if (tot > 0) active[aoff] = x;
-    int run = off;
+    int run = base_x;
     for (int w = 0; w < kPermWaves; ++w) {
       const int c = wcnt[w * E + x];
       wcnt[w * E + x] = run;
       run += c;
     }
   }
-  if (tid == 0) {
-    offsets[E] = all_pairs;
-    *nactive = all_active;
-  }
   __syncthreads();
+}
 
-  // ---- pass 2: scatter (each thread rereads the ranks it wrote) ----
+// Pass 2 over [c0, c1): every thread rereads the ranks it wrote.
+__device__ __forceinline__ void chunk_scatter(const int *topk_idx, int c0, int c1, int E, const int *wcnt,
+                                              const int *__restrict__ lrank, int *__restrict__ sorted_pair,
+                                              int *__restrict__ slot_of_pair) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = c1 - c0;
+  const int per = (n + kPermWaves * 64 - 1) / (kPermWaves * 64) * 64;
+  const int p0 = c0 + wave * per, p1 = min(c1, p0 + per);
+  const int *mine = wcnt + wave * E;
   for (int base = p0; base < p1; base += 64) {
     const int p = base + lane;
     if (p < p1) {
@@ -244,6 +241,43 @@ __device__ __forceinline__ void permute_block(
       slot_of_pair[p] = pos;
     }
   }
+}
+
+// Expert totals -> counts, offsets, the active list; returns offsets[x] for
+// thread x (E <= kPermThreads).
+__device__ __forceinline__ int expert_offsets(int tot, int E, int *scan_tmp, int *__restrict__ counts,
+                                              int *__restrict__ offsets, int *__restrict__ active,
+                                              int *__restrict__ nactive) {
+  const int x = threadIdx.x;
+  int all_pairs, all_active;
+  const int off = block_exclusive_scan(x < E ? tot : 0, scan_tmp, &all_pairs);
+  const int aoff = block_exclusive_scan(x < E && tot > 0 ? 1 : 0, scan_tmp, &all_active);
+  if (x < E) {
+    counts[x] = tot;
+    offsets[x] = off;
+    if (tot > 0) active[aoff] = x;
+  }
+  if (x == 0) {
+    offsets[E] = all_pairs;
+    *nactive = all_active;
+  }
+  return off;
+}
+
+// The whole sort in one block.
+__device__ __forceinline__ void permute_block(
+    const int *topk_idx, int te, int E, int *wcnt, int *scan_tmp,
+    int *__restrict__ counts, int *__restrict__ offsets,
+    int *__restrict__ sorted_pair, int *__restrict__ slot_of_pair,
+    int *__restrict__ lrank, int *__restrict__ active, int *__restrict__ nactive) {
+  chunk_ranks(topk_idx, 0, te, E, wcnt, lrank);
+  const int x = threadIdx.x;
+  int tot = 0;
+  if (x < E)
+    for (int w = 0; w < kPermWaves; ++w) tot += wcnt[w * E + x];
+  const int off = expert_offsets(tot, E, scan_tmp, counts, offsets, active, nactive);
+  chunk_bases(E, wcnt, off);
+  chunk_scatter(topk_idx, 0, te, E, wcnt, lrank, sorted_pair, slot_of_pair);
 }
 
 }  // namespace moe

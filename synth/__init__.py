@@ -102,6 +102,14 @@ WORKLOADS: dict[str, Workload] = {
     "large_fp8": Workload("large_fp8", m=4096, hidden=7168, experts=256,
                           topk=8, inter=2048, shared_inter=2048, dtype="fp8",
                           gating="sigmoid", routed_scale=2.5, seed=4),
+    # MFMA-bound shapes (about 1024 / 512 rows per expert): the prefill
+    # layer with m = 16384 and the large fp8 layer with m = 16384.
+    "dense_bf16": Workload("dense_bf16", m=16384, hidden=2048, experts=128,
+                           topk=8, inter=768, shared_inter=2048, dtype="bf16",
+                           gating="softmax", routed_scale=1.0, seed=6),
+    "dense_fp8": Workload("dense_fp8", m=16384, hidden=7168, experts=256,
+                          topk=8, inter=2048, shared_inter=2048, dtype="fp8",
+                          gating="sigmoid", routed_scale=2.5, seed=7),
     # Skewed routing on the large-fp8 shapes with m = 2048.
     "skew_fp8": Workload("skew_fp8", m=2048, hidden=7168, experts=256,
                          topk=8, inter=2048, shared_inter=2048, dtype="fp8",

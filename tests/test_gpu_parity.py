@@ -84,6 +84,14 @@ def test_skew_fp8_sampled():
     assert counts.max() / counts.sum() > 0.10
 
 
+@pytest.mark.parametrize("name", ["dense_bf16", "dense_fp8"])
+def test_mfma_bound_sampled(name):
+    """About 1024 (bf16) / 512 (fp8) rows per expert: several M tiles per
+    expert on the large-tile configurations."""
+    wl = synth.WORKLOADS[name]
+    run_case(wl, path="grouped", tokens=_sample(wl.m, seed=2), lazy=True)
+
+
 # ------------------------------------------- reduced shapes, all elements ---
 
 RAGGED_FP8 = synth.Workload("ragged_fp8", m=300, hidden=512, experts=16, topk=4,
