@@ -74,7 +74,7 @@ struct GCfg {
   // fp8: one 256-byte scale area per wave: areas 0 .. BM/64-1 hold the row
   // scales of rows 0 .. BM-1, area BM/64 the WN*NB weight-block scales.
   static constexpr int S_BYTES = SCALED ? NW * 256 : 0;
-  static constexpr int ROW_WAVES = BM / 64;
+  static constexpr int ROW_WAVES = (BM + 63) / 64;
   static constexpr int STAGE_BYTES = A_BYTES + B_BYTES + S_BYTES;
   static constexpr int LDS_BYTES = DEPTH * STAGE_BYTES;
   // output columns: gate/up pairs NB/2 gate with NB/2 up blocks
@@ -361,18 +361,6 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void grouped_kernel(GroupedArgs a)
         }
       }
     };
-    // fp8 scales of stage st: row scales of rows (mb0 + mb)*16 + 4*kg + i
-    // (contiguous floats) and the weight-block scales of this column group
-    auto read_scales = [&](int st, u32x4_t (&sv)[4], u32x4_t (&sw)[2]) {
-      if constexpr (C::SCALED) {
-        const uint8_t *ssc = lds + (st % DEPTH) * C::STAGE_BYTES + C::A_BYTES + C::B_BYTES;
-        const uint32_t lsr = lds_off(ssc + ((mb0 * 16) + 4 * kg) * 4);
-        lds_read4<0, 64, 128, 192>(lsr, lsr, lsr, lsr, sv[0], sv[1], sv[2], sv[3]);
-        const uint32_t lsw = lds_off(ssc + C::ROW_WAVES * 256 + wn * NB * 4);
-        if constexpr (NB == 4) lds_read1(lsw, sw[0]);
-        else lds_read2<0, 16>(lsw, lsw, sw[0], sw[1]);
-      }
-    };
 
     // fp8 stage st, operands read and multiplied in two halves of the weight
     // blocks (8 blocks of operands do not fit next to 128 accumulators)
@@ -382,17 +370,38 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void grouped_kernel(GroupedArgs a)
         const uint32_t la0 = lds_off(sl + mb0 * BLK) + loff[0];
         const uint32_t lb0 = lds_off(sl + C::A_BYTES + wn * NB * BLK) + loff[0];
         const uint32_t d1 = loff[1] - loff[0];   // the lane's second piece
-        u32x4_t aq[8];
-        lds_read4<0, 0, 2048, 2048>(la0, la0 + d1, la0, la0 + d1, aq[0], aq[1], aq[2], aq[3]);
-        lds_read4<4096, 4096, 6144, 6144>(la0, la0 + d1, la0, la0 + d1, aq[4], aq[5], aq[6], aq[7]);
-        u32x4_t sv[4], sw[2];
-        read_scales(st, sv, sw);
+        const uint8_t *ssc = sl + C::A_BYTES + C::B_BYTES;
+        // A pieces, row scales (rows (mb0 + mb)*16 + 4*kg + i: contiguous
+        // floats) and the weight-block scales of this column group: issued
+        // together, one wait
+        u32x4_t aq[2 * MBW], sv[MBW], sw[NB / 4];
+        const uint32_t lsr = lds_off(ssc + ((mb0 * 16) + 4 * kg) * 4);
+        const uint32_t lsw = lds_off(ssc + C::ROW_WAVES * 256 + wn * NB * 4);
+        static_for<0, MBW>([&](auto ic) {
+          constexpr int mb = decltype(ic)::value;
+          lds_issue<mb * BLK>(la0, aq[2 * mb]);
+          lds_issue<mb * BLK>(la0 + d1, aq[2 * mb + 1]);
+          lds_issue<mb * 64>(lsr, sv[mb]);
+        });
+        static_for<0, NB / 4>([&](auto ic) {
+          constexpr int q = decltype(ic)::value;
+          lds_issue<q * 16>(lsw, sw[q]);
+        });
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        static_for<0, MBW>([&](auto ic) {
+          constexpr int mb = decltype(ic)::value;
+          lds_tie(aq[2 * mb]);
+          lds_tie(aq[2 * mb + 1]);
+          lds_tie(sv[mb]);
+        });
+        static_for<0, NB / 4>([&](auto ic) { lds_tie(sw[decltype(ic)::value]); });
+        // weight blocks four at a time
 #pragma unroll
         for (int j0 = 0; j0 < NB; j0 += 4) {
           u32x4_t bq[8];
-          const uint32_t lb = lb0 + j0 * 2048;
-          lds_read4<0, 0, 2048, 2048>(lb, lb + d1, lb, lb + d1, bq[0], bq[1], bq[2], bq[3]);
-          lds_read4<4096, 4096, 6144, 6144>(lb, lb + d1, lb, lb + d1, bq[4], bq[5], bq[6], bq[7]);
+          const uint32_t lb = lb0 + j0 * BLK;
+          lds_read4<0, 0, BLK, BLK>(lb, lb + d1, lb, lb + d1, bq[0], bq[1], bq[2], bq[3]);
+          lds_read4<2 * BLK, 2 * BLK, 3 * BLK, 3 * BLK>(lb, lb + d1, lb, lb + d1, bq[4], bq[5], bq[6], bq[7]);
 #pragma unroll
           for (int mb = 0; mb < MBW; ++mb) {
             const i32x8_t av = as_i32x8(aq[2 * mb], aq[2 * mb + 1]);
@@ -609,7 +618,7 @@ hipError_t launch_grouped_gateup(const Dims &d, const Inputs &in,
   }
   // fp8: 128 h columns = one h scale group (2 column waves x 4 gate + 4 up
   // blocks)
-  if (big_tiles(d)) return launch_one<kFP8, kGateUp, 8, 2, 4, 4, 2, 128>(ga, s);
+  if (big_tiles(d)) return launch_one<kFP8, kGateUp, 4, 4, 2, 6, 2, 128>(ga, s);   // 192 rows, 8 waves
   return launch_one<kFP8, kGateUp, 8, 2, 2, 4, 3, 128>(ga, s);
 }
 
@@ -620,7 +629,7 @@ hipError_t launch_grouped_down(const Dims &d, const Inputs &in, const Work &w,
     if (big_tiles(d)) return launch_one<kBF16, kDown, 4, 2, 2, 4, 3, 64>(ga, s);
     return launch_one<kBF16, kDown, 4, 4, 1, 6, 3, 64>(ga, s);
   }
-  if (big_tiles(d)) return launch_one<kFP8, kDown, 4, 2, 4, 4, 3, 128>(ga, s);
+  if (big_tiles(d)) return launch_one<kFP8, kDown, 4, 4, 2, 6, 2, 128>(ga, s);      // 192 rows, 8 waves
   return launch_one<kFP8, kDown, 4, 2, 2, 4, 3, 128>(ga, s);
 }
 
