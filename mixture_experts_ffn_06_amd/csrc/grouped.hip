@@ -616,21 +616,20 @@ hipError_t launch_grouped_gateup(const Dims &d, const Inputs &in,
     if (big_tiles(d)) return launch_one<kBF16, kGateUp, 4, 2, 4, 4, 3, 64>(ga, s);
     return launch_one<kBF16, kGateUp, 4, 4, 1, 6, 3, 64>(ga, s);
   }
-  // fp8: 128 h columns = one h scale group (2 column waves x 4 gate + 4 up
-  // blocks)
+  // fp8: 128 h columns = one h scale group (4 column waves x 2 gate + 2 up
+  // blocks; 4 x 4 block tiles per wave keep the scale promotion cheap)
   if (big_tiles(d)) return launch_one<kFP8, kGateUp, 4, 4, 2, 6, 2, 128>(ga, s);   // 192 rows, 8 waves
-  return launch_one<kFP8, kGateUp, 8, 2, 2, 4, 3, 128>(ga, s);
+  return launch_one<kFP8, kGateUp, 4, 4, 2, 4, 3, 128>(ga, s);                     // 128 rows, 8 waves
 }
 
 hipError_t launch_grouped_down(const Dims &d, const Inputs &in, const Work &w,
                                hipStream_t s) {
   const GroupedArgs ga{d, in, w, 0, 0};
   if (d.wdt == kBF16) {
-    if (big_tiles(d)) return launch_one<kBF16, kDown, 4, 2, 2, 4, 3, 64>(ga, s);
+    if (big_tiles(d)) return launch_one<kBF16, kDown, 4, 4, 2, 4, 3, 64>(ga, s);   // 128 rows x 256 columns, 8 waves
     return launch_one<kBF16, kDown, 4, 4, 1, 6, 3, 64>(ga, s);
   }
-  if (big_tiles(d)) return launch_one<kFP8, kDown, 4, 4, 2, 6, 2, 128>(ga, s);      // 192 rows, 8 waves
-  return launch_one<kFP8, kDown, 4, 2, 2, 4, 3, 128>(ga, s);
+  return launch_one<kFP8, kDown, 4, 4, 2, 4, 3, 128>(ga, s);   // 128 rows x 256 columns, 8 waves
 }
 
 }  // namespace moe
