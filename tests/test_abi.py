@@ -42,6 +42,9 @@ def _cfg(**kw):
     (dict(weight_dtype="fp8", inter=96), 2), (dict(weight_dtype="fp8", hidden=320), 2),
     (dict(weight_dtype="fp8", path="small_m"), 2), (dict(weight_dtype="f32", path="grouped"), 2),
     (dict(weight_dtype="bf16", inter=48), 2),
+    # operands of 2 GiB or more (32-bit byte offsets in the expert kernels)
+    (dict(hidden=8192, max_tokens=65536, topk=2), 2),
+    (dict(hidden=32768, inter=32768, max_tokens=16), 2),
 ])
 def test_plan_rejects_bad_configs(kw, status):
     with pytest.raises(moe.MoeError) as ei:
