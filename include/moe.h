@@ -142,9 +142,10 @@ typedef struct {
  * per fp32: the expert kernels use 32-bit byte offsets). */
 int moe_plan(const moe_config_t *cfg, moe_plan_t *plan_out);
 
-/* Bytes of device workspace that moe_forward needs for m tokens (0 on a
- * NULL plan).  The workspace holds logits, the permutation, the list of
- * experts with rows, quantised activations and the sorted intermediates. */
+/* Bytes of device workspace that moe_forward needs for any call of up to m
+ * tokens (0 on a NULL plan).  The workspace holds logits, the permutation,
+ * the list of experts with rows, quantised activations, the sorted
+ * intermediates and, for calls of <= 16 tokens, the router's partial sums. */
 size_t moe_workspace_bytes(moe_plan_t plan, int32_t m);
 
 /* Forward of the layer for m tokens (page 2, MoeV41::forward: x, m and a

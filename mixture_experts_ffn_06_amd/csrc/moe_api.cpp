@@ -283,7 +283,10 @@ int moe_plan(const moe_config_t *cfg, moe_plan_t *plan_out) {
 
 size_t moe_workspace_bytes(moe_plan_t plan, int32_t m) {
   if (!plan || m < 0) return 0;
-  return layout(*plan, m).total;
+  // enough for every call of up to m tokens: the regions grow with m, but
+  // calls of <= 16 tokens also hold the router's partial sums, which larger
+  // calls do without
+  return std::max(layout(*plan, m).total, layout(*plan, std::min(m, 16)).total);
 }
 
 int moe_forward(moe_plan_t plan, int32_t m, const void *x, const void *router_w,

@@ -63,6 +63,16 @@ def test_plan_accepts_and_reports_paths_and_workspace():
     assert lib().moe_workspace_bytes(None, 4) == 0
 
 
+def test_workspace_covers_every_smaller_call():
+    """A workspace sized for m tokens serves every call of fewer tokens: with
+    many experts the router partials of a <= 16-token call outweigh the
+    extra rows of a few more tokens."""
+    p = moe.MoePlan(**_cfg(num_experts=1024, topk=2, max_tokens=40))
+    sizes = [p.workspace_bytes(m) for m in range(41)]
+    assert sizes[17] >= sizes[16] > sizes[15]
+    assert all(sizes[m] == max(sizes[:m + 1]) for m in range(41))
+
+
 FAKE = 1 << 20   # aligned, never dereferenced: validation fails first
 
 
