@@ -20,7 +20,9 @@
 //    over the waves; the WM waves of a column group share its weight chunks,
 //    the WN waves of a row group share the token chunks.  The LDS holds a ring
 //    of DEPTH stages, so DEPTH-1 stages of loads are in flight while a stage
-//    is multiplied.
+//    is multiplied.  fp8 splits the ring: the token rows (served from L2)
+//    in 2 slots, the weights (from HBM) in DEPTH slots, so that 192-row
+//    tiles still keep two weight stages in flight.
 //  * Chunks are loaded in row order (consecutive lanes take consecutive 16
 //    bytes of a row: coalesced), with the 16-byte pieces of each row
 //    XOR-swizzled so that the MFMA-order LDS reads are bank-conflict free.
@@ -76,7 +78,14 @@ struct GCfg {
   static constexpr int S_BYTES = SCALED ? NW * 256 : 0;
   static constexpr int ROW_WAVES = (BM + 63) / 64;
   static constexpr int STAGE_BYTES = A_BYTES + B_BYTES + S_BYTES;
-  static constexpr int LDS_BYTES = DEPTH * STAGE_BYTES;
+  // fp8 split ring: A in DA slots, then B + scales in DEPTH slots; each wave
+  // loads CPA A chunks and CPB B chunks (+ one scale load) per stage
+  static constexpr int DA = 2;
+  static constexpr int B_STAGE = B_BYTES + S_BYTES;
+  static constexpr int CPA = A_CH / NW;
+  static constexpr int CPB = B_CH / NW;
+  static constexpr int LA = CPA, LB = CPB + 1;
+  static constexpr int LDS_BYTES = SCALED ? DA * A_BYTES + DEPTH * B_STAGE : DEPTH * STAGE_BYTES;
   // output columns: gate/up pairs NB/2 gate with NB/2 up blocks
   static constexpr int WCOLS = MODE == kGateUp ? 16 * NB / 2 : 16 * NB;
   static constexpr int NCOLS = WN * WCOLS;
@@ -86,8 +95,11 @@ struct GCfg {
   static_assert(LPS * (DEPTH - 1) < 64, "vmcnt range");
   static_assert(!SCALED || (ROW_WAVES < NW && WN * NB <= 64), "fp8 scale areas");
   static_assert(DEPTH >= 2 && DEPTH <= 3, "wait ladder");
+  static_assert(!SCALED || (DEPTH == 3 && A_CH % NW == 0 && B_CH % NW == 0 && 2 * LB + LA < 64),
+                "fp8 split ring: A and B chunks spread evenly, vmcnt range");
   static_assert(MODE == kDown || NB % 2 == 0, "gate/up pairs");
   static_assert(!(SCALED && MODE == kGateUp) || NCOLS == 128, "fp8 gate/up tile = one h scale group");
+  static_assert(!SCALED || 128 % WCOLS == 0, "fp8: a wave's columns lie in one 128-wide scale block");
 };
 
 struct GroupedArgs {
@@ -234,20 +246,39 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void grouped_kernel(GroupedArgs a)
     // Chunk c < A_CH: A stage block mb, instruction i; otherwise B stage
     // block (cg, j), instruction i.  dst = c * 1 KB in the stage.  The lane's
     // source is (c < A_CH ? Ab : Wb) + coff[q] + the stage's K offset.
-    uint32_t coff[C::CPW];
-    int cpc[DT == kBF16 ? C::CPW : 1];   // bf16: the lane's piece offset inside the stage
+    // (fp8: A chunks wave * CPA + q and B chunks wave * CPB + q instead)
+    constexpr int NCO = C::SCALED ? 1 : C::CPW;
+    uint32_t coff[NCO];
+    int cpc[NCO];   // bf16: the lane's piece offset inside the stage
+    uint32_t coffA[C::SCALED ? C::CPA : 1], coffB[C::SCALED ? C::CPB : 1];
+    if constexpr (!C::SCALED) {
 #pragma unroll
-    for (int q = 0; q < C::CPW; ++q) {
-      const int c = wave * C::CPW + q;
-      const int i = c % C::BV;
-      const int rl = i * C::RPI + lrow;               // row inside the stage block
-      const int pc = (lpiece ^ swz(rl)) * 16;         // this lane's piece, swizzled
-      if constexpr (DT == kBF16) cpc[q] = pc;
-      if (c < C::A_CH) {
-        coff[q] = a_off((c / C::BV) * 16 + rl) + pc;
-      } else {
-        const int blk = (c - C::A_CH) / C::BV;
-        coff[q] = static_cast<uint32_t>(wrow_of(blk / NB, blk % NB) + rl) * kbytes + pc;
+      for (int q = 0; q < C::CPW; ++q) {
+        const int c = wave * C::CPW + q;
+        const int i = c % C::BV;
+        const int rl = i * C::RPI + lrow;               // row inside the stage block
+        const int pc = (lpiece ^ swz(rl)) * 16;         // this lane's piece, swizzled
+        cpc[q] = pc;
+        if (c < C::A_CH) {
+          coff[q] = a_off((c / C::BV) * 16 + rl) + pc;
+        } else {
+          const int blk = (c - C::A_CH) / C::BV;
+          coff[q] = static_cast<uint32_t>(wrow_of(blk / NB, blk % NB) + rl) * kbytes + pc;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < C::CPA; ++q) {
+        const int c = wave * C::CPA + q;
+        const int rl = (c % C::BV) * C::RPI + lrow;
+        coffA[q] = a_off((c / C::BV) * 16 + rl) + (lpiece ^ swz(rl)) * 16;
+      }
+#pragma unroll
+      for (int q = 0; q < C::CPB; ++q) {
+        const int c = wave * C::CPB + q;
+        const int rl = (c % C::BV) * C::RPI + lrow;
+        const int blk = c / C::BV;
+        coffB[q] = static_cast<uint32_t>(wrow_of(blk / NB, blk % NB) + rl) * kbytes + (lpiece ^ swz(rl)) * 16;
       }
     }
     // fp8 scales: waves < ROW_WAVES fetch row scales (lane l: row 64w + l),
@@ -272,6 +303,21 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void grouped_kernel(GroupedArgs a)
       }
     }
 
+    // fp8 split ring: A of stage st in A slot st % DA, B and the scales in
+    // B slot st % DEPTH
+    auto issue_a = [&](int st) {
+      uint8_t *sl = lds + (st % C::DA) * C::A_BYTES;
+      const uint32_t kb = static_cast<uint32_t>(st) * C::SK;
+#pragma unroll
+      for (int q = 0; q < C::CPA; ++q) dma16_to_lds(Ab + (coffA[q] + kb), sl + (wave * C::CPA + q) * 1024);
+    };
+    auto issue_b = [&](int st) {
+      uint8_t *sl = lds + C::DA * C::A_BYTES + (st % DEPTH) * C::B_STAGE;
+      const uint32_t kb = static_cast<uint32_t>(st) * C::SK;
+#pragma unroll
+      for (int q = 0; q < C::CPB; ++q) dma16_to_lds(Wb + (coffB[q] + kb), sl + (wave * C::CPB + q) * 1024);
+      dma4_to_lds(sbase + (soff + st), sl + C::B_BYTES + wave * 256);
+    };
     auto issue = [&](int st) {
       uint8_t *sl = lds + (st % DEPTH) * C::STAGE_BYTES;
       const uint32_t kb = static_cast<uint32_t>(st) * (C::SK * C::ESZ);
@@ -286,7 +332,6 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void grouped_kernel(GroupedArgs a)
           if (kb + cpc[q] >= static_cast<uint32_t>(kbytes)) off = coff[q] - cpc[q];
         dma16_to_lds(base + off, sl + c * 1024);
       }
-      if constexpr (C::SCALED) dma4_to_lds(sbase + (soff + st), sl + C::A_BYTES + C::B_BYTES + wave * 256);
     };
 
     constexpr int HALF = NB / 2;
@@ -295,8 +340,14 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void grouped_kernel(GroupedArgs a)
     for (int mb = 0; mb < MBW; ++mb)
 #pragma unroll
       for (int j = 0; j < NB; ++j) acc[mb][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    const int mb0 = wm * MBW;                 // this wave's first m-block
-    const bool rows_on = mb0 < nmb;           // any of its rows exist
+    // The wave's m-blocks: bf16 MBW consecutive ones from mb0; fp8 every
+    // WM-th from wm, so that a tile only partly filled with rows (the common
+    // case for 192-row tiles) leaves the WM row waves equal work, and the
+    // blocks past the rows are skipped.
+    const int mb0 = wm * MBW;
+    const int mfirst = C::SCALED ? wm : mb0, mstep = C::SCALED ? WM : 1;
+    auto mrow = [&](int mb) { return mfirst + mstep * mb; };
+    const bool rows_on = mfirst < nmb;        // any of its rows exist
 
     // lane L reads row L % 16 of a stage block, K slice L / 16 of each MFMA
     // step, at the swizzled positions of its 16-byte pieces: bf16 step s is
@@ -366,22 +417,23 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void grouped_kernel(GroupedArgs a)
     // blocks (8 blocks of operands do not fit next to 128 accumulators)
     auto compute_fp8 = [&](int st) {
       if constexpr (C::SCALED) {
-        const uint8_t *sl = lds + (st % DEPTH) * C::STAGE_BYTES;
-        const uint32_t la0 = lds_off(sl + mb0 * BLK) + loff[0];
-        const uint32_t lb0 = lds_off(sl + C::A_BYTES + wn * NB * BLK) + loff[0];
+        const uint8_t *sa = lds + (st % C::DA) * C::A_BYTES;
+        const uint8_t *sb = lds + C::DA * C::A_BYTES + (st % DEPTH) * C::B_STAGE;
+        const uint32_t la0 = lds_off(sa + wm * BLK) + loff[0];
+        const uint32_t lb0 = lds_off(sb + wn * NB * BLK) + loff[0];
         const uint32_t d1 = loff[1] - loff[0];   // the lane's second piece
-        const uint8_t *ssc = sl + C::A_BYTES + C::B_BYTES;
-        // A pieces, row scales (rows (mb0 + mb)*16 + 4*kg + i: contiguous
+        const uint8_t *ssc = sb + C::B_BYTES;
+        // A pieces, row scales (rows mrow(mb)*16 + 4*kg + i: contiguous
         // floats) and the weight-block scales of this column group: issued
         // together, one wait
         u32x4_t aq[2 * MBW], sv[MBW], sw[NB / 4];
-        const uint32_t lsr = lds_off(ssc + ((mb0 * 16) + 4 * kg) * 4);
+        const uint32_t lsr = lds_off(ssc + ((wm * 16) + 4 * kg) * 4);
         const uint32_t lsw = lds_off(ssc + C::ROW_WAVES * 256 + wn * NB * 4);
         static_for<0, MBW>([&](auto ic) {
           constexpr int mb = decltype(ic)::value;
-          lds_issue<mb * BLK>(la0, aq[2 * mb]);
-          lds_issue<mb * BLK>(la0 + d1, aq[2 * mb + 1]);
-          lds_issue<mb * 64>(lsr, sv[mb]);
+          lds_issue<mb * WM * BLK>(la0, aq[2 * mb]);
+          lds_issue<mb * WM * BLK>(la0 + d1, aq[2 * mb + 1]);
+          lds_issue<mb * WM * 64>(lsr, sv[mb]);
         });
         static_for<0, NB / 4>([&](auto ic) {
           constexpr int q = decltype(ic)::value;
@@ -404,16 +456,29 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void grouped_kernel(GroupedArgs a)
           lds_read4<2 * BLK, 2 * BLK, 3 * BLK, 3 * BLK>(lb, lb + d1, lb, lb + d1, bq[4], bq[5], bq[6], bq[7]);
 #pragma unroll
           for (int mb = 0; mb < MBW; ++mb) {
+            if (mrow(mb) >= nmb) continue;   // no rows in this m-block
             const i32x8_t av = as_i32x8(aq[2 * mb], aq[2 * mb + 1]);
+            // row scale x weight-block scale, once per scale group: the
+            // wave's blocks are 16 * NB <= 64 consecutive 16-aligned output
+            // columns, so its gate blocks share one 128-row weight-scale
+            // block and its up blocks another (down: all share one)
+            constexpr int NG = MODE == kGateUp ? 2 : 1;
+            float sc[NG][4];
+#pragma unroll
+            for (int gi = 0; gi < NG; ++gi) {
+              const int jr = gi * (NB / NG);
+              const float ws = __uint_as_float(sw[jr / 4][jr % 4]);
+#pragma unroll
+              for (int i = 0; i < 4; ++i) sc[gi][i] = __uint_as_float(sv[mb][i]) * ws;
+            }
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
               const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
               const f32x4_t p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                   av, as_i32x8(bq[2 * j], bq[2 * j + 1]), z, 0, 0, 0, 127, 0, 127);
-              const float ws = __uint_as_float(sw[(j0 + j) / 4][(j0 + j) % 4]);
+              const int gi = (j0 + j) / (NB / NG);
 #pragma unroll
-              for (int i = 0; i < 4; ++i)
-                acc[mb][j0 + j][i] = fmaf(p[i], __uint_as_float(sv[mb][i]) * ws, acc[mb][j0 + j][i]);
+              for (int i = 0; i < 4; ++i) acc[mb][j0 + j][i] = fmaf(p[i], sc[gi][i], acc[mb][j0 + j][i]);
             }
           }
         }
@@ -465,18 +530,21 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void grouped_kernel(GroupedArgs a)
         step(st + 1, RB, RA);
       }
     } else {
-      // ---- fp8: DEPTH-slot ring, barrier before reuse and after landing ----
-#pragma unroll
-      for (int st = 0; st < DEPTH - 1; ++st)
-        if (st < nstage) issue(st);
+      // ---- fp8: split ring (A 2 slots, B 3 slots), barrier before reuse and
+      // after landing.  Issue order: B0 A0 B1 | A1 B2 | A2 B3 | ...: step st
+      // issues A(st+1) and B(st+2); B(st) precedes A(st), so waiting for
+      // everything up to A(st) covers stage st. ----
+      issue_b(0);
+      issue_a(0);
+      if (nstage > 1) issue_b(1);
       for (int st = 0; st < nstage; ++st) {
-        if (st > 0) ring_barrier();    // slot (st - 1) % DEPTH is free again
-        const int ahead = st + DEPTH - 1;
-        if (ahead < nstage) issue(ahead);
-        // stages issued after `st`: min(DEPTH - 1, nstage - 1 - st)
-        const int later = min(DEPTH - 1, nstage - 1 - st);
-        if (DEPTH == 3 && later >= 2) wait_vm<(DEPTH - 1) * C::LPS>();
-        else if (later >= 1) wait_vm<C::LPS>();
+        if (st > 0) ring_barrier();    // the slots of stage st - 1 are free again
+        const bool na = st + 1 < nstage, nb = st + 2 < nstage;
+        if (na) issue_a(st + 1);
+        if (nb) issue_b(st + 2);
+        // issued after A(st): B(st+1), A(st+1) (if st + 1 < nstage), B(st+2)
+        if (nb) wait_vm<2 * C::LB + C::LA>();
+        else if (na) wait_vm<C::LB + C::LA>();
         else wait_vm<0>();
         ring_barrier();                // every wave's loads of stage st landed
         if (rows_on) compute_fp8(st);
@@ -496,7 +564,7 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void grouped_kernel(GroupedArgs a)
         for (int mb = 0; mb < MBW; ++mb) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int rr = (mb0 + mb) * 16 + rsub + i;
+            const int rr = mrow(mb) * 16 + rsub + i;
             if (rr < rows) {
 #pragma unroll
               for (int j = 0; j < HALF; ++j)
@@ -523,7 +591,7 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void grouped_kernel(GroupedArgs a)
             am = fmaxf(am, __shfl_xor(am, 2));
             am = fmaxf(am, __shfl_xor(am, 4));
             am = fmaxf(am, __shfl_xor(am, 8));
-            if (cl == 0) wmax[wn][(mb0 + mb) * 16 + rsub + i] = am;
+            if (cl == 0) wmax[wn][mrow(mb) * 16 + rsub + i] = am;
           }
         }
         __syncthreads();
@@ -533,7 +601,7 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void grouped_kernel(GroupedArgs a)
         for (int mb = 0; mb < MBW; ++mb) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int rr = (mb0 + mb) * 16 + rsub + i;
+            const int rr = mrow(mb) * 16 + rsub + i;
             if (rr < rows) {
               float amax = 0.f;
 #pragma unroll
@@ -555,7 +623,7 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void grouped_kernel(GroupedArgs a)
       for (int mb = 0; mb < MBW; ++mb) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int rr = (mb0 + mb) * 16 + rsub + i;
+          const int rr = mrow(mb) * 16 + rsub + i;
           if (rr < rows) {
 #pragma unroll
             for (int j = 0; j < NB; ++j)
@@ -618,7 +686,7 @@ hipError_t launch_grouped_gateup(const Dims &d, const Inputs &in,
   }
   // fp8: 128 h columns = one h scale group (4 column waves x 2 gate + 2 up
   // blocks; 4 x 4 block tiles per wave keep the scale promotion cheap)
-  if (big_tiles(d)) return launch_one<kFP8, kGateUp, 4, 4, 2, 6, 2, 128>(ga, s);   // 192 rows, 8 waves
+  if (big_tiles(d)) return launch_one<kFP8, kGateUp, 4, 4, 2, 6, 3, 128>(ga, s);   // 192 rows, 8 waves
   return launch_one<kFP8, kGateUp, 4, 4, 2, 4, 3, 128>(ga, s);                     // 128 rows, 8 waves
 }
 
@@ -629,7 +697,9 @@ hipError_t launch_grouped_down(const Dims &d, const Inputs &in, const Work &w,
     if (big_tiles(d)) return launch_one<kBF16, kDown, 4, 4, 2, 4, 3, 64>(ga, s);   // 128 rows x 256 columns, 8 waves
     return launch_one<kBF16, kDown, 4, 4, 1, 6, 3, 64>(ga, s);
   }
-  return launch_one<kFP8, kDown, 4, 4, 2, 4, 3, 128>(ga, s);   // 128 rows x 256 columns, 8 waves
+  // 192 (128) rows x 256 columns, 8 waves
+  if (big_tiles(d)) return launch_one<kFP8, kDown, 4, 4, 2, 6, 3, 128>(ga, s);
+  return launch_one<kFP8, kDown, 4, 4, 2, 4, 3, 128>(ga, s);
 }
 
 }  // namespace moe
