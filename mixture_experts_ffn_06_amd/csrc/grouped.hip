@@ -431,9 +431,11 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void grouped_kernel(GroupedArgs a)
         const uint32_t lsw = lds_off(ssc + C::ROW_WAVES * 256 + wn * NB * 4);
         static_for<0, MBW>([&](auto ic) {
           constexpr int mb = decltype(ic)::value;
-          lds_issue<mb * WM * BLK>(la0, aq[2 * mb]);
-          lds_issue<mb * WM * BLK>(la0 + d1, aq[2 * mb + 1]);
-          lds_issue<mb * WM * 64>(lsr, sv[mb]);
+          if (mrow(mb) < nmb) {   // m-blocks past the rows are neither read nor multiplied
+            lds_issue<mb * WM * BLK>(la0, aq[2 * mb]);
+            lds_issue<mb * WM * BLK>(la0 + d1, aq[2 * mb + 1]);
+            lds_issue<mb * WM * 64>(lsr, sv[mb]);
+          }
         });
         static_for<0, NB / 4>([&](auto ic) {
           constexpr int q = decltype(ic)::value;
@@ -530,23 +532,21 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void grouped_kernel(GroupedArgs a)
         step(st + 1, RB, RA);
       }
     } else {
-      // ---- fp8: split ring (A 2 slots, B 3 slots), barrier before reuse and
-      // after landing.  Issue order: B0 A0 B1 | A1 B2 | A2 B3 | ...: step st
-      // issues A(st+1) and B(st+2); B(st) precedes A(st), so waiting for
-      // everything up to A(st) covers stage st. ----
+      // ---- fp8: split ring (A 2 slots, B 3 slots), one barrier per stage.
+      // Issue order: B0 A0 B1 | A1 B2 | A2 B3 | ...  Step st waits for its
+      // own loads up to A(st) (only B(st+1) was issued after it; B(st)
+      // precedes it), passes the barrier -- every wave's stage st has landed
+      // and every wave is done with stage st - 1 -- then refills the slots of
+      // stage st - 1 with A(st+1) and B(st+2) and multiplies stage st. ----
       issue_b(0);
       issue_a(0);
       if (nstage > 1) issue_b(1);
       for (int st = 0; st < nstage; ++st) {
-        if (st > 0) ring_barrier();    // the slots of stage st - 1 are free again
-        const bool na = st + 1 < nstage, nb = st + 2 < nstage;
-        if (na) issue_a(st + 1);
-        if (nb) issue_b(st + 2);
-        // issued after A(st): B(st+1), A(st+1) (if st + 1 < nstage), B(st+2)
-        if (nb) wait_vm<2 * C::LB + C::LA>();
-        else if (na) wait_vm<C::LB + C::LA>();
+        if (st + 1 < nstage) wait_vm<C::LB>();
         else wait_vm<0>();
-        ring_barrier();                // every wave's loads of stage st landed
+        ring_barrier();
+        if (st + 1 < nstage) issue_a(st + 1);
+        if (st + 2 < nstage) issue_b(st + 2);
         if (rows_on) compute_fp8(st);
       }
     }
