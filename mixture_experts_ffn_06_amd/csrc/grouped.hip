@@ -18,11 +18,10 @@
 //    weight rows (B) -- is brought into LDS exactly once by direct
 //    global->LDS loads (no register staging), in 1 KB chunks spread evenly
 //    over the waves; the WM waves of a column group share its weight chunks,
-//    the WN waves of a row group share the token chunks.  The LDS holds a ring
-//    of DEPTH stages, so DEPTH-1 stages of loads are in flight while a stage
-//    is multiplied.  fp8 splits the ring: the token rows (served from L2)
-//    in 2 slots, the weights (from HBM) in DEPTH slots, so that 192-row
-//    tiles still keep two weight stages in flight.
+//    the WN waves of a row group share the token chunks.  The LDS ring is
+//    split in two: the token rows (served from L2) in 2 slots, the weights
+//    (from HBM) in DEPTH slots, so that several weight stages are in flight
+//    while a stage is multiplied.
 //  * Chunks are loaded in row order (consecutive lanes take consecutive 16
 //    bytes of a row: coalesced), with the 16-byte pieces of each row
 //    XOR-swizzled so that the MFMA-order LDS reads are bank-conflict free.
@@ -68,35 +67,30 @@ struct GCfg {
   static constexpr int SWZ_DIV = 256 / RB;            // rows per 256-byte bank window
   static constexpr int A_CH = MB * BV;                // chunks per stage: A ...
   static constexpr int B_CH = WN * NB * BV;           // ... and B
-  static constexpr int CPW = (A_CH + B_CH) / NW;      // chunks loaded per wave
   static constexpr bool SCALED = DT == kFP8;
-  static constexpr int LPS = CPW + (SCALED ? 1 : 0);  // loads per stage per wave
   static constexpr int A_BYTES = A_CH * 1024;
   static constexpr int B_BYTES = B_CH * 1024;
   // fp8: one 256-byte scale area per wave: areas 0 .. BM/64-1 hold the row
   // scales of rows 0 .. BM-1, area BM/64 the WN*NB weight-block scales.
   static constexpr int S_BYTES = SCALED ? NW * 256 : 0;
   static constexpr int ROW_WAVES = (BM + 63) / 64;
-  static constexpr int STAGE_BYTES = A_BYTES + B_BYTES + S_BYTES;
-  // fp8 split ring: A in DA slots, then B + scales in DEPTH slots; each wave
-  // loads CPA A chunks and CPB B chunks (+ one scale load) per stage
+  // split ring: A in DA slots, then B (+ fp8 scales) in DEPTH slots; each
+  // wave loads CPA A chunks and CPB B chunks (+ one scale load) per stage
   static constexpr int DA = 2;
   static constexpr int B_STAGE = B_BYTES + S_BYTES;
   static constexpr int CPA = A_CH / NW;
   static constexpr int CPB = B_CH / NW;
-  static constexpr int LA = CPA, LB = CPB + 1;
-  static constexpr int LDS_BYTES = SCALED ? DA * A_BYTES + DEPTH * B_STAGE : DEPTH * STAGE_BYTES;
+  static constexpr int LA = CPA, LB = CPB + (SCALED ? 1 : 0);
+  static constexpr int LDS_BYTES = DA * A_BYTES + DEPTH * B_STAGE;
   // output columns: gate/up pairs NB/2 gate with NB/2 up blocks
   static constexpr int WCOLS = MODE == kGateUp ? 16 * NB / 2 : 16 * NB;
   static constexpr int NCOLS = WN * WCOLS;
   static_assert(STAGE_K % KSTEP == 0, "stage = whole MFMA steps");
   static_assert(RB == 128, "stage rows of 128 bytes (swizzle, chunk and read layout)");
-  static_assert((A_CH + B_CH) % NW == 0, "chunks spread evenly over the waves");
-  static_assert(LPS * (DEPTH - 1) < 64, "vmcnt range");
+  static_assert(A_CH % NW == 0 && B_CH % NW == 0, "A and B chunks spread evenly over the waves");
   static_assert(!SCALED || (ROW_WAVES < NW && WN * NB <= 64), "fp8 scale areas");
-  static_assert(DEPTH >= 2 && DEPTH <= 3, "wait ladder");
-  static_assert(!SCALED || (DEPTH == 3 && A_CH % NW == 0 && B_CH % NW == 0 && 2 * LB + LA < 64),
-                "fp8 split ring: A and B chunks spread evenly, vmcnt range");
+  static_assert(SCALED ? DEPTH == 3 : (DEPTH >= 3 && (DEPTH - 2) * LB < 64),
+                "ring depth (fp8 loop: 3 weight slots; bf16: >= 3) and vmcnt range");
   static_assert(MODE == kDown || NB % 2 == 0, "gate/up pairs");
   static_assert(!(SCALED && MODE == kGateUp) || NCOLS == 128, "fp8 gate/up tile = one h scale group");
   static_assert(!SCALED || 128 % WCOLS == 0, "fp8: a wave's columns lie in one 128-wide scale block");
@@ -243,43 +237,27 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void grouped_kernel(GroupedArgs a)
     };
 
     // ---- this wave's share of every stage's chunks ----
-    // Chunk c < A_CH: A stage block mb, instruction i; otherwise B stage
-    // block (cg, j), instruction i.  dst = c * 1 KB in the stage.  The lane's
-    // source is (c < A_CH ? Ab : Wb) + coff[q] + the stage's K offset.
-    // (fp8: A chunks wave * CPA + q and B chunks wave * CPB + q instead)
-    constexpr int NCO = C::SCALED ? 1 : C::CPW;
-    uint32_t coff[NCO];
-    int cpc[NCO];   // bf16: the lane's piece offset inside the stage
-    uint32_t coffA[C::SCALED ? C::CPA : 1], coffB[C::SCALED ? C::CPB : 1];
-    if constexpr (!C::SCALED) {
+    // A chunk c = wave * CPA + q: A stage block c / BV, instruction c % BV;
+    // B chunk c = wave * CPB + q: B stage block (cg, j) = c / BV, instruction
+    // c % BV.  dst = c * 1 KB in the stage's A or B slot.  The lane's source
+    // is Ab + coffA[q] (Wb + coffB[q]) + the stage's K offset; cpcA / cpcB
+    // hold the lane's piece offset inside the stage (bf16 partial stages).
+    uint32_t coffA[C::CPA], coffB[C::CPB];
+    int cpcA[C::CPA], cpcB[C::CPB];
 #pragma unroll
-      for (int q = 0; q < C::CPW; ++q) {
-        const int c = wave * C::CPW + q;
-        const int i = c % C::BV;
-        const int rl = i * C::RPI + lrow;               // row inside the stage block
-        const int pc = (lpiece ^ swz(rl)) * 16;         // this lane's piece, swizzled
-        cpc[q] = pc;
-        if (c < C::A_CH) {
-          coff[q] = a_off((c / C::BV) * 16 + rl) + pc;
-        } else {
-          const int blk = (c - C::A_CH) / C::BV;
-          coff[q] = static_cast<uint32_t>(wrow_of(blk / NB, blk % NB) + rl) * kbytes + pc;
-        }
-      }
-    } else {
+    for (int q = 0; q < C::CPA; ++q) {
+      const int c = wave * C::CPA + q;
+      const int rl = (c % C::BV) * C::RPI + lrow;     // row inside the stage block
+      cpcA[q] = (lpiece ^ swz(rl)) * 16;              // this lane's piece, swizzled
+      coffA[q] = a_off((c / C::BV) * 16 + rl) + cpcA[q];
+    }
 #pragma unroll
-      for (int q = 0; q < C::CPA; ++q) {
-        const int c = wave * C::CPA + q;
-        const int rl = (c % C::BV) * C::RPI + lrow;
-        coffA[q] = a_off((c / C::BV) * 16 + rl) + (lpiece ^ swz(rl)) * 16;
-      }
-#pragma unroll
-      for (int q = 0; q < C::CPB; ++q) {
-        const int c = wave * C::CPB + q;
-        const int rl = (c % C::BV) * C::RPI + lrow;
-        const int blk = c / C::BV;
-        coffB[q] = static_cast<uint32_t>(wrow_of(blk / NB, blk % NB) + rl) * kbytes + (lpiece ^ swz(rl)) * 16;
-      }
+    for (int q = 0; q < C::CPB; ++q) {
+      const int c = wave * C::CPB + q;
+      const int rl = (c % C::BV) * C::RPI + lrow;
+      const int blk = c / C::BV;
+      cpcB[q] = (lpiece ^ swz(rl)) * 16;
+      coffB[q] = static_cast<uint32_t>(wrow_of(blk / NB, blk % NB) + rl) * kbytes + cpcB[q];
     }
     // fp8 scales: waves < ROW_WAVES fetch row scales (lane l: row 64w + l),
     // the other waves the weight-block scales (lane b: block b = cg*NB + j)
@@ -303,35 +281,30 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void grouped_kernel(GroupedArgs a)
       }
     }
 
-    // fp8 split ring: A of stage st in A slot st % DA, B and the scales in
-    // B slot st % DEPTH
+    // A of stage st goes to A slot st % DA, B (and the fp8 scales) to B slot
+    // st % DEPTH.  A partial last stage (bf16, K % 64 = 32) loads the pieces
+    // past the row end from K = 0: valid memory, and compute skips that step
+    // (fp8 K is a multiple of the stage).
+    auto src_off = [&](uint32_t co, int pc, uint32_t kb) -> uint32_t {
+      if constexpr (DT == kBF16)
+        if (kb + pc >= static_cast<uint32_t>(kbytes)) return co - pc;
+      return co + kb;
+    };
     auto issue_a = [&](int st) {
       uint8_t *sl = lds + (st % C::DA) * C::A_BYTES;
-      const uint32_t kb = static_cast<uint32_t>(st) * C::SK;
+      const uint32_t kb = static_cast<uint32_t>(st) * C::RB;
 #pragma unroll
-      for (int q = 0; q < C::CPA; ++q) dma16_to_lds(Ab + (coffA[q] + kb), sl + (wave * C::CPA + q) * 1024);
+      for (int q = 0; q < C::CPA; ++q)   // m-blocks past the rows are not loaded
+        if ((wave * C::CPA + q) / C::BV < nmb)
+          dma16_to_lds(Ab + src_off(coffA[q], cpcA[q], kb), sl + (wave * C::CPA + q) * 1024);
     };
     auto issue_b = [&](int st) {
       uint8_t *sl = lds + C::DA * C::A_BYTES + (st % DEPTH) * C::B_STAGE;
-      const uint32_t kb = static_cast<uint32_t>(st) * C::SK;
+      const uint32_t kb = static_cast<uint32_t>(st) * C::RB;
 #pragma unroll
-      for (int q = 0; q < C::CPB; ++q) dma16_to_lds(Wb + (coffB[q] + kb), sl + (wave * C::CPB + q) * 1024);
-      dma4_to_lds(sbase + (soff + st), sl + C::B_BYTES + wave * 256);
-    };
-    auto issue = [&](int st) {
-      uint8_t *sl = lds + (st % DEPTH) * C::STAGE_BYTES;
-      const uint32_t kb = static_cast<uint32_t>(st) * (C::SK * C::ESZ);
-#pragma unroll
-      for (int q = 0; q < C::CPW; ++q) {
-        const int c = wave * C::CPW + q;
-        const uint8_t *base = c < C::A_CH ? Ab : Wb;
-        // a partial last stage (bf16, K % 64 = 32) loads the pieces past the
-        // row end from K = 0: valid memory, and compute skips that step
-        uint32_t off = coff[q] + kb;
-        if constexpr (DT == kBF16)   // fp8 K is a multiple of the stage
-          if (kb + cpc[q] >= static_cast<uint32_t>(kbytes)) off = coff[q] - cpc[q];
-        dma16_to_lds(base + off, sl + c * 1024);
-      }
+      for (int q = 0; q < C::CPB; ++q)
+        dma16_to_lds(Wb + src_off(coffB[q], cpcB[q], kb), sl + (wave * C::CPB + q) * 1024);
+      if constexpr (C::SCALED) dma4_to_lds(sbase + (soff + st), sl + C::B_BYTES + wave * 256);
     };
 
     constexpr int HALF = NB / 2;
@@ -372,9 +345,9 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void grouped_kernel(GroupedArgs a)
       u32x4_t b[NBR];
     };
     constexpr int BLK = 16 * C::RB;   // bytes of a stage block
-    auto read_stage = [&](int slot, Regs &R) {
-      const uint32_t la = lds_off(lds + slot * C::STAGE_BYTES + mb0 * BLK);
-      const uint32_t lb = lds_off(lds + slot * C::STAGE_BYTES + C::A_BYTES + wn * NB * BLK);
+    auto read_stage = [&](int st, Regs &R) {
+      const uint32_t la = lds_off(lds + (st % C::DA) * C::A_BYTES + mb0 * BLK);
+      const uint32_t lb = lds_off(lds + C::DA * C::A_BYTES + (st % DEPTH) * C::B_STAGE + wn * NB * BLK);
       // bf16 a[s * MBW + mb] / b[s * NB + j]: piece loff[s] of block mb / j;
       // fp8 a[2 mb + h] / b[2 j + h]: piece loff[h]
       static_for<0, NA>([&](auto ic) {
@@ -489,43 +462,47 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void grouped_kernel(GroupedArgs a)
 
     __syncthreads();   // the previous unit is done with every slot
     if constexpr (DT == kBF16) {
-      // ---- bf16: single-barrier ring of DEPTH = 3 LDS slots ----
-      // Step st issues the loads of stage st + 2 (into the slot of stage
-      // st - 1, whose LDS reads every wave finished in step st - 2), waits
-      // for its own loads of stage st + 1, passes the barrier (stage st + 1
-      // has landed for all waves), issues the LDS reads of stage st + 1,
-      // multiplies stage st from registers, then waits for those reads: the
-      // reads of one stage overlap the MFMAs of the previous one.
-      static_assert(DEPTH == 3, "single-barrier ring");
+      // ---- bf16: split ring (A 2 slots, B DEPTH slots), one barrier per
+      // stage, operands read into registers one stage ahead.  Issue order:
+      // B0 A0 B1 .. B(D-2) [stage 0 read] A1 B(D-1) | A2 BD | A3 B(D+1) | ...  Step st
+      // waits for its own loads up to A(st+1) (only B(st+D-1) was issued
+      // after it; B(st+1) precedes it), passes the barrier -- every wave's
+      // stage st+1 has landed, and every wave has read stage st into
+      // registers -- refills the slots of stage st with A(st+2) and
+      // B(st+D), issues the LDS reads of stage st+1, multiplies stage st
+      // from registers, then waits for those reads: the reads of one stage
+      // overlap the MFMAs of the previous one. ----
       Regs RA, RB;
       auto step = [&](int st, Regs &cur, Regs &next) {
-        if (st + 2 < nstage) {
-          issue(st + 2);
-          wait_vm<C::LPS>();
-        } else {
-          wait_vm<0>();
-        }
+        if (st + DEPTH - 1 < nstage) wait_vm<C::LB>();
+        else wait_vm<0>();
         ring_barrier();
+        if (st + 2 < nstage) issue_a(st + 2);
+        if (st + DEPTH < nstage) issue_b(st + DEPTH);
         if (rows_on) {
-          if (st + 1 < nstage) read_stage((st + 1) % DEPTH, next);
+          if (st + 1 < nstage) read_stage(st + 1, next);
           __builtin_amdgcn_sched_barrier(0);
           compute(st, cur);
           __builtin_amdgcn_sched_barrier(0);
           if (st + 1 < nstage) lds_wait(next);
         }
       };
-      issue(0);
-      if (nstage > 1) {
-        issue(1);
-        wait_vm<C::LPS>();
-      } else {
-        wait_vm<0>();
-      }
+      issue_b(0);
+      issue_a(0);
+      static_for<1, DEPTH - 1>([&](auto ic) {
+        if (decltype(ic)::value < nstage) issue_b(decltype(ic)::value);
+      });
+      // issued after A(0): B(1 .. D-2), where they exist (a wave's A loads
+      // per stage vary with the tile's rows, so waits only ever count B loads)
+      if (nstage >= DEPTH - 1) wait_vm<(DEPTH - 2) * C::LB>();
+      else wait_vm<0>();
       ring_barrier();   // stage 0 landed
       if (rows_on) {
         read_stage(0, RA);
         lds_wait(RA);
       }
+      if (nstage > 1) issue_a(1);
+      if (DEPTH - 1 < nstage) issue_b(DEPTH - 1);
       for (int st = 0; st < nstage; st += 2) {
         step(st, RA, RB);
         if (st + 1 >= nstage) break;
@@ -681,8 +658,8 @@ hipError_t launch_grouped_gateup(const Dims &d, const Inputs &in,
   if (d.wdt == kBF16) {
     // 256-row tiles (64 h columns, 2 x 4 waves) when experts average more
     // than 96 rows, else 96-row tiles (128 h columns, 4 column waves)
-    if (big_tiles(d)) return launch_one<kBF16, kGateUp, 4, 2, 4, 4, 3, 64>(ga, s);
-    return launch_one<kBF16, kGateUp, 4, 4, 1, 6, 3, 64>(ga, s);
+    if (big_tiles(d)) return launch_one<kBF16, kGateUp, 4, 2, 4, 4, 4, 64>(ga, s);
+    return launch_one<kBF16, kGateUp, 4, 4, 1, 6, 4, 64>(ga, s);
   }
   // fp8: 128 h columns = one h scale group (4 column waves x 2 gate + 2 up
   // blocks; 4 x 4 block tiles per wave keep the scale promotion cheap)
@@ -695,7 +672,7 @@ hipError_t launch_grouped_down(const Dims &d, const Inputs &in, const Work &w,
   const GroupedArgs ga{d, in, w, 0, 0};
   if (d.wdt == kBF16) {
     if (big_tiles(d)) return launch_one<kBF16, kDown, 4, 4, 2, 4, 3, 64>(ga, s);   // 128 rows x 256 columns, 8 waves
-    return launch_one<kBF16, kDown, 4, 4, 1, 6, 3, 64>(ga, s);
+    return launch_one<kBF16, kDown, 4, 4, 1, 6, 4, 64>(ga, s);
   }
   // 192 (128) rows x 256 columns, 8 waves
   if (big_tiles(d)) return launch_one<kFP8, kDown, 4, 4, 2, 6, 3, 128>(ga, s);
