@@ -117,6 +117,26 @@ def test_ragged_bf16_all(path):
     run_case(RAGGED_BF16, path=path)
 
 
+# More than 96 rows per expert on average: the large-tile configurations
+# (bf16 gate/up 256-row tiles, bf16 down 128-row, fp8 192-row tiles), with
+# experts of 61-368 rows, so some span two or three M tiles and the last
+# tile of each is partly filled.
+BIG_FP8 = synth.Workload("big_fp8", m=600, hidden=256, experts=8, topk=2, inter=256,
+                         shared_inter=128, dtype="fp8", gating="sigmoid", routed_scale=2.5,
+                         seed=37, zipf_alpha=0.05)
+BIG_BF16 = synth.Workload("big_bf16", m=600, hidden=288, experts=8, topk=2, inter=96,
+                          shared_inter=160, dtype="bf16", gating="sigmoid", routed_scale=1.0,
+                          seed=38, zipf_alpha=0.05)
+
+
+@pytest.mark.parametrize("wl", [BIG_FP8, BIG_BF16], ids=["fp8", "bf16"])
+def test_large_tiles_all(wl):
+    rep, *_, (out, idx, w, dbg) = run_case(wl, path="grouped")
+    counts = to_np(dbg["counts"])
+    assert wl.m * wl.topk > 96 * wl.experts       # the large-tile configurations
+    assert counts.max() > 256 and counts.min() < 96
+
+
 @pytest.mark.parametrize("m", [1, 7, 13, 16])
 def test_small_m_with_shared_expert(m):
     run_case(RAGGED_BF16, path="small_m", m=m)
