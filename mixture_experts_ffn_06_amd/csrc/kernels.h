@@ -61,10 +61,13 @@ struct Work {
 };
 
 // permute.hip: one block below kPermMultiMin pairs, else chunks of
-// kPermChunk pairs (needs Work::perm_blk of permute_chunks(d) * E ints)
-constexpr int kPermChunk = 4096;
+// perm_chunk(te) pairs, about eight of them (needs Work::perm_blk of
+// permute_chunks(te) * E ints)
 constexpr int kPermMultiMin = 8192;
-int permute_chunks(const Dims &d);
+__host__ __device__ inline int perm_chunk(long te) { return te >= 32768 ? 4096 : (te >= 16384 ? 2048 : 1024); }
+__host__ __device__ inline int permute_chunks(long te) {
+  return te >= kPermMultiMin ? static_cast<int>((te + perm_chunk(te) - 1) / perm_chunk(te)) : 0;
+}
 hipError_t launch_permute(const Dims &d, const int *topk_idx, const Work &w,
                           hipStream_t s);
 

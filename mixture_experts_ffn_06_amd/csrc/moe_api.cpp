@@ -72,8 +72,7 @@ Layout layout(const moe_plan_s &p, int m) {
   L.size[Layout::kLrank] = te * 4;
   L.size[Layout::kActive] = E * 4;
   L.size[Layout::kNactive] = 4;
-  L.size[Layout::kPermBlk] = te >= static_cast<size_t>(moe::kPermMultiMin)
-                                 ? (te + moe::kPermChunk - 1) / moe::kPermChunk * E * 4 : 0;
+  L.size[Layout::kPermBlk] = static_cast<size_t>(moe::permute_chunks(static_cast<long>(te))) * E * 4;
   L.size[Layout::kXq] = fp8 ? m * H : 0;
   L.size[Layout::kSx] = fp8 ? m * (H / 128) * 4 : 0;
   L.size[Layout::kH] = te * I * hb;

@@ -34,7 +34,7 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Many pairs (te >= kPermMultiMin): the same sort over chunks of kPermChunk
+// Many pairs (te >= kPermMultiMin): the same sort over chunks of `chunk`
 // consecutive pairs, one block per chunk, in three launches:
 //   1. each block counts its chunk's pairs per expert (blk[b][e]);
 //   2. one block turns the counts into expert totals, offsets, the active
@@ -45,11 +45,11 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
 // Chunks are contiguous ranges of p in chunk order, so the result is the
 // same stable permutation as the single-block sort.
 __global__ __launch_bounds__(kPermThreads) void permute_hist_kernel(const int *__restrict__ topk_idx, int te,
-                                                                    int E, int *__restrict__ blk) {
+                                                                    int E, int chunk, int *__restrict__ blk) {
   extern __shared__ int hist[];   // [E]
   for (int i = threadIdx.x; i < E; i += kPermThreads) hist[i] = 0;
   __syncthreads();
-  const int c0 = blockIdx.x * kPermChunk, c1 = min(te, c0 + kPermChunk);
+  const int c0 = blockIdx.x * chunk, c1 = min(te, c0 + chunk);
   for (int p = c0 + threadIdx.x; p < c1; p += kPermThreads) atomicAdd(&hist[topk_idx[p]], 1);
   __syncthreads();
   for (int i = threadIdx.x; i < E; i += kPermThreads) blk[static_cast<size_t>(blockIdx.x) * E + i] = hist[i];
@@ -75,18 +75,14 @@ __global__ __launch_bounds__(kPermThreads) void permute_scan_kernel(int nblk, in
 }
 
 __global__ __launch_bounds__(kPermThreads) void permute_scatter_kernel(
-    const int *__restrict__ topk_idx, int te, int E, const int *__restrict__ blk,
+    const int *__restrict__ topk_idx, int te, int E, int chunk, const int *__restrict__ blk,
     int *__restrict__ sorted_pair, int *__restrict__ slot_of_pair, int *__restrict__ lrank) {
   extern __shared__ int wcnt[];   // [kPermWaves][E]
-  const int c0 = blockIdx.x * kPermChunk, c1 = min(te, c0 + kPermChunk);
+  const int c0 = blockIdx.x * chunk, c1 = min(te, c0 + chunk);
   chunk_ranks(topk_idx, c0, c1, E, wcnt, lrank);
   const int x = threadIdx.x;
   chunk_bases(E, wcnt, x < E ? blk[static_cast<size_t>(blockIdx.x) * E + x] : 0);
   chunk_scatter(topk_idx, c0, c1, E, wcnt, lrank, sorted_pair, slot_of_pair);
-}
-
-int permute_chunks(const Dims &d) {
-  return d.te >= kPermMultiMin ? (d.te + kPermChunk - 1) / kPermChunk : 0;
 }
 
 hipError_t launch_permute(const Dims &d, const int *topk_idx, const Work &w,
@@ -102,7 +98,7 @@ hipError_t launch_permute(const Dims &d, const int *topk_idx, const Work &w,
     }
     attr = true;
   }
-  const int nblk = permute_chunks(d);
+  const int nblk = permute_chunks(d.te), chunk = perm_chunk(d.te);
   if (nblk == 0) {
     hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(kPermThreads), lds, s, topk_idx,
                        d.te, d.E, w.counts, w.offsets, w.sorted_pair, w.slot_of_pair,
@@ -110,11 +106,11 @@ hipError_t launch_permute(const Dims &d, const int *topk_idx, const Work &w,
     return hipGetLastError();
   }
   hipLaunchKernelGGL(permute_hist_kernel, dim3(nblk), dim3(kPermThreads), d.E * sizeof(int), s,
-                     topk_idx, d.te, d.E, w.perm_blk);
+                     topk_idx, d.te, d.E, chunk, w.perm_blk);
   hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(kPermThreads), 0, s, nblk, d.E, w.perm_blk,
                      w.counts, w.offsets, w.active, w.nactive);
   hipLaunchKernelGGL(permute_scatter_kernel, dim3(nblk), dim3(kPermThreads), lds, s, topk_idx, d.te, d.E,
-                     w.perm_blk, w.sorted_pair, w.slot_of_pair, w.lrank);
+                     chunk, w.perm_blk, w.sorted_pair, w.slot_of_pair, w.lrank);
   return hipGetLastError();
 }
 
