@@ -152,9 +152,11 @@ hipError_t launch_router(const Dims &d, const Inputs &in, const Work &w,
     }
     if (d.m <= 64) return launch_router_mfma<1, 1>(d, in, w, s);
     // 32 x 64 tiles unless they leave CUs idle (then 16 x 32: more re-reads
-    // of x and Wr, but four times the blocks)
+    // of x and Wr, but four times the blocks), 64 x 64 when those fill them
     const long big_tiles = static_cast<long>((d.E + 63) / 64) * ((d.m + 31) / 32);
     if (big_tiles < 256) return launch_router_mfma<1, 2>(d, in, w, s);
+    // 64 x 64 tiles once they alone fill the CUs: half the re-reads of Wr
+    if (static_cast<long>((d.E + 63) / 64) * ((d.m + 63) / 64) >= 256) return launch_router_mfma<4, 4>(d, in, w, s);
     return launch_router_mfma<2, 4>(d, in, w, s);
   }
   dim3 grid((d.E + kRouterWaves - 1) / kRouterWaves,
