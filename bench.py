@@ -254,7 +254,7 @@ def main():
     # the kernel's bound: whichever of its bytes and flops takes longer at peak
     mfma_peak = MFMA_PEAK_TFLOPS[wl.dtype]
     mfma_bound = cnt[dom]["flops"] / (mfma_peak * 1e12) > cnt[dom]["bytes"] / (HBM_PEAK_GBPS * 1e9)
-    kernel_names = {"small_m": "sm_gateup_kernel", "grouped": "grouped_kernel<gateup>",
+    kernel_names = {"small_m": "sm_kernel<gateup>", "grouped": "grouped_kernel<gateup>",
                     "simple": "simple_gateup_kernel"}
     path = layers[0].plan.path_for(m)
     result = {
