@@ -322,16 +322,20 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void grouped_kernel(GroupedArgs a)
     auto mrow = [&](int mb) { return mfirst + mstep * mb; };
     const bool rows_on = mfirst < nmb;        // any of its rows exist
 
-    // lane L reads row L % 16 of a stage block, K slice L / 16 of each MFMA
-    // step, at the swizzled positions of its 16-byte pieces: bf16 step s is
-    // logical piece 4 s + L / 16 (loff[s]); fp8 (one step) pieces 2 (L / 16)
-    // and 2 (L / 16) + 1 (loff[0], loff[1]).
+    // lane L reads row L % 16 of a stage block at the swizzled positions of
+    // its 16-byte pieces: bf16 step s is logical piece 4 s + L / 16 (loff[s]);
+    // fp8 (one 128-wide step, 32 bytes per lane) takes pieces L / 16 and
+    // 4 + L / 16 (loff[0], loff[1]).  Any split of the 128 K bytes over the
+    // lanes gives the same product as long as A and B use the same one; this
+    // one makes each read instruction touch the same pieces as a bf16 read,
+    // which the swizzle keeps free of LDS bank conflicts (pieces 2 L/16 and
+    // 2 L/16 + 1 conflicted).
     const int rr16 = lane & 15, kg = lane >> 4;
     constexpr int NOFF = DT == kBF16 ? C::STEPS : 2;
     uint32_t loff[NOFF];
 #pragma unroll
     for (int s = 0; s < NOFF; ++s) {
-      const int piece = DT == kBF16 ? 4 * s + kg : 2 * kg + s;
+      const int piece = 4 * s + kg;
       loff[s] = rr16 * C::RB + ((piece ^ swz(rr16)) * 16);
     }
 
