@@ -175,7 +175,7 @@ hipError_t launch_router(const Dims &d, const Inputs &in, const Work &w,
 // launches instead of three.  (One CU pulls only a small share of HBM
 // bandwidth, so the partials that single block reads are kept few.)
 constexpr int kFusedThreads = 1024;
-constexpr int kRouterBlocksTarget = 8;
+constexpr int kRouterBlocksTarget = 32;
 
 bool route_fused_ok(const Dims &d) { return d.wdt != kF32 && d.m <= 16; }
 
