@@ -37,15 +37,23 @@ def dense_mask(logits: np.ndarray, k: int, gating: str, bias=None,
     """``M[t, e]`` = gate weight of expert e for token t, 0 if not selected."""
     m, E = logits.shape
     M = np.zeros((m, E))
+    b = None if bias is None else np.asarray(bias, np.float32).astype(np.float64)
     for t in range(m):
         l = logits[t]
         if gating == "softmax":
-            # ranking by softmax probability == ranking by logit
-            rank_key = l.copy()
+            if b is None:
+                # ranking by softmax probability == ranking by logit
+                rank_key = l.copy()
+            else:
+                e = np.exp(l - l.max())
+                rank_key = e / e.sum() + b
         else:
-            rank_key = 1.0 / (1.0 + np.exp(-l))
-            if bias is not None:
-                rank_key = rank_key + np.asarray(bias, np.float32).astype(np.float64)
+            if gating == "sigmoid":
+                rank_key = 1.0 / (1.0 + np.exp(-l))
+            else:   # sqrtsoftplus; the tiny inputs keep e^l finite
+                rank_key = np.sqrt(np.log1p(np.exp(l)))
+            if b is not None:
+                rank_key = rank_key + b
         order = np.lexsort((np.arange(E), -rank_key))
         sel = order[:k]
         if gating == "softmax":
@@ -57,7 +65,10 @@ def dense_mask(logits: np.ndarray, k: int, gating: str, bias=None,
                 z = l - l.max()
                 w = (np.exp(z) / np.exp(z).sum())[sel]
         else:
-            s = 1.0 / (1.0 + np.exp(-l[sel]))
+            if gating == "sigmoid":
+                s = 1.0 / (1.0 + np.exp(-l[sel]))
+            else:
+                s = np.sqrt(np.log1p(np.exp(l[sel])))
             w = s / s.sum() if renormalize else s
         M[t, sel] = w * scale
     return M
@@ -66,14 +77,18 @@ def dense_mask(logits: np.ndarray, k: int, gating: str, bias=None,
 def dense_forward(xt: np.ndarray, logits: np.ndarray, k: int, gating: str,
                   W13: np.ndarray, W2: np.ndarray, inter: int, dtype: str,
                   bias=None, scale: float = 1.0, shared=None,
-                  shared_inter: int = 0, block: int = 128) -> np.ndarray:
+                  shared_inter: int = 0, block: int = 128,
+                  renormalize: bool = True, x_gate=None,
+                  gate=None) -> np.ndarray:
     """Dense fp64 layer output ``[m, H]`` (unrounded).
 
     ``xt [m,H]``: expert input values (dequantised for fp8);
     ``logits [m,E]``: router logits; ``W13 [E,2I,H]``, ``W2 [E,H,I]``:
-    exact weight values; ``shared``: ``(W13s [2Is,H], W2s [H,Is])`` or None.
+    exact weight values; ``shared``: ``(W13s [2Is,H], W2s [H,Is])`` or None;
+    ``gate [H]`` with ``x_gate [m,H]`` (the unquantised input): the shared
+    row of token t is scaled by ``1 / (1 + exp(-x_gate[t] . gate))``.
     """
-    M = dense_mask(logits, k, gating, bias, scale)
+    M = dense_mask(logits, k, gating, bias, scale, renormalize)
     g = np.einsum("th,eih->tei", xt, W13[:, :inter, :])
     u = np.einsum("th,eih->tei", xt, W13[:, inter:, :])
     a = g / (1.0 + np.exp(-g)) * u
@@ -85,5 +100,8 @@ def dense_forward(xt: np.ndarray, logits: np.ndarray, k: int, gating: str,
         gs = xt @ S13[:shared_inter].T
         us = xt @ S13[shared_inter:].T
         hs = _round_h(gs / (1.0 + np.exp(-gs)) * us, dtype, block)
-        out = out + _store_y(hs @ S2.T, dtype)
+        ys = _store_y(hs @ S2.T, dtype)
+        if gate is not None:
+            ys = ys / (1.0 + np.exp(-(x_gate @ gate)))[:, None]
+        out = out + ys
     return out

@@ -20,6 +20,11 @@ notes of the repository):
   "the bias selects experts, weights gather pre-bias scores"), weights are
   the unbiased sigmoid scores renormalised then multiplied by the routed
   scaling factor;
+* sqrtsoftplus gating (page 3, top-k dispatch: the DeepSeek-V4 scoring
+  function, with the same correction bias) scores ``sqrt(softplus(l))``
+  with ``softplus(l) = ln(1 + e^l)`` and is otherwise handled like sigmoid;
+* softmax with a correction bias (page 3, top-k dispatch, the softmax +
+  bias branch) ranks ``p + bias`` and weights the unbiased probabilities;
 * the routing weight multiplies at the combine (page 3, step 7
   ``moe_unpermute_reduce_indexed``), not inside the SwiGLU;
 * SwiGLU is ``silu(w1 x) * (w3 x)`` with no clamp; the expert intermediate is
@@ -30,7 +35,12 @@ notes of the repository):
   sorted BF16 ``expert_down_out``), for the shared expert too; the fp32
   layer keeps it in fp32;
 * the shared expert is added with weight 1 (page 2, ``MoeV41::forward``:
-  routed and shared rows are summed into one fp32 accumulator, cleared first);
+  routed and shared rows are summed into one fp32 accumulator, cleared first),
+  or, when the layer has a shared-expert gate vector g, with weight
+  ``sigmoid(x . g)`` per token (page 3, step 8, the shared-expert blend: a
+  per-token logistic factor of the input's dot product with a gate vector
+  scales the shared row).  The dot product takes the layer input as given,
+  never its fp8 quantisation;
 * the output is rounded once, from the fp64 sum, to the activation format.
 """
 from __future__ import annotations
@@ -52,7 +62,7 @@ class LayerSpec:
     inter: int
     shared_inter: int
     dtype: str            # "f32" | "bf16" | "fp8"
-    gating: str           # "softmax" | "sigmoid"
+    gating: str           # "softmax" | "sigmoid" | "sqrtsoftplus"
     routed_scale: float = 1.0
     renormalize: bool = True
     block: int = 128
@@ -109,6 +119,10 @@ def gate_scores(logits: np.ndarray, gating: str):
         return p, p
     if gating == "sigmoid":
         s = 1.0 / (1.0 + np.exp(-logits))
+        return s, s
+    if gating == "sqrtsoftplus":
+        # softplus(l) = ln(e^0 + e^l), evaluated without overflow
+        s = np.sqrt(np.logaddexp(0.0, logits))
         return s, s
     raise ValueError(gating)
 
@@ -223,7 +237,8 @@ def forward(spec: LayerSpec, x, router_w, w13, w2, w13_scale=None,
     likewise.  ``w13[e]``, ``w2[e]`` (and ``w13_scale[e]``, ``w2_scale[e]``
     for fp8) are indexed per expert, so callers may pass lazy containers.
     ``shared`` is ``None`` or a dict with ``w13, w2`` (+ ``w13_scale,
-    w2_scale``).  ``bias [E]`` fp32 is a selection-only bias.
+    w2_scale``, and ``gate [H]`` in the activation format for the
+    sigmoid-gated blend).  ``bias [E]`` fp32 is a selection-only bias.
 
     ``tokens``: optional sorted token subset for which expert outputs and
     ``out`` are evaluated (gating and permutation are always computed for
@@ -288,6 +303,10 @@ def forward(spec: LayerSpec, x, router_w, w13, w2, w13_scale=None,
         s2 = weight_values(shared["w2"], shared.get("w2_scale"), spec.dtype, B)
         ysh, _, _, _ = expert_mlp(xt[tok], s13, s2, spec.shared_inter,
                                   spec.dtype, B)
+        if shared.get("gate") is not None:
+            gl = xv[tok] @ act_values(shared["gate"], act)
+            res["shared_gate"] = 1.0 / (1.0 + np.exp(-gl))
+            ysh = res["shared_gate"][:, None] * ysh
         acc += ysh
     res["tokens"] = tok
     res["out64"] = acc

@@ -20,6 +20,8 @@ Draw recipe (all seeds are fixed integers):
 * expert e   ~ N(0, 0.02), torch generator seeded from ``(seed, 1, e)``; drawn
   one expert at a time on the device that will hold it.
 * shared     ~ N(0, 0.02), torch generator seeded from ``(seed, 2, 0)``.
+* shared gate (workloads with a gated shared-expert blend): a ``[H]`` vector
+  ~ N(0, 0.02), ``default_rng([seed, 5])``, stored like x.
 * selection bias (skewed workload only): a seeded permutation assigns each
   expert a popularity rank r in 1..E; ``b_1 = 0`` and, for r >= 2,
   ``b_r = -head - alpha * s * ln r``, i.e. ``alpha * ln(p_r / p_1)`` for
@@ -41,7 +43,7 @@ import numpy as np
 import torch
 
 __all__ = ["Workload", "WORKLOADS", "make_inputs", "draw_x", "draw_router",
-           "draw_bias", "expert_seed"]
+           "draw_bias", "draw_shared_gate", "expert_seed"]
 
 
 @dataclass(frozen=True)
@@ -55,7 +57,7 @@ class Workload:
     inter: int             # I (per routed expert)
     shared_inter: int      # I_s, 0 = no shared expert
     dtype: str             # "f32" | "bf16" | "fp8"
-    gating: str            # "softmax" | "sigmoid"
+    gating: str            # "softmax" | "sigmoid" | "sqrtsoftplus"
     routed_scale: float    # multiplier after renormalisation
     seed: int
     router_subseed: int = 0
@@ -63,6 +65,8 @@ class Workload:
     zipf_s: float = 1.2
     zipf_head: float = 0.0   # extra gap below the most popular expert
     block: int = 128         # fp8 block edge
+    renormalize: bool = True   # divide the selected weights by their sum
+    shared_gate: bool = False  # shared expert scaled by sigmoid(x . g)
 
     def replace(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
@@ -155,6 +159,13 @@ def draw_bias(wl: Workload, alpha: float | None = None) -> np.ndarray | None:
     return b.astype(np.float32)
 
 
+def draw_shared_gate(wl: Workload) -> np.ndarray:
+    """fp32 N(0, 0.02) shared-expert gate vector ``[H]`` (before storage
+    rounding)."""
+    return (np.float32(0.02) *
+            _np_rng(wl.seed, 5).standard_normal(wl.hidden, dtype=np.float32))
+
+
 def _store_act(a: np.ndarray, dtype: str, device) -> torch.Tensor:
     t = torch.from_numpy(np.ascontiguousarray(a))
     if dtype == "f32":
@@ -193,7 +204,8 @@ def make_inputs(wl: Workload, device="cpu", m: int | None = None) -> dict:
 
     Keys: ``x [m,H]``, ``router_w [E,H]``, ``w13 [E,2I,H]``, ``w2 [E,H,I]``,
     ``w13_scale [E,2I/128,H/128]`` / ``w2_scale [E,H/128,I/128]`` (fp8 only),
-    ``shared_w13 [2Is,H]``, ``shared_w2 [H,Is]`` (+ scales), ``bias [E]``.
+    ``shared_w13 [2Is,H]``, ``shared_w2 [H,Is]`` (+ scales), ``shared_gate
+    [H]`` (activation format), ``bias [E]``.
     Absent entries are None.  ``m`` takes a prefix of the token draw.
     """
     device = torch.device(device)
@@ -225,7 +237,7 @@ def make_inputs(wl: Workload, device="cpu", m: int | None = None) -> dict:
             s2[e].copy_(sc2)
     out.update(w13=w13, w2=w2, w13_scale=s13, w2_scale=s2)
     out.update(shared_w13=None, shared_w2=None, shared_w13_scale=None,
-               shared_w2_scale=None)
+               shared_w2_scale=None, shared_gate=None)
     if wl.shared_inter > 0:
         Is = wl.shared_inter
         a = _draw_matrix(expert_seed(wl.seed, 2, 0), 3 * Is, H, device)
@@ -233,4 +245,6 @@ def make_inputs(wl: Workload, device="cpu", m: int | None = None) -> dict:
         c2, sc2 = _store_weight(a[2 * Is:].t().contiguous(), wl.dtype, wl.block)
         out.update(shared_w13=c13.contiguous(), shared_w2=c2.contiguous(),
                    shared_w13_scale=sc13, shared_w2_scale=sc2)
+        if wl.shared_gate:
+            out["shared_gate"] = _store_act(draw_shared_gate(wl), wl.act_dtype, device)
     return out

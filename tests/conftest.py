@@ -53,7 +53,8 @@ def oracle_inputs(wl, inp, lazy=False):
     spec = LayerSpec(hidden=wl.hidden, experts=wl.experts, topk=wl.topk,
                      inter=wl.inter, shared_inter=wl.shared_inter,
                      dtype=wl.dtype, gating=wl.gating,
-                     routed_scale=wl.routed_scale, block=wl.block)
+                     routed_scale=wl.routed_scale, renormalize=wl.renormalize,
+                     block=wl.block)
     wrap = LazyExperts if lazy else to_np
     kw = dict(x=to_np(inp["x"]), router_w=to_np(inp["router_w"]),
               w13=wrap(inp["w13"]), w2=wrap(inp["w2"]),
@@ -64,7 +65,8 @@ def oracle_inputs(wl, inp, lazy=False):
         kw["shared"] = {"w13": to_np(inp["shared_w13"]),
                         "w2": to_np(inp["shared_w2"]),
                         "w13_scale": to_np(inp["shared_w13_scale"]),
-                        "w2_scale": to_np(inp["shared_w2_scale"])}
+                        "w2_scale": to_np(inp["shared_w2_scale"]),
+                        "gate": to_np(inp.get("shared_gate"))}
     return spec, kw
 
 

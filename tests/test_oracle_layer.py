@@ -3,9 +3,11 @@
 The sparse oracle (``oracle.layer``) is pinned against:
 
 * brute-force dense evaluation (``oracle.dense``: every expert on every
-  token, masked by the gate weights) on the tiny fp32 workload and on 60
+  token, masked by the gate weights) on the tiny fp32 workload, on 60
   random tiny layers covering fp32 / bf16 / fp8, softmax / sigmoid, a
-  selection bias, k = 1 and k = E, and a shared expert;
+  selection bias, k = 1 and k = E, and a shared expert, and on 30 more
+  covering the gating variants (sqrtsoftplus, softmax with a correction
+  bias, no renormalisation, the sigmoid-gated shared blend);
 * closed forms of the gating (renormalised softmax == softmax of the
   selected logits; weights sum to the routed scale; k = E gives the full
   softmax; x = 0 gives experts 0..k-1 with equal weights);
@@ -56,6 +58,8 @@ def _values(wl, inp):
     if wl.shared_inter:
         out["shared"] = (wt(inp["shared_w13"], inp["shared_w13_scale"]),
                          wt(inp["shared_w2"], inp["shared_w2_scale"]))
+    if inp.get("shared_gate") is not None:
+        out["gate"] = act(inp["shared_gate"])
     return out
 
 
@@ -65,7 +69,8 @@ def _dense(wl, inp):
     return dense_forward(v["xt"], logits, wl.topk, wl.gating, v["W13"], v["W2"],
                          wl.inter, wl.dtype, bias=to_np(inp["bias"]),
                          scale=wl.routed_scale, shared=v.get("shared"),
-                         shared_inter=wl.shared_inter, block=wl.block)
+                         shared_inter=wl.shared_inter, block=wl.block,
+                         renormalize=wl.renormalize, x_gate=v["x"], gate=v.get("gate"))
 
 
 def _oracle(wl, inp, **kw):
@@ -101,6 +106,30 @@ def _random_workloads(n=60):
     return out
 
 
+def _variant_workloads(n=30):
+    """Gating variants: sqrtsoftplus and softmax with a correction bias, no
+    renormalisation, and the sigmoid-gated shared-expert blend."""
+    rng = np.random.default_rng(78)
+    out = []
+    for i in range(n):
+        dt = ["f32", "bf16", "fp8"][i % 3]
+        sizes = [128, 256] if dt == "fp8" else [32, 64, 128]
+        E = int(rng.integers(2, 17))
+        k = int(rng.integers(1, E + 1))
+        gating = ["sqrtsoftplus", "softmax", "sigmoid"][(i // 3) % 3]
+        out.append(synth.Workload(
+            f"var{i}", m=int(rng.integers(1, 9)), hidden=int(rng.choice(sizes)),
+            experts=E, topk=k, inter=int(rng.choice(sizes)),
+            shared_inter=int(rng.choice(sizes)) if i % 4 != 3 else 0,
+            dtype=dt, gating=gating, routed_scale=float(rng.choice([1.0, 1.5, 2.5])),
+            seed=2000 + i,
+            # softmax probabilities are ~1/E: a bias of the same order
+            zipf_alpha=(0.02 if gating == "softmax" else 0.3) if i % 2 == 0 else 0.0,
+            zipf_head=0.0 if gating == "softmax" else 0.2,
+            renormalize=(i % 5) != 1, shared_gate=(i % 4) in (0, 1)))
+    return out
+
+
 def test_tiny_workload_sparse_equals_dense():
     wl = synth.WORKLOADS["tiny_f32"]
     inp = synth.make_inputs(wl)
@@ -118,7 +147,77 @@ def test_random_tiny_layers_sparse_equals_dense(wl):
     assert _rel(r["out64"], d) < 1e-12
 
 
+@pytest.mark.parametrize("wl", _variant_workloads(), ids=lambda w: w.name)
+def test_gating_variants_sparse_equals_dense(wl):
+    inp = synth.make_inputs(wl)
+    r = _oracle(wl, inp)
+    assert _rel(r["out64"], _dense(wl, inp)) < 1e-12
+
+
 # --------------------------------------------------------------- gating ---
+
+def test_sqrtsoftplus_closed_forms():
+    """sqrt(softplus): s(0)^2 = ln 2; s(l)^2 - s(-l)^2 = l (softplus(l) -
+    softplus(-l) = l); s(l)^2 -> l for large l and -> e^l for very negative
+    l; ranking equals logit ranking."""
+    l = np.linspace(-30.0, 30.0, 601)[None, :]
+    _, s = OL.gate_scores(l, "sqrtsoftplus")
+    _, s0 = OL.gate_scores(np.zeros((1, 1)), "sqrtsoftplus")
+    assert s0[0, 0] == pytest.approx(np.sqrt(np.log(2.0)), rel=1e-15)
+    _, sn = OL.gate_scores(-l, "sqrtsoftplus")
+    assert np.max(np.abs(s ** 2 - sn ** 2 - l)) < 1e-12
+    _, big = OL.gate_scores(np.array([[60.0, -60.0]]), "sqrtsoftplus")
+    assert big[0, 0] ** 2 == pytest.approx(60.0, rel=1e-15)
+    assert big[0, 1] ** 2 == pytest.approx(np.exp(-60.0), rel=1e-12)
+    rng = np.random.default_rng(5)
+    lg = rng.standard_normal((20, 32))
+    idx, _ = OL.top_k(OL.gate_scores(lg, "sqrtsoftplus")[1], 6)
+    for t in range(20):
+        assert np.array_equal(idx[t], np.lexsort((np.arange(32), -lg[t]))[:6])
+
+
+def test_softmax_correction_bias_selects_but_does_not_weight():
+    """A large bias on experts {3, 9} forces them in with k = 2; the weights
+    are the unbiased softmax probabilities (renormalised: the softmax of the
+    two logits; not renormalised: scipy's softmax over all experts)."""
+    from scipy.special import softmax
+    rng = np.random.default_rng(6)
+    lg = rng.standard_normal((10, 16))
+    b = np.zeros(16)
+    b[[3, 9]] = 1.0
+    p, score = OL.gate_scores(lg, "softmax")
+    idx, _ = OL.top_k(score + b[None, :], 2)
+    assert all(set(row) == {3, 9} for row in idx.tolist())
+    w = OL.gate_weights(p, idx, True, 1.0)
+    assert np.allclose(w, softmax(np.take_along_axis(lg, idx.astype(np.int64), 1), axis=1),
+                       rtol=1e-14, atol=0)
+    w_raw = OL.gate_weights(p, idx, False, 1.0)
+    assert np.allclose(w_raw, np.take_along_axis(softmax(lg, axis=1), idx.astype(np.int64), 1),
+                       rtol=1e-14, atol=0)
+
+
+def test_shared_gate_zero_halves_the_shared_expert():
+    """g = 0 gives the factor sigmoid(0) = 1/2 exactly: out = routed +
+    (ungated - routed) / 2."""
+    wl = synth.Workload("sg", m=7, hidden=64, experts=5, topk=2, inter=32,
+                        shared_inter=64, dtype="bf16", gating="softmax",
+                        routed_scale=1.0, seed=12, shared_gate=True)
+    inp = synth.make_inputs(wl)
+    spec, args = oracle_inputs(wl, inp)
+    gated0 = dict(args, shared=dict(args["shared"], gate=np.zeros(64, np.uint16)))
+    ungated = dict(args, shared=dict(args["shared"], gate=None))
+    routed = dict(args, shared=None)
+    o0 = OL.forward(spec, **gated0)["out64"]
+    ou = OL.forward(spec, **ungated)["out64"]
+    orr = OL.forward(spec, **routed)["out64"]
+    assert np.max(np.abs(o0 - (orr + 0.5 * (ou - orr)))) < 1e-12 * np.abs(ou).max()
+    # the factor uses the unquantised input and the stored gate values
+    from scipy.special import expit
+    r = OL.forward(spec, **args)
+    xg = bf16_decode(to_np(inp["x"])) @ bf16_decode(to_np(inp["shared_gate"]))
+    assert np.allclose(r["shared_gate"], expit(xg), rtol=1e-14, atol=0)
+
+
 
 def test_softmax_renormalised_equals_softmax_of_selected(np_rng):
     logits = np_rng.standard_normal((50, 16)) * 2
@@ -322,6 +421,57 @@ def test_planted_dropped_shared_expert_is_caught(monkeypatch):
     bad = 0
     for wl in _random_workloads(12):
         if wl.shared_inter == 0:
+            continue
+        inp = synth.make_inputs(wl)
+        bad += _rel(_oracle(wl, inp)["out64"], _dense(wl, inp)) > 1e-9
+    assert bad > 0
+
+
+def _variant_mismatch(monkeypatch, attr, fn, n=12):
+    monkeypatch.setattr(OL, attr, fn)
+    bad = 0
+    for wl in _variant_workloads(n):
+        inp = synth.make_inputs(wl)
+        bad += _rel(_oracle(wl, inp)["out64"], _dense(wl, inp)) > 1e-9
+    return bad
+
+
+def test_planted_sqrtsoftplus_sign_error_is_caught(monkeypatch):
+    orig = OL.gate_scores
+
+    def wrong(l, gating):
+        if gating == "sqrtsoftplus":
+            s = np.sqrt(np.logaddexp(0.0, -l))
+            return s, s
+        return orig(l, gating)
+    assert _variant_mismatch(monkeypatch, "gate_scores", wrong) > 0
+
+
+def test_planted_biased_weights_are_caught(monkeypatch):
+    """Weights taken from the biased score instead of the unbiased one."""
+    orig_top_k = OL.top_k
+    seen = {}
+
+    def top_k_keep(score, k):
+        seen["score"] = score
+        return orig_top_k(score, k)
+    orig_w = OL.gate_weights
+    monkeypatch.setattr(OL, "top_k", top_k_keep)
+    assert _variant_mismatch(monkeypatch, "gate_weights",
+                             lambda p, i, r, s: orig_w(seen["score"], i, r, s)) > 0
+
+
+def test_planted_ignored_shared_gate_is_caught(monkeypatch):
+    orig = OL.forward
+
+    def no_gate(spec, *a, **kw):
+        if kw.get("shared") is not None:
+            kw["shared"] = dict(kw["shared"], gate=None)
+        return orig(spec, *a, **kw)
+    monkeypatch.setattr(OL, "forward", no_gate)
+    bad = 0
+    for wl in _variant_workloads(12):
+        if not wl.shared_gate or wl.shared_inter == 0:
             continue
         inp = synth.make_inputs(wl)
         bad += _rel(_oracle(wl, inp)["out64"], _dense(wl, inp)) > 1e-9
