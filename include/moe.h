@@ -48,12 +48,20 @@ typedef struct moe_plan_s *moe_plan_t;
 /* Storage formats.  MOE_FP8_E4M3 is OCP e4m3fn (bias 7, max 448, no inf). */
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype_t;
 
-/* Gating (page 3, step 2 "Batched topK dispatch"):
- *  SOFTMAX: p = softmax(l) over all E; experts ranked by p (ties -> lower
- *           index); w_j = p_j / sum_sel p (if renormalize) * routed_scale.
- *  SIGMOID: s = sigmoid(l); experts ranked by s + bias (the bias selects
- *           only); w_j = s_j / sum_sel s (if renormalize) * routed_scale. */
-typedef enum { MOE_GATE_SOFTMAX = 0, MOE_GATE_SIGMOID = 1 } moe_gating_t;
+/* Gating (page 3, step 2 "Batched topK dispatch": softmax, sigmoid with a
+ * correction bias, sqrtsoftplus with a correction bias, softmax with a
+ * correction bias).  Experts are ranked by score + bias (bias = 0 when
+ * router_bias is NULL; the bias selects only), ties -> lower index; the
+ * weights use the unbiased scores:
+ *  SOFTMAX:      score p = softmax(l) over all E;
+ *  SIGMOID:      score s = 1 / (1 + e^-l);
+ *  SQRTSOFTPLUS: score s = sqrt(ln(1 + e^l));
+ *  w_j = score_j / sum_sel score (if renormalize) * routed_scale. */
+typedef enum {
+  MOE_GATE_SOFTMAX = 0,
+  MOE_GATE_SIGMOID = 1,
+  MOE_GATE_SQRTSOFTPLUS = 2
+} moe_gating_t;
 
 /* Expert-path choice.  AUTO: fp32 weights -> SIMPLE; m <= 16 -> SMALL_M;
  * otherwise GROUPED.  The others force a path (for testing; every path
@@ -91,12 +99,17 @@ typedef struct {
 /* Shared expert weights (NULL pointer to this struct iff shared_inter == 0).
  * w13 [2*I_s, H]: rows [0, I_s) = w1 (gate), rows [I_s, 2*I_s) = w3 (up).
  * w2  [H, I_s].  fp8: w13_scale [2*I_s/128, H/128], w2_scale [H/128, I_s/128]
- * fp32 per 128x128 block (value = code * scale); NULL otherwise. */
+ * fp32 per 128x128 block (value = code * scale); NULL otherwise.
+ * gate [H] in the format of x (fp32 or bf16), or NULL: when set, the shared
+ * row of token t is added with weight sigmoid(x[t] . gate) (fp32 dot product
+ * of the unquantised input; page 3, step 8, the shared-expert blend),
+ * otherwise with weight 1. */
 typedef struct {
   const void *w13;
   const void *w2;
   const float *w13_scale;
   const float *w2_scale;
+  const void *gate;
 } moe_shared_t;
 
 /* Stages of one forward, in launch order (page 3, MoeLayer::forward_prefill
@@ -130,6 +143,11 @@ typedef struct {
                              format: fp32 (F32), bf16 (BF16), codes (FP8)   */
   float *h_scale;         /* [te, I/128] scales of h (FP8 weights only)     */
   void *events[MOE_NUM_STAGES + 1];
+  void *h_shared;         /* [m, I_s] shared-expert SwiGLU output, as h     */
+  float *h_shared_scale;  /* [m, I_s/128] its scales (FP8 weights only)     */
+  void *y;                /* [te, H] routed down output, sorted rows: bf16
+                             (fp32 for F32 weights)                          */
+  void *y_shared;         /* [m, H] shared-expert down output, as y         */
 } moe_debug_t;
 
 /* Validate cfg and create a plan (host memory only; no device work).
@@ -161,7 +179,7 @@ size_t moe_workspace_bytes(moe_plan_t plan, int32_t m);
  *   out        [m, H]     fp32 (F32 weights) or bf16; overwritten.
  *   topk_idx   [m, k]     int32 expert ids, descending score, ties -> lower id.
  *   topk_w     [m, k]     fp32 gate weights in the same order.
- *   router_bias[E]        fp32 selection-only bias, or NULL (SIGMOID only).
+ *   router_bias[E]        fp32 selection-only bias, or NULL (any gating).
  *   w13_scale  [E, 2I/128, H/128], w2_scale [E, H/128, I/128]: fp32 block
  *                         scales for FP8 weights, NULL otherwise.
  *   workspace  device buffer of >= moe_workspace_bytes(plan, m) bytes,

@@ -13,11 +13,12 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libmoe.so")
 
 F32, BF16, FP8_E4M3 = 0, 1, 2
-GATE_SOFTMAX, GATE_SIGMOID = 0, 1
+GATE_SOFTMAX, GATE_SIGMOID, GATE_SQRTSOFTPLUS = 0, 1, 2
 PATHS = {"auto": 0, "simple": 1, "grouped": 2, "small_m": 3}
 PATH_NAMES = {v: k for k, v in PATHS.items()}
 DTYPES = {"f32": F32, "bf16": BF16, "fp8": FP8_E4M3}
-GATINGS = {"softmax": GATE_SOFTMAX, "sigmoid": GATE_SIGMOID}
+GATINGS = {"softmax": GATE_SOFTMAX, "sigmoid": GATE_SIGMOID,
+           "sqrtsoftplus": GATE_SQRTSOFTPLUS}
 
 EXPORTS = ("moe_plan", "moe_workspace_bytes", "moe_forward", "moe_forward_debug",
            "moe_path_for", "moe_plan_destroy", "moe_strerror")
@@ -34,7 +35,8 @@ class MoeConfig(ctypes.Structure):
 
 class MoeShared(ctypes.Structure):
     _fields_ = [("w13", ctypes.c_void_p), ("w2", ctypes.c_void_p),
-                ("w13_scale", ctypes.c_void_p), ("w2_scale", ctypes.c_void_p)]
+                ("w13_scale", ctypes.c_void_p), ("w2_scale", ctypes.c_void_p),
+                ("gate", ctypes.c_void_p)]
 
 
 NUM_STAGES = 7
@@ -43,9 +45,13 @@ DEBUG_BUFFERS = ("logits", "counts", "offsets", "sorted_pair", "slot_of_pair",
                  "xq", "sx", "h", "h_scale")
 
 
+DEBUG_BUFFERS_2 = ("h_shared", "h_shared_scale", "y", "y_shared")
+
+
 class MoeDebug(ctypes.Structure):
     _fields_ = ([(n, ctypes.c_void_p) for n in DEBUG_BUFFERS] +
-                [("events", ctypes.c_void_p * (NUM_STAGES + 1))])
+                [("events", ctypes.c_void_p * (NUM_STAGES + 1))] +
+                [(n, ctypes.c_void_p) for n in DEBUG_BUFFERS_2])
 
 
 class MoeError(RuntimeError):
@@ -115,7 +121,7 @@ class MoePlan:
                  renormalize: bool = True, routed_scale: float = 1.0,
                  weight_dtype: str = "bf16", path: str = "auto"):
         self.cfg = MoeConfig(hidden, num_experts, inter, shared_inter, topk,
-                             max_tokens, GATINGS[gating], int(renormalize),
+                             max_tokens, GATINGS.get(gating, gating), int(renormalize),
                              float(routed_scale), DTYPES[weight_dtype], PATHS[path])
         self._h = ctypes.c_void_p()
         st = lib().moe_plan(ctypes.byref(self.cfg), ctypes.byref(self._h))
@@ -146,7 +152,7 @@ class MoePlan:
 
         Tensors are torch device tensors (or raw device addresses).
         ``shared`` is None or a dict with ``w13, w2`` (+ ``w13_scale,
-        w2_scale``); ``debug`` is None or a dict of stage tensors named as
+        w2_scale``, ``gate``); ``debug`` is None or a dict of stage tensors named as
         in ``moe_debug_t``, plus optionally ``events``: a sequence of
         ``NUM_STAGES + 1`` ``torch.cuda.Event`` (or None) recorded around the
         stages.  Returns the status; raises MoeError on failure when
@@ -165,7 +171,8 @@ class MoePlan:
         sh = None
         if shared is not None:
             sh = MoeShared(_ptr(shared["w13"]), _ptr(shared["w2"]),
-                           _ptr(shared.get("w13_scale")), _ptr(shared.get("w2_scale")))
+                           _ptr(shared.get("w13_scale")), _ptr(shared.get("w2_scale")),
+                           _ptr(shared.get("gate")))
         args = [self._h, m, _ptr(x), _ptr(router_w), _ptr(w13), _ptr(w2),
                 ctypes.byref(sh) if sh is not None else None, self.cfg.topk,
                 _ptr(out), _ptr(topk_idx), _ptr(topk_w), _ptr(bias),
@@ -175,6 +182,8 @@ class MoePlan:
             st = lib().moe_forward(*args)
         else:
             dbg = MoeDebug(*[_ptr(debug.get(n)) for n in DEBUG_BUFFERS])
+            for n in DEBUG_BUFFERS_2:
+                setattr(dbg, n, _ptr(debug.get(n)))
             for i, ev in enumerate(debug.get("events") or ()):
                 dbg.events[i] = None if ev is None else _event_handle(ev)
             st = lib().moe_forward_debug(*args, ctypes.byref(dbg))

@@ -1,6 +1,12 @@
 // Unpermute + weighted top-k reduce + shared-expert blend.
 //
-// out[t, n] = sum_{j<k} w[t,j] * y[slot(t*k+j), n]  (+ y_shared[t, n])
+// out[t, n] = sum_{j<k} w[t,j] * y[slot(t*k+j), n]  (+ g_t * y_shared[t, n])
+//
+// g_t = 1 without a shared-expert gate vector, else sigmoid(x[t] . gate)
+// (forward_prefill.rs, page 3, step 8: the shared-expert blend).  Every
+// block of token t computes that dot product itself, in one fixed order
+// (8-element runs per thread, a wave butterfly, then the waves in order), so
+// the factor is the same in every block and on every call.
 //
 // forward_prefill.rs (page 3, step 7 "Unpermute + weighted reduce") gathers
 // each token's sorted expert rows through the token-to-slot map and applies
@@ -13,14 +19,57 @@
 
 namespace moe {
 
+// Eight consecutive elements of an activation-format row as fp32.
+template <bool F32>
+__device__ __forceinline__ void load8(const void *base, size_t i, float (&v)[8]) {
+  if constexpr (F32) {
+    const float4 *src = reinterpret_cast<const float4 *>(static_cast<const float *>(base) + i);
+    const float4 a = src[0], b = src[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  } else {
+    const uint4 q = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(base) + i);
+    const uint32_t u[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[2 * j] = bf16_to_f32(static_cast<uint16_t>(u[j] & 0xffffu));
+      v[2 * j + 1] = bf16_to_f32(static_cast<uint16_t>(u[j] >> 16));
+    }
+  }
+}
+
+// sigmoid(x[t] . gate) by the whole block (H a multiple of 8).
+template <bool F32>
+__device__ __forceinline__ float shared_gate_factor(const void *x, const void *gate, int t, int H) {
+  __shared__ float part[256 / kWave];
+  float acc = 0.f;
+  for (int h = threadIdx.x * 8; h < H; h += 256 * 8) {
+    float a[8], g[8];
+    load8<F32>(x, static_cast<size_t>(t) * H + h, a);
+    load8<F32>(gate, h, g);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc = fmaf(a[i], g[i], acc);
+  }
+  acc = wave_sum(acc);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  float dot = 0.f;
+#pragma unroll
+  for (int w = 0; w < 256 / kWave; ++w) dot += part[w];
+  return 1.0f / (1.0f + expf(-dot));
+}
+
 // One block per token row chunk; 8 columns per thread (16-byte y loads).
 template <bool F32>
 __global__ __launch_bounds__(256) void combine_kernel(
     const void *__restrict__ y, const void *__restrict__ y_sh,
     const int *__restrict__ slot_of_pair, const float *__restrict__ topk_w,
+    const void *__restrict__ x, const void *__restrict__ sgate,
     int m, int H, int k, void *__restrict__ out) {
   const int t = blockIdx.y;
   const int n0 = (blockIdx.x * 256 + threadIdx.x) * 8;
+  // every thread of the block takes part in the gate's reduction
+  const float gsh = (y_sh && sgate) ? shared_gate_factor<F32>(x, sgate, t, H) : 1.0f;
   if (n0 >= H) return;
   float acc[8];
 #pragma unroll
@@ -28,37 +77,20 @@ __global__ __launch_bounds__(256) void combine_kernel(
   for (int j = 0; j < k; ++j) {
     const float wj = topk_w[static_cast<size_t>(t) * k + j];
     const size_t row = static_cast<size_t>(slot_of_pair[static_cast<size_t>(t) * k + j]);
-    if constexpr (F32) {
-      const float4 *src = reinterpret_cast<const float4 *>(static_cast<const float *>(y) + row * H + n0);
-      const float4 a = src[0], b = src[1];
-      const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    float v[8];
+    load8<F32>(y, row * H + n0, v);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] = fmaf(wj, v[i], acc[i]);
-    } else {
-      const uint4 q = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(y) + row * H + n0);
-      const uint32_t u[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        acc[2 * i] = fmaf(wj, bf16_to_f32(static_cast<uint16_t>(u[i] & 0xffffu)), acc[2 * i]);
-        acc[2 * i + 1] = fmaf(wj, bf16_to_f32(static_cast<uint16_t>(u[i] >> 16)), acc[2 * i + 1]);
-      }
-    }
+    for (int i = 0; i < 8; ++i) acc[i] = fmaf(wj, v[i], acc[i]);
   }
   if (y_sh) {
-    if constexpr (F32) {
-      const float4 *src = reinterpret_cast<const float4 *>(static_cast<const float *>(y_sh) + static_cast<size_t>(t) * H + n0);
-      const float4 a = src[0], b = src[1];
-      const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    float v[8];
+    load8<F32>(y_sh, static_cast<size_t>(t) * H + n0, v);
+    if (sgate) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = fmaf(gsh, v[i], acc[i]);
+    } else {
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc[i] += v[i];
-    } else {
-      const uint4 q = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(y_sh) + static_cast<size_t>(t) * H + n0);
-      const uint32_t u[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        acc[2 * i] += bf16_to_f32(static_cast<uint16_t>(u[i] & 0xffffu));
-        acc[2 * i + 1] += bf16_to_f32(static_cast<uint16_t>(u[i] >> 16));
-      }
     }
   }
   if constexpr (F32) {
@@ -75,17 +107,18 @@ __global__ __launch_bounds__(256) void combine_kernel(
   }
 }
 
-hipError_t launch_combine(const Dims &d, const Work &w, const int *topk_idx,
+hipError_t launch_combine(const Dims &d, const Inputs &in, const Work &w, const int *topk_idx,
                           const float *topk_w, void *out, hipStream_t s) {
   (void)topk_idx;
   const dim3 grid((d.H / 8 + 255) / 256, d.m);
   const void *ysh = d.Is > 0 ? w.y_sh : nullptr;
+  const void *sg = d.Is > 0 ? in.sgate : nullptr;
   if (d.wdt == kF32)
     hipLaunchKernelGGL(combine_kernel<true>, grid, dim3(256), 0, s, w.y, ysh,
-                       w.slot_of_pair, topk_w, d.m, d.H, d.k, out);
+                       w.slot_of_pair, topk_w, in.x, sg, d.m, d.H, d.k, out);
   else
     hipLaunchKernelGGL(combine_kernel<false>, grid, dim3(256), 0, s, w.y, ysh,
-                       w.slot_of_pair, topk_w, d.m, d.H, d.k, out);
+                       w.slot_of_pair, topk_w, in.x, sg, d.m, d.H, d.k, out);
   return hipGetLastError();
 }
 

@@ -18,7 +18,7 @@ struct Dims {
   int k;        // top-k
   int te;       // m * k
   int wdt;      // weight storage: kF32 / kBF16 / kFP8
-  int gating;   // 0 softmax, 1 sigmoid
+  int gating;   // 0 softmax, 1 sigmoid, 2 sqrtsoftplus
   int renorm;   // 1: renormalise the selected weights
   float scale;  // routed scaling factor
 };
@@ -36,6 +36,7 @@ struct Inputs {
   const void *sw2;         // shared [H,Is]
   const float *sw13_scale; // [2Is/128,H/128]
   const float *sw2_scale;  // [H/128,Is/128]
+  const void *sgate;       // [H] shared-expert gate vector (format of x) or null
 };
 
 // Device regions carved from the caller's workspace.
@@ -101,7 +102,7 @@ hipError_t launch_small_m_gateup(const Dims &d, const Inputs &in, const Work &w,
 hipError_t launch_small_m_down(const Dims &d, const Inputs &in, const Work &w, hipStream_t s);
 
 // combine.hip
-hipError_t launch_combine(const Dims &d, const Work &w, const int *topk_idx,
+hipError_t launch_combine(const Dims &d, const Inputs &in, const Work &w, const int *topk_idx,
                           const float *topk_w, void *out, hipStream_t s);
 
 }  // namespace moe

@@ -121,7 +121,7 @@ int check_cfg(const moe_config_t &c) {
     return MOE_ERR_INVALID_ARG;
   if (c.num_experts > 1024) return MOE_ERR_INVALID_ARG;
   if (c.topk > c.num_experts || c.topk > 32) return MOE_ERR_INVALID_ARG;
-  if (c.gating != MOE_GATE_SOFTMAX && c.gating != MOE_GATE_SIGMOID) return MOE_ERR_INVALID_ARG;
+  if (c.gating < MOE_GATE_SOFTMAX || c.gating > MOE_GATE_SQRTSOFTPLUS) return MOE_ERR_INVALID_ARG;
   if (c.weight_dtype < MOE_F32 || c.weight_dtype > MOE_FP8_E4M3) return MOE_ERR_INVALID_ARG;
   if (c.path < MOE_PATH_AUTO || c.path > MOE_PATH_SMALL_M) return MOE_ERR_INVALID_ARG;
   if (!(c.routed_scale == c.routed_scale)) return MOE_ERR_INVALID_ARG;  // NaN
@@ -167,14 +167,14 @@ int run_forward(moe_plan_t plan, int32_t m, const void *x, const void *router_w,
   } else if (w13_scale || w2_scale) {
     return MOE_ERR_INVALID_ARG;
   }
-  if (bias && (c.gating != MOE_GATE_SIGMOID || !aligned(bias, 16)))
-    return bias && c.gating != MOE_GATE_SIGMOID ? MOE_ERR_UNSUPPORTED : MOE_ERR_INVALID_ARG;
+  if (bias && !aligned(bias, 16)) return MOE_ERR_INVALID_ARG;
   if ((c.shared_inter > 0) != (shared != nullptr)) return MOE_ERR_INVALID_ARG;
   if (shared) {
     if (!shared->w13 || !shared->w2 || !aligned(shared->w13, 16) || !aligned(shared->w2, 16))
       return MOE_ERR_INVALID_ARG;
     if (fp8 && (!shared->w13_scale || !shared->w2_scale)) return MOE_ERR_INVALID_ARG;
     if (!fp8 && (shared->w13_scale || shared->w2_scale)) return MOE_ERR_INVALID_ARG;
+    if (shared->gate && !aligned(shared->gate, 16)) return MOE_ERR_INVALID_ARG;
   }
   const int path = resolve_path(c, m);
   if (path == MOE_PATH_SMALL_M && m > 16) return MOE_ERR_UNSUPPORTED;
@@ -193,6 +193,7 @@ int run_forward(moe_plan_t plan, int32_t m, const void *x, const void *router_w,
   in.sw2 = shared ? shared->w2 : nullptr;
   in.sw13_scale = shared ? shared->w13_scale : nullptr;
   in.sw2_scale = shared ? shared->w2_scale : nullptr;
+  in.sgate = shared ? shared->gate : nullptr;
   const moe::Work w = carve(L, ws);
   hipStream_t s = static_cast<hipStream_t>(stream);
 
@@ -237,7 +238,7 @@ int run_forward(moe_plan_t plan, int32_t m, const void *x, const void *router_w,
           default: return moe::launch_grouped_down(d, in, w, s);
         }
       }) &&
-      stage(MOE_STAGE_COMBINE, "combine", [&] { return moe::launch_combine(d, w, topk_idx, topk_w, out, s); }) &&
+      stage(MOE_STAGE_COMBINE, "combine", [&] { return moe::launch_combine(d, in, w, topk_idx, topk_w, out, s); }) &&
       stage(MOE_NUM_STAGES, "end event", [&] { return hipSuccess; });
   if (!ok) return hip_fail(e, what);
 
@@ -254,6 +255,10 @@ int run_forward(moe_plan_t plan, int32_t m, const void *x, const void *router_w,
         {dbg->sx, Layout::kSx, L.size[Layout::kSx]},
         {dbg->h, Layout::kH, L.size[Layout::kH]},
         {dbg->h_scale, Layout::kHs, L.size[Layout::kHs]},
+        {dbg->h_shared, Layout::kHsh, L.size[Layout::kHsh]},
+        {dbg->h_shared_scale, Layout::kHshs, L.size[Layout::kHshs]},
+        {dbg->y, Layout::kY, L.size[Layout::kY]},
+        {dbg->y_shared, Layout::kYsh, L.size[Layout::kYsh]},
     };
     for (const Copy &cp : copies) {
       if (!cp.dst || cp.bytes == 0) continue;

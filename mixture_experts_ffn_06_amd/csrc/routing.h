@@ -7,9 +7,11 @@ namespace moe {
 
 // ---------------------------------------------------------------------------
 // Gating + top-k of one token by one wave (router.hip describes the gating).
-// Lane l holds experts l, l+64, ...  Softmax ranks by the logit itself (same
-// order as the softmax probability, without its rounding); sigmoid ranks by
-// sigmoid(l) + bias.  Equal scores: lower expert index first.
+// Lane l holds experts l, l+64, ...  Experts are ranked by score + bias:
+// softmax without a bias ranks by the logit itself (same order as the
+// probability, without its rounding), softmax with a bias by p + bias, p the
+// fp32 probability over all E; sigmoid by 1/(1+e^-l) + bias; sqrtsoftplus by
+// sqrt(softplus(l)) + bias.  Equal scores: lower expert index first.
 //
 // Selection without cross-lane shuffles: scores become order-preserving
 // 32-bit keys, and the k-th largest key T is found bit by bit from the top
@@ -32,6 +34,12 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// sqrt(ln(1 + e^l)), with softplus written as max(l, 0) + ln(1 + e^-|l|) so
+// that e^l never overflows.
+__device__ __forceinline__ float sqrt_softplus(float l) {
+  return sqrtf(fmaxf(l, 0.0f) + log1pf(expf(-fabsf(l))));
+}
+
 template <int EPL>
 __device__ __forceinline__ void topk_token(const float *lrow, int E, int k, int gating,
                                            int renorm, float scale, const float *bias,
@@ -47,11 +55,33 @@ __device__ __forceinline__ void topk_token(const float *lrow, int E, int k, int 
     const int e = lane + kWave * i;
     valid[i] = e < E;
     l[i] = valid[i] ? lrow[e] : 0.f;
+  }
+  // softmax over all E: its maximum and normaliser, needed to rank with a
+  // bias and for unrenormalised weights
+  float lmax = -INFINITY, z = 1.f;
+  if (gating == 0 && (bias || !renorm)) {
+#pragma unroll
+    for (int i = 0; i < EPL; ++i)
+      if (valid[i]) lmax = fmaxf(lmax, l[i]);
+    lmax = wave_max(lmax);
+    z = 0.f;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i)
+      if (valid[i]) z += expf(l[i] - lmax);
+    z = wave_sum(z);
+  }
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int e = lane + kWave * i;
     float c = l[i];
-    if (gating != 0) {
+    if (gating == 0) {
+      if (bias) c = expf(l[i] - lmax) / z;
+    } else if (gating == 1) {
       c = 1.0f / (1.0f + expf(-l[i]));
-      if (bias) c += valid[i] ? bias[e] : 0.f;
+    } else {
+      c = sqrt_softplus(l[i]);
     }
+    if (bias) c += valid[i] ? bias[e] : 0.f;
     key[i] = valid[i] ? order_key(c) : 0u;
   }
   // T = the largest value with at least k keys >= T (the k-th largest key)
@@ -108,25 +138,17 @@ __device__ __forceinline__ void topk_token(const float *lrow, int E, int k, int 
   // Gate weights of the selected experts.
   float wj = 0.f;
   if (gating == 0) {
-    const float l0 = __shfl(my_l, 0);  // largest selected logit
     if (renorm) {
+      // softmax of the selected logits, shifted by their largest
+      const float l0 = wave_max(lane < k ? my_l : -INFINITY);
       const float ex = lane < k ? expf(my_l - l0) : 0.f;
       wj = ex / wave_sum(ex);
     } else {
-      float lmax = -INFINITY;
-#pragma unroll
-      for (int i = 0; i < EPL; ++i)
-        if (valid[i]) lmax = fmaxf(lmax, l[i]);
-      lmax = wave_max(lmax);
-      float z = 0.f;
-#pragma unroll
-      for (int i = 0; i < EPL; ++i)
-        if (valid[i]) z += expf(l[i] - lmax);
-      z = wave_sum(z);
       wj = expf(my_l - lmax) / z;
     }
   } else {
-    const float sj = lane < k ? 1.0f / (1.0f + expf(-my_l)) : 0.f;
+    float sj = 0.f;
+    if (lane < k) sj = gating == 1 ? 1.0f / (1.0f + expf(-my_l)) : sqrt_softplus(my_l);
     wj = renorm ? sj / wave_sum(sj) : sj;
   }
   if (lane < k) {

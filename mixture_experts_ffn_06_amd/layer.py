@@ -14,7 +14,8 @@ class MoeLayer:
 
     ``weights`` keys: ``router_w [E,H]``, ``w13 [E,2I,H]``, ``w2 [E,H,I]``,
     optional ``w13_scale``, ``w2_scale`` (fp8), ``shared_w13``,
-    ``shared_w2`` (+ ``shared_w13_scale``, ``shared_w2_scale``), ``bias``.
+    ``shared_w2`` (+ ``shared_w13_scale``, ``shared_w2_scale``, and
+    ``shared_gate [H]`` for the sigmoid-gated blend), ``bias``.
     """
 
     def __init__(self, weights: dict, *, hidden: int, num_experts: int,
@@ -36,7 +37,8 @@ class MoeLayer:
         if shared_inter > 0:
             self.shared = {"w13": weights["shared_w13"], "w2": weights["shared_w2"],
                            "w13_scale": weights.get("shared_w13_scale"),
-                           "w2_scale": weights.get("shared_w2_scale")}
+                           "w2_scale": weights.get("shared_w2_scale"),
+                           "gate": weights.get("shared_gate")}
 
     def __call__(self, x: torch.Tensor, out=None, topk_idx=None, topk_w=None,
                  stream=None, debug=None):

@@ -38,6 +38,7 @@ def _cfg(**kw):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(topk=0), 1), (dict(topk=9), 1), (dict(num_experts=2000, topk=2), 1),
+    (dict(gating=3), 1),
     (dict(hidden=0), 1), (dict(hidden=100), 2),
     (dict(weight_dtype="fp8", inter=96), 2), (dict(weight_dtype="fp8", hidden=320), 2),
     (dict(weight_dtype="fp8", path="small_m"), 2), (dict(weight_dtype="f32", path="grouped"), 2),
@@ -96,7 +97,7 @@ def test_forward_validation_errors_return_before_any_launch():
     assert _fwd(p, workspace=FAKE + 16) == 1        # workspace not 256-aligned
     assert _fwd(p, ws_bytes=16) == 3                # workspace too small
     assert _fwd(p, w13_scale=FAKE) == 1             # scales on bf16 weights
-    assert _fwd(p, bias=FAKE) == 2                  # bias with softmax gating
+    assert _fwd(p, bias=FAKE + 4) == 1              # misaligned bias
     assert _fwd(p, shared={"w13": FAKE, "w2": FAKE}) == 1   # plan has no shared expert
     assert _fwd(p, m=0) == 0                        # empty batch: nothing to do
     f = moe.MoePlan(**_cfg(weight_dtype="fp8"))
@@ -104,6 +105,7 @@ def test_forward_validation_errors_return_before_any_launch():
     s = moe.MoePlan(**_cfg(shared_inter=128))
     assert _fwd(s) == 1                             # shared expert missing
     assert _fwd(s, shared={"w13": FAKE, "w2": None}) == 1
+    assert _fwd(s, shared={"w13": FAKE, "w2": FAKE, "gate": FAKE + 2}) == 1   # misaligned gate
     r = lib().moe_forward(None, 4, *([None] * 4), None, 2, *([None] * 7), 0, None)
     assert r == 1
 

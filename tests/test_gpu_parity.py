@@ -28,7 +28,8 @@ def make_layer(wl, inp, path="auto", max_tokens=None):
     return MoeLayer(w, hidden=wl.hidden, num_experts=wl.experts, inter=wl.inter,
                     topk=wl.topk, max_tokens=max_tokens or inp["x"].shape[0],
                     shared_inter=wl.shared_inter, gating=wl.gating,
-                    routed_scale=wl.routed_scale, weight_dtype=wl.dtype, path=path)
+                    renormalize=wl.renormalize, routed_scale=wl.routed_scale,
+                    weight_dtype=wl.dtype, path=path)
 
 
 def run_case(wl, path="auto", m=None, tokens=None, lazy=False, inp=None):
@@ -168,6 +169,53 @@ def test_empty_experts_many_tiles():
                         routed_scale=1.0, seed=36)
     rep, *_, (out, idx, w, dbg) = run_case(wl, path="grouped")
     assert int((to_np(dbg["counts"]) == 0).sum()) >= 256 - 40
+
+
+# ------------------------------------------------------ gating variants ---
+# sqrtsoftplus and softmax with a correction bias, no renormalisation, and
+# the sigmoid-gated shared-expert blend (page 3, top-k dispatch and step 8).
+
+SQRTSP_BF16 = synth.Workload("sqrtsp_bf16", m=77, hidden=256, experts=32, topk=6,
+                             inter=128, shared_inter=160, dtype="bf16",
+                             gating="sqrtsoftplus", routed_scale=1.5, seed=40,
+                             zipf_alpha=0.2, zipf_head=0.1, shared_gate=True)
+SOFTMAX_BIAS_BF16 = synth.Workload("softmax_bias_bf16", m=77, hidden=256, experts=32,
+                                   topk=6, inter=128, shared_inter=96, dtype="bf16",
+                                   gating="softmax", routed_scale=1.0, seed=41,
+                                   zipf_alpha=0.005, renormalize=False)
+GATED_FP8 = synth.Workload("gated_fp8", m=300, hidden=512, experts=16, topk=4,
+                           inter=256, shared_inter=384, dtype="fp8",
+                           gating="sqrtsoftplus", routed_scale=2.5, seed=42,
+                           zipf_alpha=0.3, zipf_head=0.2, shared_gate=True)
+GATED_F32 = synth.Workload("gated_f32", m=9, hidden=64, experts=8, topk=2, inter=32,
+                           shared_inter=64, dtype="f32", gating="softmax",
+                           routed_scale=1.0, seed=43, zipf_alpha=0.01,
+                           renormalize=False, shared_gate=True)
+
+
+@pytest.mark.parametrize("path", ["grouped", "small_m", "simple"])
+def test_sqrtsoftplus_bias_gated_shared_bf16(path):
+    run_case(SQRTSP_BF16, path=path, m=16 if path == "small_m" else None)
+
+
+@pytest.mark.parametrize("path", ["grouped", "small_m"])
+def test_softmax_bias_unrenormalised_bf16(path):
+    run_case(SOFTMAX_BIAS_BF16, path=path, m=13 if path == "small_m" else None)
+
+
+@pytest.mark.parametrize("path", ["grouped", "simple"])
+def test_sqrtsoftplus_gated_shared_fp8(path):
+    run_case(GATED_FP8, path=path)
+
+
+def test_gated_shared_unrenormalised_f32():
+    run_case(GATED_F32)
+
+
+def test_decode_sqrtsoftplus_bias_full_size():
+    wl = synth.WORKLOADS["decode_bf16"].replace(name="decode_sqrtsp", gating="sqrtsoftplus",
+                                                routed_scale=2.5, zipf_alpha=0.05)
+    run_case(wl, path="small_m")
 
 
 # ------------------------------------------------------------ behaviour ---
