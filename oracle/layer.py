@@ -212,25 +212,31 @@ def round_down_output(y: np.ndarray, dtype: str) -> np.ndarray:
 
 
 def expert_mlp(a_rows: np.ndarray, w13: np.ndarray, w2: np.ndarray,
-               inter: int, dtype: str, block: int):
+               inter: int, dtype: str, block: int, h_given=None):
     """SwiGLU expert on rows ``a_rows [n, H]`` with exact fp64 weights.
 
     ``w13 [2I, H]`` holds w1 (gate) in rows [0, I) and w3 (up) in [I, 2I);
     ``w2 [H, I]``.  Returns ``(y [n, H] as stored, h values [n, I], h codes,
-    h scales)``.
+    h scales, h before rounding)``.
+
+    ``h_given [n, I]``: rounded intermediate values decided elsewhere (the
+    fp8 codes times scales of another implementation); the down product and
+    the storage of y then start from them.
     """
     g = a_rows @ w13[:inter].T
     u = a_rows @ w13[inter:].T
     h = silu(g) * u
     hv, hc, hs = round_intermediate(h, dtype, block)
-    return round_down_output(hv @ w2.T, dtype), hv, hc, hs
+    if h_given is not None:
+        hv = np.asarray(h_given, dtype=np.float64)
+    return round_down_output(hv @ w2.T, dtype), hv, hc, hs, h
 
 
 # ------------------------------------------------------------------ all ---
 
 def forward(spec: LayerSpec, x, router_w, w13, w2, w13_scale=None,
             w2_scale=None, shared=None, bias=None, tokens=None,
-            idx_override=None, keep_h=False) -> dict:
+            idx_override=None, keep_h=False, h_override=None) -> dict:
     """Oracle forward of the layer.
 
     ``x [m,H]``: bf16 bit patterns (uint16) or fp32.  ``router_w [E,H]``
@@ -244,7 +250,14 @@ def forward(spec: LayerSpec, x, router_w, w13, w2, w13_scale=None,
     ``out`` are evaluated (gating and permutation are always computed for
     all m tokens).  ``idx_override [m,k]``: evaluate with these expert
     indices instead of the oracle's own top-k (weights from the oracle's fp64
-    probabilities at those indices).
+    probabilities at those indices).  ``keep_h``: also return, per pair p
+    (routed) and per token (shared), the intermediate before rounding
+    (``h_pre``, ``h_sh_pre``), its rounded values (``h``, ``h_sh``) and, for
+    fp8, its scales (``h_scale``, ``h_sh_scale``).  ``h_override``: a pair
+    ``(routed [te, I] by pair, shared [m, I_s] by token)`` of rounded
+    intermediate values to continue from instead of the oracle's own
+    rounding (a quantised code decided by another implementation, checked
+    first by the caller); either part may be None.
 
     Returns a dict with ``logits, prob, score, idx, gap, w, counts, offsets,
     sorted_pair, slot_of_pair, out64 [n,H], out [n,H]`` (rounded to the
@@ -278,7 +291,8 @@ def forward(spec: LayerSpec, x, router_w, w13, w2, w13_scale=None,
     tok = np.arange(m) if tokens is None else np.asarray(sorted(tokens))
     pos_of_tok = {int(t): i for i, t in enumerate(tok)}
     acc = np.zeros((len(tok), H))
-    h_rows = {}
+    h_rows, h_pre, h_sc = {}, {}, {}
+    h_or, hs_or = (None, None) if h_override is None else h_override
     # routed experts: walk the sorted pairs expert by expert (grouped GEMM).
     for e in range(E):
         seg = sorted_pair[offsets[e]:offsets[e + 1]]
@@ -290,10 +304,14 @@ def forward(spec: LayerSpec, x, router_w, w13, w2, w13_scale=None,
                              spec.dtype, B)
         w2e = weight_values(w2[e], None if w2_scale is None else w2_scale[e],
                             spec.dtype, B)
-        y, hv, _, _ = expert_mlp(xt[rows], w13e, w2e, I, spec.dtype, B)
+        y, hv, _, hs, hp = expert_mlp(xt[rows], w13e, w2e, I, spec.dtype, B,
+                                      None if h_or is None else h_or[seg])
         if keep_h:
             for i, p in enumerate(seg):
                 h_rows[p] = hv[i]
+                h_pre[p] = hp[i]
+                if hs is not None:
+                    h_sc[p] = hs[i]
         # unpermute + weighted reduce: each pair adds into its token's row
         for i, p in enumerate(seg):
             t, j = divmod(p, k)
@@ -301,8 +319,11 @@ def forward(spec: LayerSpec, x, router_w, w13, w2, w13_scale=None,
     if shared is not None and spec.shared_inter > 0:
         s13 = weight_values(shared["w13"], shared.get("w13_scale"), spec.dtype, B)
         s2 = weight_values(shared["w2"], shared.get("w2_scale"), spec.dtype, B)
-        ysh, _, _, _ = expert_mlp(xt[tok], s13, s2, spec.shared_inter,
-                                  spec.dtype, B)
+        ysh, hv, _, hs, hp = expert_mlp(xt[tok], s13, s2, spec.shared_inter,
+                                        spec.dtype, B,
+                                        None if hs_or is None else hs_or[tok])
+        if keep_h:
+            res.update(h_sh=hv, h_sh_pre=hp, h_sh_scale=hs)
         if shared.get("gate") is not None:
             gl = xv[tok] @ act_values(shared["gate"], act)
             res["shared_gate"] = 1.0 / (1.0 + np.exp(-gl))
@@ -314,5 +335,5 @@ def forward(spec: LayerSpec, x, router_w, w13, w2, w13_scale=None,
     if spec.dtype == "f32":
         res["out"] = acc.astype(np.float32).astype(np.float64)
     if keep_h:
-        res["h"] = h_rows
+        res.update(h=h_rows, h_pre=h_pre, h_scale=h_sc)
     return res

@@ -317,6 +317,29 @@ def test_shared_only_contribution_and_unit_weight():
     assert np.max(np.abs(r["out64"] - ref.numpy())) < 1e-6 * np.abs(ref.numpy()).max()
 
 
+def test_h_override_with_own_rounding_is_the_identity():
+    """Continuing from the oracle's own rounded intermediates reproduces its
+    output exactly; a changed intermediate changes it."""
+    wl = synth.Workload("hov", m=9, hidden=256, experts=5, topk=2, inter=256,
+                        shared_inter=128, dtype="fp8", gating="sigmoid",
+                        routed_scale=2.5, seed=13)
+    inp = synth.make_inputs(wl)
+    spec, args = oracle_inputs(wl, inp)
+    r = OL.forward(spec, **args, keep_h=True)
+    te = wl.m * wl.topk
+    h = np.stack([r["h"][p] for p in range(te)])
+    again = OL.forward(spec, **args, h_override=(h, r["h_sh"]))
+    assert np.array_equal(again["out64"], r["out64"])
+    h2 = h.copy()
+    h2[3, 7] *= 2.0
+    moved = OL.forward(spec, **args, h_override=(h2, None))
+    assert not np.array_equal(moved["out64"], r["out64"])
+    # the pre-rounding values round to the kept ones
+    assert np.all(np.abs(np.stack([r["h_pre"][p] for p in range(te)]) - h) <=
+                  np.abs(h) * 2.0 ** -3 + 2.0 ** -9 * np.repeat(
+                      np.stack([r["h_scale"][p] for p in range(te)]), 128, axis=1))
+
+
 # ---------------------------------------------------------- symmetries ---
 
 def test_token_permutation_equivariance():
@@ -406,8 +429,8 @@ def test_planted_unnormalised_weights_are_caught(monkeypatch):
 def test_planted_swapped_gate_up_is_caught(monkeypatch):
     orig = OL.expert_mlp
 
-    def swapped(a, w13, w2, inter, dt, blk):
-        return orig(a, np.concatenate([w13[inter:], w13[:inter]]), w2, inter, dt, blk)
+    def swapped(a, w13, w2, inter, dt, blk, h_given=None):
+        return orig(a, np.concatenate([w13[inter:], w13[:inter]]), w2, inter, dt, blk, h_given)
     assert _dense_mismatch(monkeypatch, "expert_mlp", swapped) > 0
 
 
