@@ -14,6 +14,12 @@ Definitions written from the formats themselves:
 * Block rule for the fp8 layer (weights per 128x128 block, activations per
   row per 128 columns): ``s = fp32(amax / 448)``; ``code = e4m3(fp32(v / s))``;
   ``s = 1`` and all codes 0 when amax is 0.  Scales are plain fp32.
+* MXFP4 (OCP Microscaling formats, FP4 E2M1 elements with an E8M0 scale
+  shared by 32 consecutive elements): an element is 1 sign, 2 exponent
+  (bias 1) and 1 mantissa bit; exponent field 0 is subnormal (``0.5 * M``);
+  the magnitudes are 0, 0.5, 1, 1.5, 2, 3, 4, 6.  An E8M0 scale byte ``e`` is
+  the power of two ``2**(e - 127)`` (255 is NaN).  Element j of a row is
+  stored in byte j // 2, the even element in the low nibble.
 """
 from __future__ import annotations
 
@@ -138,3 +144,32 @@ def dequant_blocks(codes: np.ndarray, scales: np.ndarray, block: int = 128) -> n
     table = e4m3_decode(np.arange(256, dtype=np.uint8))   # value of every code
     vals = table[codes].reshape(sr, br, sc, bc)
     return (vals * np.asarray(scales, np.float64)[:, None, :, None]).reshape(R, C)
+
+
+# ---------------------------------------------------------------- MXFP4 --
+
+def e2m1_decode(codes: np.ndarray) -> np.ndarray:
+    """4-bit e2m1 codes (values 0..15) -> exact float64 values."""
+    c = np.asarray(codes, dtype=np.int64) & 0xF
+    e = (c >> 1) & 0x3
+    mt = (c & 1).astype(np.float64)
+    val = np.where(e == 0, 0.5 * mt, np.ldexp(1.0 + mt / 2.0, e - 1))
+    return np.where(c & 0x8, -val, val)
+
+
+def e8m0_decode(e: np.ndarray) -> np.ndarray:
+    """E8M0 scale bytes -> float64 powers of two (NaN for 255)."""
+    e = np.asarray(e, dtype=np.int64)
+    return np.where(e == 255, np.nan, np.ldexp(1.0, e - 127))
+
+
+def mxfp4_decode(packed: np.ndarray, scales: np.ndarray, block: int = 32) -> np.ndarray:
+    """Packed MXFP4 matrix -> exact float64 values.
+
+    ``packed [rows, cols/2]`` uint8 (element 2i in the low nibble of byte i,
+    element 2i+1 in the high nibble); ``scales [rows, cols/block]`` E8M0
+    bytes, one per ``block`` consecutive elements of a row.
+    """
+    p = np.asarray(packed, dtype=np.uint8)
+    codes = np.stack([p & 0xF, p >> 4], axis=-1).reshape(p.shape[0], -1)
+    return e2m1_decode(codes) * np.repeat(e8m0_decode(scales), block, axis=1)

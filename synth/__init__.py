@@ -32,7 +32,13 @@ Draw recipe (all seeds are fixed integers):
 
 fp8 weights are stored blockwise: for each 128x128 block, scale =
 amax / 448 (fp32) and codes = torch's float8_e4m3fn cast of the clamped
-quotient.  The layer receives codes and scales as given.
+quotient.  MXFP4 weights (OCP Microscaling, FP4 E2M1 elements with an E8M0
+scale per 32 consecutive elements of a row, along K): shared exponent
+``X = floor(log2(amax)) - 2`` (2 = the element format's largest exponent),
+scale byte ``X + 127``, elements rounded to the nearest of 0, 0.5, 1, 1.5,
+2, 3, 4, 6 (ties to the even code) after division by ``2**X``, saturating
+at 6; two elements per byte, the even one in the low nibble.  The layer
+receives codes and scales as given.
 """
 from __future__ import annotations
 
@@ -56,7 +62,7 @@ class Workload:
     topk: int              # k
     inter: int             # I (per routed expert)
     shared_inter: int      # I_s, 0 = no shared expert
-    dtype: str             # "f32" | "bf16" | "fp8"
+    dtype: str             # "f32" | "bf16" | "fp8" | "mxfp4" (weights)
     gating: str            # "softmax" | "sigmoid" | "sqrtsoftplus"
     routed_scale: float    # multiplier after renormalisation
     seed: int
@@ -96,6 +102,10 @@ WORKLOADS: dict[str, Workload] = {
     "decode_bf16": Workload("decode_bf16", m=16, hidden=2048, experts=128,
                             topk=8, inter=768, shared_inter=0, dtype="bf16",
                             gating="softmax", routed_scale=1.0, seed=2),
+    # The decode layer with MXFP4 expert weights (same x and router draws).
+    "decode_mxfp4": Workload("decode_mxfp4", m=16, hidden=2048, experts=128,
+                             topk=8, inter=768, shared_inter=0, dtype="mxfp4",
+                             gating="softmax", routed_scale=1.0, seed=2),
     # Prefill bf16 layer with one unweighted shared expert (I_s = 2048).
     "prefill_bf16": Workload("prefill_bf16", m=1024, hidden=2048,
                              experts=128, topk=8, inter=768,
@@ -184,6 +194,24 @@ def _block_fp8(w: torch.Tensor, block: int) -> tuple[torch.Tensor, torch.Tensor]
     return codes.contiguous(), scale.contiguous()
 
 
+def _mx_fp4(w: torch.Tensor) -> tuple[torch.Tensor, torch.Tensor]:
+    """Store a 2-D fp32 matrix as packed MXFP4 codes and E8M0 scale bytes
+    (one per 32 consecutive elements of a row)."""
+    r, c = w.shape
+    wb = w.reshape(r, c // 32, 32)
+    amax = wb.abs().amax(dim=-1)
+    X = torch.floor(torch.log2(amax.clamp_min(2.0 ** -126))) - 2
+    X = torch.where(amax > 0, X, torch.full_like(X, -127.0)).clamp(-127.0, 127.0)
+    q = wb / torch.exp2(X)[..., None]
+    mag = q.abs()
+    # index of the nearest e2m1 magnitude, ties to the even code
+    idx = ((mag > 0.25).int() + (mag >= 0.75).int() + (mag > 1.25).int() +
+           (mag >= 1.75).int() + (mag > 2.5).int() + (mag >= 3.5).int() + (mag > 5.0).int())
+    code = (idx | ((q < 0).int() << 3)).reshape(r, c)
+    packed = (code[:, 0::2] | (code[:, 1::2] << 4)).to(torch.uint8)
+    return packed.contiguous(), (X + 127).to(torch.uint8).contiguous()
+
+
 def _draw_matrix(seed: int, rows: int, cols: int, device) -> torch.Tensor:
     g = torch.Generator(device=device)
     g.manual_seed(seed)
@@ -196,6 +224,8 @@ def _store_weight(w: torch.Tensor, dtype: str, block: int):
         return w, None
     if dtype == "bf16":
         return w.to(torch.bfloat16), None
+    if dtype == "mxfp4":
+        return _mx_fp4(w)
     return _block_fp8(w, block)
 
 
@@ -217,10 +247,15 @@ def make_inputs(wl: Workload, device="cpu", m: int | None = None) -> dict:
     b = draw_bias(wl)
     out["bias"] = None if b is None else torch.from_numpy(b).to(device)
     E, H, I = wl.experts, wl.hidden, wl.inter
-    wdt = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}[wl.dtype]
-    w13 = torch.empty((E, 2 * I, H), dtype=wdt, device=device)
-    w2 = torch.empty((E, H, I), dtype=wdt, device=device)
+    wdt = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8,
+           "mxfp4": torch.uint8}[wl.dtype]
+    pk = 2 if wl.dtype == "mxfp4" else 1     # elements per stored byte along K
+    w13 = torch.empty((E, 2 * I, H // pk), dtype=wdt, device=device)
+    w2 = torch.empty((E, H, I // pk), dtype=wdt, device=device)
     s13 = s2 = None
+    if wl.dtype == "mxfp4":
+        s13 = torch.empty((E, 2 * I, H // 32), dtype=torch.uint8, device=device)
+        s2 = torch.empty((E, H, I // 32), dtype=torch.uint8, device=device)
     if wl.dtype == "fp8":
         B = wl.block
         s13 = torch.empty((E, 2 * I // B, H // B), dtype=torch.float32, device=device)

@@ -150,3 +150,66 @@ def test_weight_block_dequant_layout(shape, np_rng):
             blk = dq[bi * 128:(bi + 1) * 128, bj * 128:(bj + 1) * 128]
             ref = e4m3_decode(codes[bi * 128:(bi + 1) * 128, bj * 128:(bj + 1) * 128]) * float(s[bi, bj])
             assert np.array_equal(blk, ref)
+
+
+# ---------------------------------------------------------------- MXFP4 --
+# OCP Microscaling Formats (MX) v1.0: FP4 E2M1 element magnitudes, in code
+# order 0..7, as the format's definition tabulates them.
+E2M1_MAGNITUDES = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+
+
+def test_e2m1_codes_match_the_format_table():
+    from oracle.codec import e2m1_decode
+    v = e2m1_decode(np.arange(16))
+    assert list(v[:8]) == E2M1_MAGNITUDES
+    assert list(-v[8:]) == E2M1_MAGNITUDES          # bit 3 is the sign
+    assert np.signbit(v[8])                         # code 8 is -0
+
+
+def test_e8m0_is_a_power_of_two_with_bias_127():
+    from oracle.codec import e8m0_decode
+    e = np.arange(255)
+    assert np.array_equal(e8m0_decode(e), np.ldexp(1.0, e - 127))
+    assert e8m0_decode(np.array([127]))[0] == 1.0 and np.isnan(e8m0_decode(np.array([255]))[0])
+
+
+def test_mxfp4_decode_packing_and_block_scales():
+    """Element 2i in the low nibble of byte i; one scale per 32 elements."""
+    from oracle.codec import mxfp4_decode
+    codes = np.arange(64).reshape(1, 64) % 16
+    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    scales = np.array([[127 + 3, 127 - 2]], np.uint8)
+    v = mxfp4_decode(packed, scales)
+    mags = np.array(E2M1_MAGNITUDES + [-m for m in E2M1_MAGNITUDES])
+    want = mags[codes[0]] * np.where(np.arange(64) < 32, 8.0, 0.25)
+    assert np.array_equal(v[0], want)
+
+
+def test_synth_mxfp4_storage_is_nearest_with_saturation():
+    """The stored codes are the nearest e2m1 value of v / 2**X (brute-force
+    search over the 8 magnitudes; exact ties excluded), with X =
+    floor(log2(amax)) - 2 per 32 elements."""
+    import torch
+    import synth
+    from oracle.codec import mxfp4_decode
+    g = torch.Generator().manual_seed(3)
+    w = torch.randn((8, 256), generator=g) * 0.02
+    w[0, :32] = 0.0                                 # an all-zero block
+    packed, sc = synth._mx_fp4(w)
+    v = mxfp4_decode(packed.numpy(), sc.numpy())
+    wn = w.double().numpy()
+    for r in range(8):
+        for b in range(8):
+            blk = wn[r, 32 * b:32 * b + 32]
+            amax = np.abs(blk).max()
+            if amax == 0:
+                assert np.all(v[r, 32 * b:32 * b + 32] == 0)
+                continue
+            X = np.floor(np.log2(amax)) - 2
+            assert sc.numpy()[r, b] == X + 127
+            q = np.abs(blk) / 2.0 ** X
+            d = np.abs(q[:, None] - np.array(E2M1_MAGNITUDES)[None, :])
+            near = np.array(E2M1_MAGNITUDES)[np.argmin(d, axis=1)]
+            got = np.abs(v[r, 32 * b:32 * b + 32]) / 2.0 ** X
+            assert np.array_equal(got, near)
+            assert np.all(np.sign(v[r, 32 * b:32 * b + 32]) * np.sign(blk) >= 0)

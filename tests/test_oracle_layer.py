@@ -25,7 +25,8 @@ import torch
 
 import oracle.layer as OL
 import synth
-from oracle.codec import bf16_decode, dequant_blocks, e4m3_decode, e4m3_quantize_rows
+from oracle.codec import (bf16_decode, dequant_blocks, e2m1_decode, e4m3_decode,
+                          e4m3_quantize_rows)
 from oracle.dense import dense_forward
 from tests.conftest import oracle_inputs, to_np
 
@@ -42,6 +43,14 @@ def _values(wl, inp):
             return a.astype(np.float64)
         if wl.dtype == "bf16":
             return bf16_decode(a)
+        if wl.dtype == "mxfp4":
+            # unpacked here with shifts on the stacked array and a lookup
+            # table of the element values, independently of mxfp4_decode
+            table = e2m1_decode(np.arange(16))
+            lo, hi = table[a & 15], table[a >> 4]
+            vals = np.empty(a.shape[:-1] + (2 * a.shape[-1],))
+            vals[..., 0::2], vals[..., 1::2] = lo, hi
+            return vals * np.exp2(np.repeat(to_np(s).astype(np.float64) - 127.0, 32, axis=-1))
         s = to_np(s)
         if a.ndim == 3:
             return np.stack([dequant_blocks(a[e], s[e], wl.block) for e in range(a.shape[0])])
@@ -145,6 +154,45 @@ def test_random_tiny_layers_sparse_equals_dense(wl):
     # ties in fp8 / bf16 rounding of h are computed identically on both
     # sides, so the two formulations agree to fp64 accumulation error
     assert _rel(r["out64"], d) < 1e-12
+
+
+def _mxfp4_workloads(n=10):
+    """MXFP4 expert weights (bf16 x, h and y): random tiny layers."""
+    rng = np.random.default_rng(79)
+    out = []
+    for i in range(n):
+        E = int(rng.integers(1, 13))
+        gating = ["softmax", "sigmoid", "sqrtsoftplus"][i % 3]
+        out.append(synth.Workload(
+            f"mx{i}", m=int(rng.integers(1, 9)), hidden=int(rng.choice([32, 64, 256])),
+            experts=E, topk=int(rng.integers(1, E + 1)), inter=int(rng.choice([32, 96, 256])),
+            shared_inter=int(rng.choice([0, 64, 256])), dtype="mxfp4", gating=gating,
+            routed_scale=2.5 if gating != "softmax" else 1.0, seed=3000 + i,
+            zipf_alpha=0.3 if i % 2 else 0.0, zipf_head=0.2, shared_gate=i % 4 == 0))
+    return out
+
+
+@pytest.mark.parametrize("wl", _mxfp4_workloads(), ids=lambda w: w.name)
+def test_mxfp4_layers_sparse_equals_dense(wl):
+    inp = synth.make_inputs(wl)
+    r = _oracle(wl, inp)
+    assert _rel(r["out64"], _dense(wl, inp)) < 1e-12
+
+
+def test_mxfp4_one_expert_is_swiglu_mlp_on_decoded_weights():
+    """k = 1 of a single MXFP4 expert: torch's silu on the decoded weights,
+    h rounded to bf16 and y stored in bf16 as the layer defines."""
+    wl = synth.Workload("mx_one", m=5, hidden=64, experts=1, topk=1, inter=32,
+                        shared_inter=0, dtype="mxfp4", gating="softmax",
+                        routed_scale=1.0, seed=14)
+    inp = synth.make_inputs(wl)
+    r = _oracle(wl, inp)
+    v = _values(wl, inp)
+    x = torch.from_numpy(v["x"])
+    w13, w2 = torch.from_numpy(v["W13"][0]), torch.from_numpy(v["W2"][0])
+    h = (torch.nn.functional.silu(x @ w13[:32].T) * (x @ w13[32:].T)).to(torch.bfloat16).double()
+    ref = (h @ w2.T).to(torch.bfloat16).double()
+    assert np.max(np.abs(r["out64"] - ref.numpy())) <= 1e-12 * np.abs(ref.numpy()).max()
 
 
 @pytest.mark.parametrize("wl", _variant_workloads(), ids=lambda w: w.name)
