@@ -31,7 +31,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
-MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
+# MXFP4 weights are converted to bf16 in registers and multiplied on the
+# bf16 MFMA
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3, "mxfp4": 2500.0}
+COMPUTE_DTYPE = {"mxfp4": "bf16"}
 METRIC = "MoE layer tokens/s; prefill TFLOP/s vs MFMA peak; decode GB/s vs HBM peak"
 
 
@@ -58,7 +61,7 @@ def parse():
 
 
 def esz(dtype):
-    return {"f32": 4, "bf16": 2, "fp8": 1}[dtype]
+    return {"f32": 4, "bf16": 2, "fp8": 1, "mxfp4": 0.5}[dtype]
 
 
 # Source files of each expert-kernel family: HBM byte counters recorded in
@@ -100,10 +103,15 @@ def layer_counts(wl, m, D):
     te = m * k
     we = esz(wl.dtype)
     ae = 4 if wl.dtype == "f32" else 2              # x / out / y element bytes
-    sc = (lambda r, c: (r // 128) * (c // 128) * 4) if wl.dtype == "fp8" else (lambda r, c: 0)
+    if wl.dtype == "fp8":
+        sc = lambda r, c: (r // 128) * (c // 128) * 4     # fp32 per 128x128 block
+    elif wl.dtype == "mxfp4":
+        sc = lambda r, c: r * (c // 32)                    # E8M0 byte per 32 along K
+    else:
+        sc = lambda r, c: 0
     w13 = D * (2 * I * H * we + sc(2 * I, H)) + (2 * Is * H * we + sc(2 * Is, H) if Is else 0)
     w2 = D * (H * I * we + sc(H, I)) + (H * Is * we + sc(H, Is) if Is else 0)
-    hb = we if wl.dtype != "f32" else 4
+    hb = {"f32": 4, "bf16": 2, "fp8": 1, "mxfp4": 2}[wl.dtype]   # h element bytes
     h_bytes = (te * I + m * Is) * hb + ((te * I + m * Is) // 128 * 4 if wl.dtype == "fp8" else 0)
     x_in = m * H * (1 + 4 / 128 if wl.dtype == "fp8" else ae)
     y_bytes = (te + (m if Is else 0)) * H * ae
@@ -261,7 +269,7 @@ def main():
         "metric": METRIC, "value": m / (ms_per_step * 1e-3), "unit": "tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic",
+        "vs_baseline": None, "dtype": COMPUTE_DTYPE.get(wl.dtype, wl.dtype), "data": "synthetic",
         "config": {"workload": f"{wl.name}: m={m} H={wl.hidden} E={wl.experts} "
                                f"k={wl.topk} I={wl.inter} I_s={wl.shared_inter} "
                                f"{wl.dtype} {wl.gating}",

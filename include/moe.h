@@ -45,8 +45,14 @@ extern "C" {
 
 typedef struct moe_plan_s *moe_plan_t;
 
-/* Storage formats.  MOE_FP8_E4M3 is OCP e4m3fn (bias 7, max 448, no inf). */
-typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype_t;
+/* Storage formats.  MOE_FP8_E4M3 is OCP e4m3fn (bias 7, max 448, no inf).
+ * MOE_MXFP4 (expert weights only) is OCP Microscaling FP4: e2m1 elements
+ * (magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6), two per byte along K (even element
+ * in the low nibble), with one E8M0 scale byte 2^(e - 127) per 32 consecutive
+ * elements of a row; scale bytes 0 and 255 are not supported.  The MX
+ * elements are the "block-scaled" weight format of page 1 (its NVFP4 W4A4
+ * MoE) on gfx950's own FP4 conversion; x, h and out stay bf16. */
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2, MOE_MXFP4 = 3 } moe_dtype_t;
 
 /* Gating (page 3, step 2 "Batched topK dispatch": softmax, sigmoid with a
  * correction bias, sqrtsoftplus with a correction bias, softmax with a
@@ -70,7 +76,7 @@ typedef enum {
   MOE_PATH_AUTO = 0,
   MOE_PATH_SIMPLE = 1,   /* fp32 VALU kernels, any dtype */
   MOE_PATH_GROUPED = 2,  /* MFMA grouped GEMM, bf16 / fp8 */
-  MOE_PATH_SMALL_M = 3   /* weight-streaming path, bf16, m <= 16 */
+  MOE_PATH_SMALL_M = 3   /* weight-streaming path, bf16 / MXFP4, m <= 16 */
 } moe_path_t;
 
 typedef enum {
@@ -92,14 +98,16 @@ typedef struct {
   int32_t renormalize;   /* 1: divide the k selected weights by their sum */
   float routed_scale;    /* multiplier applied after renormalisation */
   int32_t weight_dtype;  /* moe_dtype_t.  F32 => x/out are fp32;
-                            BF16 or FP8_E4M3 => x/out are bf16 */
+                            BF16, FP8_E4M3 or MXFP4 => x/out are bf16 */
   int32_t path;          /* moe_path_t */
 } moe_config_t;
 
 /* Shared expert weights (NULL pointer to this struct iff shared_inter == 0).
  * w13 [2*I_s, H]: rows [0, I_s) = w1 (gate), rows [I_s, 2*I_s) = w3 (up).
  * w2  [H, I_s].  fp8: w13_scale [2*I_s/128, H/128], w2_scale [H/128, I_s/128]
- * fp32 per 128x128 block (value = code * scale); NULL otherwise.
+ * fp32 per 128x128 block (value = code * scale); MXFP4: w13 [2*I_s, H/2] and
+ * w2 [H, I_s/2] bytes, w13_scale [2*I_s, H/32] and w2_scale [H, I_s/32] E8M0
+ * bytes; NULL otherwise.
  * gate [H] in the format of x (fp32 or bf16), or NULL: when set, the shared
  * row of token t is added with weight sigmoid(x[t] . gate) (fp32 dot product
  * of the unquantised input; page 3, step 8, the shared-expert blend),
@@ -107,8 +115,8 @@ typedef struct {
 typedef struct {
   const void *w13;
   const void *w2;
-  const float *w13_scale;
-  const float *w2_scale;
+  const void *w13_scale;
+  const void *w2_scale;
   const void *gate;
 } moe_shared_t;
 
@@ -154,7 +162,10 @@ typedef struct {
  * Errors: MOE_ERR_INVALID_ARG for non-positive sizes, topk outside
  * [1, min(E,32)], E > 1024, unknown enums; MOE_ERR_UNSUPPORTED for fp8 with
  * H, I or I_s not multiples of 128, bf16/fp8 with H, I or I_s not multiples
- * of 32, SMALL_M forced with fp8/fp32 weights, or sizes whose operands
+ * of 32, MXFP4 with H, I or I_s not multiples of 256, with max_tokens above
+ * 16 or with a path other than AUTO / SMALL_M (MXFP4 runs on the m <= 16
+ * weight-streaming path only), SMALL_M forced with fp8/fp32 weights, or
+ * sizes whose operands
  * reach 2 GiB (max_tokens * topk * max(H, I, I_s) elements, or one expert's
  * 2 * max(I, I_s) * H weight elements, at 2 bytes per bf16/fp8 element and 4
  * per fp32: the expert kernels use 32-bit byte offsets). */
@@ -181,7 +192,10 @@ size_t moe_workspace_bytes(moe_plan_t plan, int32_t m);
  *   topk_w     [m, k]     fp32 gate weights in the same order.
  *   router_bias[E]        fp32 selection-only bias, or NULL (any gating).
  *   w13_scale  [E, 2I/128, H/128], w2_scale [E, H/128, I/128]: fp32 block
- *                         scales for FP8 weights, NULL otherwise.
+ *                         scales for FP8 weights; [E, 2I, H/32] and
+ *                         [E, H, I/32] E8M0 bytes for MXFP4 weights (then
+ *                         experts_w13 is [E, 2I, H/2] and experts_w2
+ *                         [E, H, I/2] bytes); NULL otherwise.
  *   workspace  device buffer of >= moe_workspace_bytes(plan, m) bytes,
  *              256-byte aligned; its contents need not be initialised.
  * Every pointer must be 16-byte aligned.  FP8: activations are quantised
@@ -192,7 +206,7 @@ int moe_forward(moe_plan_t plan, int32_t m, const void *x, const void *router_w,
                 const void *experts_w13, const void *experts_w2,
                 const moe_shared_t *shared_w, int32_t topk, void *out,
                 int32_t *topk_idx, float *topk_w, const float *router_bias,
-                const float *w13_scale, const float *w2_scale,
+                const void *w13_scale, const void *w2_scale,
                 void *workspace, size_t workspace_bytes, void *stream);
 
 /* moe_forward with stage timing events, then copies of the intermediate
@@ -203,8 +217,8 @@ int moe_forward_debug(moe_plan_t plan, int32_t m, const void *x,
                       const void *router_w, const void *experts_w13,
                       const void *experts_w2, const moe_shared_t *shared_w,
                       int32_t topk, void *out, int32_t *topk_idx, float *topk_w,
-                      const float *router_bias, const float *w13_scale,
-                      const float *w2_scale, void *workspace,
+                      const float *router_bias, const void *w13_scale,
+                      const void *w2_scale, void *workspace,
                       size_t workspace_bytes, void *stream,
                       const moe_debug_t *dbg);
 

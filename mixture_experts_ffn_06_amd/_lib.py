@@ -12,11 +12,11 @@ import os
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libmoe.so")
 
-F32, BF16, FP8_E4M3 = 0, 1, 2
+F32, BF16, FP8_E4M3, MXFP4 = 0, 1, 2, 3
 GATE_SOFTMAX, GATE_SIGMOID, GATE_SQRTSOFTPLUS = 0, 1, 2
 PATHS = {"auto": 0, "simple": 1, "grouped": 2, "small_m": 3}
 PATH_NAMES = {v: k for k, v in PATHS.items()}
-DTYPES = {"f32": F32, "bf16": BF16, "fp8": FP8_E4M3}
+DTYPES = {"f32": F32, "bf16": BF16, "fp8": FP8_E4M3, "mxfp4": MXFP4}
 GATINGS = {"softmax": GATE_SOFTMAX, "sigmoid": GATE_SIGMOID,
            "sqrtsoftplus": GATE_SQRTSOFTPLUS}
 
@@ -122,7 +122,8 @@ class MoePlan:
                  weight_dtype: str = "bf16", path: str = "auto"):
         self.cfg = MoeConfig(hidden, num_experts, inter, shared_inter, topk,
                              max_tokens, GATINGS.get(gating, gating), int(renormalize),
-                             float(routed_scale), DTYPES[weight_dtype], PATHS[path])
+                             float(routed_scale), DTYPES.get(weight_dtype, weight_dtype),
+                             PATHS[path])
         self._h = ctypes.c_void_p()
         st = lib().moe_plan(ctypes.byref(self.cfg), ctypes.byref(self._h))
         if st != 0:

@@ -40,7 +40,7 @@ bool aligned(const void *p, size_t a) {
 int resolve_path(const moe_config_t &c, int m) {
   if (c.path != MOE_PATH_AUTO) return c.path;
   if (c.weight_dtype == MOE_F32) return MOE_PATH_SIMPLE;
-  if (c.weight_dtype == MOE_BF16 && m <= 16) return MOE_PATH_SMALL_M;
+  if ((c.weight_dtype == MOE_BF16 || c.weight_dtype == MOE_MXFP4) && m <= 16) return MOE_PATH_SMALL_M;
   return MOE_PATH_GROUPED;
 }
 
@@ -122,7 +122,7 @@ int check_cfg(const moe_config_t &c) {
   if (c.num_experts > 1024) return MOE_ERR_INVALID_ARG;
   if (c.topk > c.num_experts || c.topk > 32) return MOE_ERR_INVALID_ARG;
   if (c.gating < MOE_GATE_SOFTMAX || c.gating > MOE_GATE_SQRTSOFTPLUS) return MOE_ERR_INVALID_ARG;
-  if (c.weight_dtype < MOE_F32 || c.weight_dtype > MOE_FP8_E4M3) return MOE_ERR_INVALID_ARG;
+  if (c.weight_dtype < MOE_F32 || c.weight_dtype > MOE_MXFP4) return MOE_ERR_INVALID_ARG;
   if (c.path < MOE_PATH_AUTO || c.path > MOE_PATH_SMALL_M) return MOE_ERR_INVALID_ARG;
   if (!(c.routed_scale == c.routed_scale)) return MOE_ERR_INVALID_ARG;  // NaN
   if (c.hidden % 8) return MOE_ERR_UNSUPPORTED;
@@ -134,7 +134,14 @@ int check_cfg(const moe_config_t &c) {
     return MOE_ERR_UNSUPPORTED;
   if (c.weight_dtype == MOE_F32 && c.path != MOE_PATH_AUTO && c.path != MOE_PATH_SIMPLE)
     return MOE_ERR_UNSUPPORTED;
-  if (c.path == MOE_PATH_SMALL_M && c.weight_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (c.path == MOE_PATH_SMALL_M && c.weight_dtype != MOE_BF16 && c.weight_dtype != MOE_MXFP4)
+    return MOE_ERR_UNSUPPORTED;
+  // MXFP4 runs on the weight-streaming path only: one stage is 256 K
+  // elements, batches of at most 16 tokens
+  if (c.weight_dtype == MOE_MXFP4 &&
+      (c.hidden % 256 || c.inter % 256 || c.shared_inter % 256 || c.max_tokens > 16 ||
+       (c.path != MOE_PATH_AUTO && c.path != MOE_PATH_SMALL_M)))
+    return MOE_ERR_UNSUPPORTED;
   // the expert kernels address each operand (token rows, the sorted h / y
   // rows, one expert's weight matrix) with 32-bit byte offsets
   const int64_t esz = c.weight_dtype == MOE_F32 ? 4 : 2;
@@ -149,19 +156,20 @@ int check_cfg(const moe_config_t &c) {
 int run_forward(moe_plan_t plan, int32_t m, const void *x, const void *router_w,
                 const void *w13, const void *w2, const moe_shared_t *shared,
                 int32_t topk, void *out, int32_t *topk_idx, float *topk_w,
-                const float *bias, const float *w13_scale,
-                const float *w2_scale, void *ws, size_t ws_bytes,
+                const float *bias, const void *w13_scale,
+                const void *w2_scale, void *ws, size_t ws_bytes,
                 void *stream, const moe_debug_t *dbg) {
   if (!plan) return MOE_ERR_INVALID_ARG;
   const moe_config_t &c = plan->cfg;
   if (m < 0 || m > c.max_tokens || topk != c.topk) return MOE_ERR_INVALID_ARG;
   if (m == 0) return MOE_OK;
   const bool fp8 = c.weight_dtype == MOE_FP8_E4M3;
+  const bool scaled = fp8 || c.weight_dtype == MOE_MXFP4;   // block scales given
   const void *need[] = {x, router_w, w13, w2, out, topk_idx, topk_w, ws};
   for (const void *q : need)
     if (!q || !aligned(q, 16)) return MOE_ERR_INVALID_ARG;
   if (!aligned(ws, 256)) return MOE_ERR_INVALID_ARG;
-  if (fp8) {
+  if (scaled) {
     if (!w13_scale || !w2_scale || !aligned(w13_scale, 16) || !aligned(w2_scale, 16))
       return MOE_ERR_INVALID_ARG;
   } else if (w13_scale || w2_scale) {
@@ -172,8 +180,10 @@ int run_forward(moe_plan_t plan, int32_t m, const void *x, const void *router_w,
   if (shared) {
     if (!shared->w13 || !shared->w2 || !aligned(shared->w13, 16) || !aligned(shared->w2, 16))
       return MOE_ERR_INVALID_ARG;
-    if (fp8 && (!shared->w13_scale || !shared->w2_scale)) return MOE_ERR_INVALID_ARG;
-    if (!fp8 && (shared->w13_scale || shared->w2_scale)) return MOE_ERR_INVALID_ARG;
+    if (scaled && (!shared->w13_scale || !shared->w2_scale || !aligned(shared->w13_scale, 16) ||
+                   !aligned(shared->w2_scale, 16)))
+      return MOE_ERR_INVALID_ARG;
+    if (!scaled && (shared->w13_scale || shared->w2_scale)) return MOE_ERR_INVALID_ARG;
     if (shared->gate && !aligned(shared->gate, 16)) return MOE_ERR_INVALID_ARG;
   }
   const int path = resolve_path(c, m);
@@ -184,15 +194,19 @@ int run_forward(moe_plan_t plan, int32_t m, const void *x, const void *router_w,
   moe::Dims d;
   d.m = m; d.H = c.hidden; d.E = c.num_experts; d.I = c.inter;
   d.Is = c.shared_inter; d.k = c.topk; d.te = m * c.topk;
-  d.wdt = c.weight_dtype == MOE_F32 ? moe::kF32 : (fp8 ? moe::kFP8 : moe::kBF16);
+  d.wdt = c.weight_dtype == MOE_F32 ? moe::kF32
+        : fp8 ? moe::kFP8
+        : c.weight_dtype == MOE_MXFP4 ? moe::kMXFP4 : moe::kBF16;
   d.gating = c.gating; d.renorm = c.renormalize ? 1 : 0; d.scale = c.routed_scale;
   moe::Inputs in;
   in.x = x; in.router_w = router_w; in.w13 = w13; in.w2 = w2;
-  in.w13_scale = w13_scale; in.w2_scale = w2_scale; in.bias = bias;
+  in.w13_scale = static_cast<const float *>(w13_scale);   // E8M0 bytes for MXFP4
+  in.w2_scale = static_cast<const float *>(w2_scale);
+  in.bias = bias;
   in.sw13 = shared ? shared->w13 : nullptr;
   in.sw2 = shared ? shared->w2 : nullptr;
-  in.sw13_scale = shared ? shared->w13_scale : nullptr;
-  in.sw2_scale = shared ? shared->w2_scale : nullptr;
+  in.sw13_scale = shared ? static_cast<const float *>(shared->w13_scale) : nullptr;
+  in.sw2_scale = shared ? static_cast<const float *>(shared->w2_scale) : nullptr;
   in.sgate = shared ? shared->gate : nullptr;
   const moe::Work w = carve(L, ws);
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -297,7 +311,7 @@ int moe_forward(moe_plan_t plan, int32_t m, const void *x, const void *router_w,
                 const void *experts_w13, const void *experts_w2,
                 const moe_shared_t *shared_w, int32_t topk, void *out,
                 int32_t *topk_idx, float *topk_w, const float *router_bias,
-                const float *w13_scale, const float *w2_scale, void *workspace,
+                const void *w13_scale, const void *w2_scale, void *workspace,
                 size_t workspace_bytes, void *stream) {
   return run_forward(plan, m, x, router_w, experts_w13, experts_w2, shared_w,
                      topk, out, topk_idx, topk_w, router_bias, w13_scale,
@@ -308,8 +322,8 @@ int moe_forward_debug(moe_plan_t plan, int32_t m, const void *x,
                       const void *router_w, const void *experts_w13,
                       const void *experts_w2, const moe_shared_t *shared_w,
                       int32_t topk, void *out, int32_t *topk_idx, float *topk_w,
-                      const float *router_bias, const float *w13_scale,
-                      const float *w2_scale, void *workspace,
+                      const float *router_bias, const void *w13_scale,
+                      const void *w2_scale, void *workspace,
                       size_t workspace_bytes, void *stream,
                       const moe_debug_t *dbg) {
   return run_forward(plan, m, x, router_w, experts_w13, experts_w2, shared_w,

@@ -240,6 +240,235 @@ __global__ __launch_bounds__(kSmBlockWaves * kWave) void sm_kernel(Dims d, Input
   }
 }
 
+// ---------------------------------------------------------------------------
+// MXFP4 weights (OCP MX: FP4 E2M1 elements, one E8M0 scale per 32 elements
+// of a row along K; tokens and h stay bf16).  Same items, K split and
+// two-slot ring as sm_kernel with NBLK = 2; a stage is 128 bytes = 256 K
+// elements of each of the item's 32 weight rows (four 1 KB direct loads of 8
+// whole rows each, pieces swizzled per row) plus the rows' 8 scale bytes (one
+// 4-byte direct load per lane).  Lane group g = lane / 16 takes the K
+// elements [64 g, 64 g + 64) of a stage -- 32 contiguous bytes of its row,
+// eight elements per MFMA step -- and reads the token row to match (any split
+// of K over the lanes gives the same product when A and B share it).  The
+// weights become bf16 in registers by the scaled fp4 -> bf16 conversion, which
+// multiplies by 2 to the power of the scale operand's exponent: with the scale
+// 2^(e - 127) built from the E8M0 byte that is exact.  The MFMA is the bf16
+// 16x16x32 of the bf16 path.
+constexpr int kFp4Run = 128;                            // fp4 bytes per row per stage
+constexpr int kFp4StageK = 2 * kFp4Run;                 // K elements per stage
+constexpr int kFp4Rows = 32;                            // weight rows per item
+constexpr int kFp4WBytes = kFp4Rows * kFp4Run;          // weight bytes per stage
+constexpr int kFp4SBytes = kFp4Rows * kFp4StageK / 32;  // scale bytes per stage
+constexpr int kFp4Stage = kFp4WBytes + kFp4SBytes;
+constexpr int kFp4WaveLds = 2 * kFp4Stage;
+constexpr int kFp4Lds = kSmBlockWaves * kFp4WaveLds;
+static_assert(kFp4WaveLds >= 2 * kWave * 16, "partial sums fit the ring");
+
+// The lane's stage operands: pieces p0, p1 of its row in blocks 0 and 1 and
+// the two blocks' 8 scale bytes of the row, read and waited for together.
+__device__ __forceinline__ void fp4_stage_reads(uint32_t p0, uint32_t p1, uint32_t ps, u32x4_t &b0,
+                                                u32x4_t &b1, u32x4_t &b2, u32x4_t &b3, u32x2_t &s0,
+                                                u32x2_t &s1) {
+  asm volatile(
+      "ds_read_b128 %0, %6\n"
+      "ds_read_b128 %1, %7\n"
+      "ds_read_b128 %2, %6 offset:%9\n"
+      "ds_read_b128 %3, %7 offset:%9\n"
+      "ds_read_b64 %4, %8\n"
+      "ds_read_b64 %5, %8 offset:%10\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(b0), "=&v"(b1), "=&v"(b2), "=&v"(b3), "=&v"(s0), "=&v"(s1)
+      : "v"(p0), "v"(p1), "v"(ps), "i"(16 * kFp4Run), "i"(16 * 8));
+}
+
+// Eight e2m1 codes (one 32-bit word, the even element in the low nibble of
+// each byte) times 2^(e - 127), as bf16.
+__device__ __forceinline__ bf16x8_t fp4x8_to_bf16(uint32_t word, uint32_t e) {
+  const float sc = __uint_as_float(e << 23);
+  const bf16x2_t q0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, sc, 0);
+  const bf16x2_t q1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, sc, 1);
+  const bf16x2_t q2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, sc, 2);
+  const bf16x2_t q3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, sc, 3);
+  return bf16x8_t{q0[0], q0[1], q1[0], q1[1], q2[0], q2[1], q3[0], q3[1]};
+}
+
+template <int MODE>
+__global__ __launch_bounds__(kSmBlockWaves * kWave) void sm_fp4_kernel(Dims d, Inputs in, Work w, int ks) {
+  constexpr int CW = MODE == kSmGateUp ? 16 : 32;   // output columns per item
+  extern __shared__ __align__(1024) uint8_t lds[];
+  const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6);
+  uint8_t *ring = lds + wave * kFp4WaveLds;
+  const int item = uniform(blockIdx.x * (kSmBlockWaves / ks) + wave / ks);
+  const int kp = uniform(wave % ks);
+
+  // ---- the item: slot and column group ----
+  const int na = uniform(*w.nactive);
+  const int ncol_r = MODE == kSmGateUp ? d.I : d.H;
+  const int ipr = (ncol_r + CW - 1) / CW;
+  const int ips = d.Is > 0 ? ((MODE == kSmGateUp ? d.Is : d.H) + CW - 1) / CW : 0;
+  const bool live = item < na * ipr + ips;
+
+  f32x4_t acc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+  int seg0 = 0, rows = 0, inter = 0, c0 = 0, ncol = 0;
+  bool shared = false;
+  if (live) {
+    int e, cg;
+    if (item < na * ipr) {
+      const int slot = item / ipr;
+      cg = item - slot * ipr;
+      e = uniform(w.active[slot]);
+      seg0 = uniform(w.offsets[e]);
+      rows = uniform(w.offsets[e + 1]) - seg0;   // <= m <= 16
+      inter = d.I;
+    } else {
+      shared = true;
+      e = d.E;
+      cg = item - na * ipr;
+      rows = d.m;
+      inter = d.Is;
+    }
+    c0 = cg * CW;
+    ncol = MODE == kSmGateUp ? inter : d.H;
+    const int K = MODE == kSmGateUp ? d.H : inter;
+    const int abytes = K * 2, wbytes = K / 2, sbytes = K / 32;   // per token / weight row
+
+    const int r = lane & 15, g = lane >> 4;
+    const int ar = min(r, rows - 1);   // rows past the slot's end repeat its last row
+    const uint8_t *Ab, *Wb, *Sb;
+    uint32_t aoff;
+    const uint8_t *s13 = reinterpret_cast<const uint8_t *>(shared ? in.sw13_scale : in.w13_scale);
+    const uint8_t *s2 = reinterpret_cast<const uint8_t *>(shared ? in.sw2_scale : in.w2_scale);
+    if (MODE == kSmGateUp) {
+      const int tok = shared ? ar : w.sorted_pair[seg0 + ar] / d.k;
+      Ab = static_cast<const uint8_t *>(in.x);
+      aoff = static_cast<uint32_t>(tok) * abytes;
+      const size_t eo = shared ? 0 : static_cast<size_t>(e) * 2 * d.I;   // first weight row
+      Wb = static_cast<const uint8_t *>(shared ? in.sw13 : in.w13) + eo * (d.H / 2);
+      Sb = s13 + eo * (d.H / 32);
+    } else {
+      Ab = static_cast<const uint8_t *>(shared ? w.h_sh : w.h);
+      aoff = static_cast<uint32_t>(seg0 + ar) * abytes;
+      const size_t eo = shared ? 0 : static_cast<size_t>(e) * d.H;
+      Wb = static_cast<const uint8_t *>(shared ? in.sw2 : in.w2) + eo * (d.I / 2);
+      Sb = s2 + eo * (d.I / 32);
+    }
+    aoff += g * 128;   // the lane's 64 K elements of each stage, in bf16
+    // First weight row of block j (blocks past the last column read row 0
+    // and store nothing).
+    auto wrow = [&](int j) -> int {
+      if (MODE == kSmGateUp) {
+        const int c = c0;
+        return c < ncol ? (j == 0 ? c : inter + c) : 0;
+      }
+      const int c = c0 + 16 * j;
+      return c < ncol ? c : 0;
+    };
+    // Direct load q covers item rows 8 q .. 8 q + 7 (block q / 2); the lane
+    // fetches logical piece sm_swz(lane % 8, row) of its row.
+    uint32_t qoff[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int row = (q % 2) * 8 + lane / 8;
+      qoff[q] = static_cast<uint32_t>(wrow(q / 2) + row) * wbytes + sm_swz<kFp4Run>(lane % 8, row) * 16;
+    }
+    // scales: lane l fetches 4 of the 8 scale bytes of item row l / 2
+    const int srow = lane >> 1;
+    const uint32_t soff = static_cast<uint32_t>(wrow(srow / 16) + srow % 16) * sbytes + (lane & 1) * 4;
+
+    const int nst_all = K / kFp4StageK;
+    const int st0 = uniform(nst_all * kp / ks), st1 = uniform(nst_all * (kp + 1) / ks);
+    uint4 aA[8], aB[8];
+    auto issue = [&](int st, int sl, uint4 (&A)[8]) {
+      uint8_t *slot = ring + sl * kFp4Stage;
+      const uint32_t kw = static_cast<uint32_t>(st) * kFp4Run;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) dma16_to_lds(Wb + (qoff[q] + kw), slot + q * 1024);
+      dma4_to_lds(Sb + (soff + static_cast<uint32_t>(st) * 8), slot + kFp4WBytes);
+      const uint32_t ka = static_cast<uint32_t>(st) * kFp4StageK * 2;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) A[i] = *reinterpret_cast<const uint4 *>(Ab + (aoff + ka) + i * 16);
+    };
+    // lane reads logical pieces 2 g, 2 g + 1 of row r in both blocks and the
+    // row's scale bytes 2 g, 2 g + 1 (the 32-element blocks of its K range)
+    const uint32_t pp0 = static_cast<uint32_t>(r * kFp4Run + sm_swz<kFp4Run>(2 * g, r) * 16);
+    const uint32_t pp1 = static_cast<uint32_t>(r * kFp4Run + sm_swz<kFp4Run>(2 * g + 1, r) * 16);
+    const int sh = (2 * g % 4) * 8;    // bit offset of scale byte 2 g in its word
+    auto compute = [&](int sl, const uint4 (&A)[8]) {
+      const uint8_t *slot = ring + sl * kFp4Stage;
+      const uint32_t base = lds_off(slot);
+      u32x4_t b0, b1, b2, b3;
+      u32x2_t q0, q1;
+      fp4_stage_reads(base + pp0, base + pp1, base + kFp4WBytes + r * 8, b0, b1, b2, b3, q0, q1);
+      const uint32_t sw0 = g < 2 ? q0.x : q0.y, sw1 = g < 2 ? q1.x : q1.y;
+      const uint32_t e0[2] = {(sw0 >> sh) & 0xffu, (sw0 >> (sh + 8)) & 0xffu};
+      const uint32_t e1[2] = {(sw1 >> sh) & 0xffu, (sw1 >> (sh + 8)) & 0xffu};
+      const uint32_t w0[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+      const uint32_t w1[8] = {b2.x, b2.y, b2.z, b2.w, b3.x, b3.y, b3.z, b3.w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const bf16x8_t a = __builtin_bit_cast(bf16x8_t, A[i]);
+        acc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, fp4x8_to_bf16(w0[i], e0[i / 4]), acc[0], 0, 0, 0);
+        acc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, fp4x8_to_bf16(w1[i], e1[i / 4]), acc[1], 0, 0, 0);
+      }
+    };
+    constexpr int LPS = 4 + 1 + 8;   // vector-memory ops per stage
+    const int n = st1 - st0;
+    if (n > 0) {
+      issue(st0, 0, aA);
+      int st = st0;
+      for (int p = 0; p < n / 2; ++p, st += 2) {
+        issue(st + 1, 1, aB);
+        wait_vm<LPS>();
+        compute(0, aA);
+        issue(min(st + 2, st1 - 1), 0, aA);
+        wait_vm<LPS>();
+        compute(1, aB);
+      }
+      wait_vm<0>();
+      if (n & 1) compute(0, aA);
+    }
+  }
+
+  // ---- partial sums of the KS waves of an item meet in LDS ----
+  if (ks > 1) {
+    f32x4_t *part = reinterpret_cast<f32x4_t *>(ring);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) part[j * kWave + lane] = acc[j];
+    __syncthreads();
+    if (kp != 0) return;
+    for (int q = 1; q < ks; ++q) {
+      const f32x4_t *other = reinterpret_cast<const f32x4_t *>(lds + (wave + q) * kFp4WaveLds);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[j] += other[j * kWave + lane];
+    }
+  }
+  if (!live) return;
+
+  // ---- epilogue: lane holds rows 4*(lane/16) + i, column lane % 16 ----
+  const int cl = lane & 15;
+  if (MODE == kSmGateUp) {
+    uint16_t *h = static_cast<uint16_t *>(shared ? w.h_sh : w.h) + static_cast<size_t>(seg0) * inter;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = (lane >> 4) * 4 + i;
+      if (row < rows && c0 < ncol)
+        h[static_cast<size_t>(row) * inter + c0 + cl] = f32_to_bf16(silu(acc[0][i]) * acc[1][i]);
+    }
+  } else {
+    uint16_t *y = static_cast<uint16_t *>(shared ? w.y_sh : w.y) + static_cast<size_t>(seg0) * d.H;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = (lane >> 4) * 4 + i;
+      if (row < rows) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          if (c0 + 16 * j < ncol)
+            y[static_cast<size_t>(row) * d.H + c0 + 16 * j + cl] = f32_to_bf16(acc[j][i]);
+      }
+    }
+  }
+}
+
 static int sm_cus() {
   static int cus = 0;
   if (cus == 0) {
@@ -292,7 +521,41 @@ static hipError_t sm_launch(const Dims &d, const Inputs &in, const Work &w, hipS
   return hipGetLastError();
 }
 
-// H, I multiples of 32 and m <= 16 are checked by the caller.  A stage moves
+// MXFP4 launch: the item count, K split and grid of sm_launch.
+template <int MODE>
+static hipError_t sm_fp4_launch(const Dims &d, const Inputs &in, const Work &w, hipStream_t s) {
+  constexpr int CW = MODE == kSmGateUp ? 16 : 32;
+  auto kern = sm_fp4_kernel<MODE>;
+  static int blocks_per_cu = 0;
+  if (blocks_per_cu == 0) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kFp4Lds);
+    if (e != hipSuccess) return e;
+    int nb = 0;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kern, kSmBlockWaves * kWave, kFp4Lds);
+    if (e != hipSuccess) return e;
+    if (nb < 1) return hipErrorInvalidConfiguration;
+    blocks_per_cu = nb;
+  }
+  const int slots = d.te < d.E ? d.te : d.E;
+  const int ncol_r = MODE == kSmGateUp ? d.I : d.H;
+  const int ipr = (ncol_r + CW - 1) / CW;
+  const int ips = d.Is > 0 ? ((MODE == kSmGateUp ? d.Is : d.H) + CW - 1) / CW : 0;
+  const long items = static_cast<long>(slots) * ipr + ips;
+  const long cap = static_cast<long>(sm_cus()) * blocks_per_cu * kSmBlockWaves;
+  const int kmin = MODE == kSmGateUp ? d.H : (d.Is > 0 && d.Is < d.I ? d.Is : d.I);
+  const int nst = kmin / kFp4StageK;
+  int ks = 1;
+  while (ks < kSmBlockWaves && items * ks * 2 <= 3 * cap && nst / (ks * 2) >= 3) ks *= 2;
+  const long per_block = kSmBlockWaves / ks;
+  const long grid = (items + per_block - 1) / per_block;
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(kSmBlockWaves * kWave), kFp4Lds, s,
+                     d, in, w, ks);
+  return hipGetLastError();
+}
+
+// H, I multiples of 32 and m <= 16 are checked by the caller (MXFP4: H, I and
+// I_s multiples of 256, one stage).  A stage moves
 // RUN contiguous bytes of each row: 256 when K is a multiple of 128 (longer
 // runs stream faster), else 128 or 64.
 template <int MODE, int NBLK>
@@ -304,11 +567,13 @@ static hipError_t sm_dispatch(const Dims &d, const Inputs &in, const Work &w, hi
 
 hipError_t launch_small_m_gateup(const Dims &d, const Inputs &in, const Work &w,
                                  hipStream_t s) {
+  if (d.wdt == kMXFP4) return sm_fp4_launch<kSmGateUp>(d, in, w, s);
   return sm_dispatch<kSmGateUp, 2>(d, in, w, s, d.H);   // 16 h columns per item
 }
 
 hipError_t launch_small_m_down(const Dims &d, const Inputs &in, const Work &w,
                                hipStream_t s) {
+  if (d.wdt == kMXFP4) return sm_fp4_launch<kSmDown>(d, in, w, s);
   // K is I for routed slots and I_s for the shared one: stages fit both
   const int kg = d.Is > 0 ? (d.I % 128 == 0 && d.Is % 128 == 0 ? 128 : (d.I % 64 == 0 && d.Is % 64 == 0 ? 64 : 32))
                           : d.I;

@@ -45,6 +45,10 @@ def _cfg(**kw):
     (dict(weight_dtype="bf16", inter=48), 2),
     # operands of 2 GiB or more (32-bit byte offsets in the expert kernels)
     (dict(hidden=8192, max_tokens=65536, topk=2), 2),
+    # MXFP4: weight-streaming path only (m <= 16), K in stages of 256
+    (dict(weight_dtype="mxfp4", max_tokens=17), 2), (dict(weight_dtype="mxfp4", inter=128, max_tokens=16), 2),
+    (dict(weight_dtype="mxfp4", path="grouped", max_tokens=16), 2),
+    (dict(weight_dtype="mxfp4", path="simple", max_tokens=16), 2), (dict(weight_dtype=4), 1),
     (dict(hidden=32768, inter=32768, max_tokens=16), 2),
 ])
 def test_plan_rejects_bad_configs(kw, status):
@@ -61,6 +65,7 @@ def test_plan_accepts_and_reports_paths_and_workspace():
     assert p.workspace_bytes(64) > p.workspace_bytes(8) > 0
     assert moe.MoePlan(**_cfg(weight_dtype="f32", hidden=64, inter=32)).path_for(4) == "simple"
     assert moe.MoePlan(**_cfg(weight_dtype="fp8")).path_for(4) == "grouped"
+    assert moe.MoePlan(**_cfg(weight_dtype="mxfp4", inter=256, max_tokens=16)).path_for(16) == "small_m"
     assert lib().moe_workspace_bytes(None, 4) == 0
 
 
@@ -102,6 +107,9 @@ def test_forward_validation_errors_return_before_any_launch():
     assert _fwd(p, m=0) == 0                        # empty batch: nothing to do
     f = moe.MoePlan(**_cfg(weight_dtype="fp8"))
     assert _fwd(f) == 1                             # fp8 needs scales
+    mx = moe.MoePlan(**_cfg(weight_dtype="mxfp4", inter=256, max_tokens=16))
+    assert _fwd(mx) == 1                            # MXFP4 needs its E8M0 scales
+    assert _fwd(mx, w13_scale=FAKE, w2_scale=FAKE + 4) == 1   # misaligned scales
     s = moe.MoePlan(**_cfg(shared_inter=128))
     assert _fwd(s) == 1                             # shared expert missing
     assert _fwd(s, shared={"w13": FAKE, "w2": None}) == 1

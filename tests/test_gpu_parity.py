@@ -218,6 +218,32 @@ def test_decode_sqrtsoftplus_bias_full_size():
     run_case(wl, path="small_m")
 
 
+# ---------------------------------------------------------- MXFP4 experts ---
+# OCP MX FP4 weights with E8M0 scales on the weight-streaming path.
+
+MX_SMALL = synth.Workload("mx_small", m=16, hidden=512, experts=16, topk=4, inter=256,
+                          shared_inter=256, dtype="mxfp4", gating="sqrtsoftplus",
+                          routed_scale=2.5, seed=44, zipf_alpha=0.3, zipf_head=0.2,
+                          shared_gate=True)
+
+
+@pytest.mark.parametrize("m", [1, 4, 16])
+def test_decode_mxfp4(m):
+    run_case(synth.WORKLOADS["decode_mxfp4"], path="small_m", m=m)
+
+
+@pytest.mark.parametrize("m", [1, 7, 13, 16])
+def test_mxfp4_shared_gated_small(m):
+    run_case(MX_SMALL, path="small_m", m=m)
+
+
+def test_mxfp4_k_equals_E():
+    wl = synth.Workload("mx_keqE", m=9, hidden=256, experts=4, topk=4, inter=512,
+                        shared_inter=0, dtype="mxfp4", gating="softmax",
+                        routed_scale=1.0, seed=45, renormalize=False)
+    run_case(wl, path="small_m")
+
+
 # ------------------------------------------------------------ behaviour ---
 
 def test_m_zero_is_a_noop():
