@@ -198,10 +198,38 @@ __global__ __launch_bounds__(kFusedThreads) void topk_permute_kernel(Dims d, Inp
   float *lg = reinterpret_cast<float *>(smem);                // [m][E]
   int *idx_s = reinterpret_cast<int *>(lg + m * E);           // [m * k]
   int *wcnt = idx_s + ((m * d.k + 3) & ~3);                   // [16][E]
-  // ---- logits: partial tiles summed in split order ----
-  for (int i = threadIdx.x; i < m * E; i += kFusedThreads) {
+  int *lrank = wcnt + kPermWaves * E;                         // [m * k]
+  // ---- logits: partial tiles summed in split order.  The first
+  // kSumPre * kFusedThreads logits have all of their partials loaded before
+  // any is summed or stored (one round trip to memory, not one per logit
+  // group); larger m * E continue in a plain loop. ----
+  const int mE = m * E;
+  constexpr int kSumPre = 4;
+  {
+    float part[kSumPre][kRouterMaxSplits];
+#pragma unroll
+    for (int u = 0; u < kSumPre; ++u) {
+      const int i = threadIdx.x + u * kFusedThreads;
+#pragma unroll
+      for (int q = 0; q < kRouterMaxSplits; ++q)
+        part[u][q] = (i < mE && q < ks) ? w.rpart[static_cast<size_t>(q) * mE + i] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < kSumPre; ++u) {
+      const int i = threadIdx.x + u * kFusedThreads;
+      float v = part[u][0];
+#pragma unroll
+      for (int q = 1; q < kRouterMaxSplits; ++q)
+        if (q < ks) v += part[u][q];
+      if (i < mE) {
+        lg[i] = v;
+        w.logits[i] = v;
+      }
+    }
+  }
+  for (int i = threadIdx.x + kSumPre * kFusedThreads; i < mE; i += kFusedThreads) {
     float v = w.rpart[i];
-    for (int q = 1; q < ks; ++q) v += w.rpart[static_cast<size_t>(q) * m * E + i];
+    for (int q = 1; q < ks; ++q) v += w.rpart[static_cast<size_t>(q) * mE + i];
     lg[i] = v;
     w.logits[i] = v;
   }
@@ -214,13 +242,13 @@ __global__ __launch_bounds__(kFusedThreads) void topk_permute_kernel(Dims d, Inp
   __syncthreads();
   // ---- stable sort by expert ----
   permute_block(idx_s, d.te, E, wcnt, scan_tmp, w.counts, w.offsets, w.sorted_pair, w.slot_of_pair,
-                w.lrank, w.active, w.nactive);
+                lrank, w.active, w.nactive);
 }
 
 hipError_t launch_topk_permute(const Dims &d, const Inputs &in, const Work &w, int *topk_idx,
                                float *topk_w, hipStream_t s) {
   const size_t lds = static_cast<size_t>(d.m) * d.E * 4 + static_cast<size_t>((d.m * d.k + 3) & ~3) * 4 +
-                     static_cast<size_t>(kPermWaves) * d.E * 4;
+                     static_cast<size_t>(kPermWaves) * d.E * 4 + static_cast<size_t>(d.m) * d.k * 4;
   const int epl = (d.E + kWave - 1) / kWave;
   const int ks = router_splits(d);
 #define MOE_FUSED_CASE(N)                                                                      \
