@@ -482,11 +482,18 @@ static int sm_cus() {
 
 // Grid for the largest possible item count (the number of slots is only
 // known on the device: items past it exit at once).  KS, the waves per item
-// (each streams 1/KS of K, partial sums meet in LDS), is the largest of 1, 2,
-// 4 that keeps the wave tasks within three rounds of what fits at once and
-// leaves every wave at least three stages: smaller tasks shorten the tail
-// of a launch that would otherwise leave CUs idle (m = 4 gate/up: 46 -> 37
-// us), while tasks of one or two stages cost more than they balance.
+// (each streams 1/KS of K, partial sums meet in LDS), is at least 2 whenever
+// every wave keeps three stages, then the largest of 2, 4 that keeps the wave
+// tasks within three rounds of what fits at once and leaves every wave at
+// least three stages: smaller tasks shorten the tail of a launch that would
+// otherwise leave CUs idle (m = 4 gate/up: 46 -> 37 us; m = 16 gate/up with
+// 2 rather than 1: 96 -> 84 us), while tasks of one or two stages cost more
+// than they balance.
+static int sm_pick_ks(long items, long cap, int nst) {
+  int ks = nst >= 6 ? 2 : 1;
+  while (ks < kSmBlockWaves && items * ks * 2 <= 3 * cap && nst / (ks * 2) >= 3) ks *= 2;
+  return ks;
+}
 template <int MODE, int NBLK, int RUN, int DEPTH>
 static hipError_t sm_launch(const Dims &d, const Inputs &in, const Work &w, hipStream_t s) {
   using C = SmCfg<NBLK, RUN, DEPTH>;
@@ -512,8 +519,7 @@ static hipError_t sm_launch(const Dims &d, const Inputs &in, const Work &w, hipS
   // K stages of the shortest item (the shared expert's down K is I_s)
   const int kmin = MODE == kSmGateUp ? d.H : (d.Is > 0 && d.Is < d.I ? d.Is : d.I);
   const int nst = kmin * 2 / RUN;
-  int ks = 1;
-  while (ks < kSmBlockWaves && items * ks * 2 <= 3 * cap && nst / (ks * 2) >= 3) ks *= 2;
+  const int ks = sm_pick_ks(items, cap, nst);
   const long per_block = kSmBlockWaves / ks;
   const long grid = (items + per_block - 1) / per_block;
   hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(kSmBlockWaves * kWave), C::LDS, s,
@@ -545,8 +551,7 @@ static hipError_t sm_fp4_launch(const Dims &d, const Inputs &in, const Work &w, 
   const long cap = static_cast<long>(sm_cus()) * blocks_per_cu * kSmBlockWaves;
   const int kmin = MODE == kSmGateUp ? d.H : (d.Is > 0 && d.Is < d.I ? d.Is : d.I);
   const int nst = kmin / kFp4StageK;
-  int ks = 1;
-  while (ks < kSmBlockWaves && items * ks * 2 <= 3 * cap && nst / (ks * 2) >= 3) ks *= 2;
+  const int ks = sm_pick_ks(items, cap, nst);
   const long per_block = kSmBlockWaves / ks;
   const long grid = (items + per_block - 1) / per_block;
   hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(kSmBlockWaves * kWave), kFp4Lds, s,

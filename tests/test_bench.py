@@ -33,6 +33,19 @@ def test_decode_counts_match_the_byte_rule():
     assert c["flops"] == 2 * 16 * E * H + 2 * 16 * 8 * 3 * H * I
 
 
+def test_mxfp4_counts_take_half_a_byte_per_weight_and_a_scale_byte_per_32():
+    wl = synth.WORKLOADS["decode_mxfp4"]
+    D = 76
+    c = bench.layer_counts(wl, 16, D)
+    H, I, E = wl.hidden, wl.inter, wl.experts
+    w13 = D * (2 * I * H // 2 + 2 * I * H // 32)
+    w2 = D * (H * I // 2 + H * I // 32)
+    assert c["bytes"] == w13 + w2 + E * H * 2 + 2 * 16 * H * 2
+    assert c["gateup"]["bytes"] == w13 + 16 * H * 2 + 16 * 8 * I * 2   # x in, bf16 h out
+    assert bench.MFMA_PEAK_TFLOPS["mxfp4"] == bench.MFMA_PEAK_TFLOPS["bf16"]
+    assert bench.COMPUTE_DTYPE["mxfp4"] == "bf16"
+
+
 def test_recorded_traffic_follows_the_kernel_sources(tmp_path, monkeypatch):
     """The counters stand only while the kernel's sources are the ones counted."""
     files = bench.KERNEL_SOURCES["small_m"]
