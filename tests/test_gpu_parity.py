@@ -212,6 +212,20 @@ def test_gated_shared_unrenormalised_f32():
     run_case(GATED_F32)
 
 
+def test_prefill_gated_shared_full_size():
+    """The prefill layer with the sigmoid-gated shared blend, every token."""
+    wl = synth.WORKLOADS["prefill_bf16"].replace(name="prefill_gated", shared_gate=True)
+    run_case(wl, path="grouped")
+
+
+def test_large_fp8_sqrtsoftplus_gated_shared_sampled():
+    """H = 7168: every token's row spans four combine blocks, each forming
+    the gate's dot product itself; sqrtsoftplus with a selection bias."""
+    wl = synth.WORKLOADS["large_fp8"].replace(name="large_gated", m=512, gating="sqrtsoftplus",
+                                              zipf_alpha=0.05, shared_gate=True)
+    run_case(wl, path="grouped", tokens=_sample(wl.m, seed=3), lazy=True)
+
+
 def test_decode_sqrtsoftplus_bias_full_size():
     wl = synth.WORKLOADS["decode_bf16"].replace(name="decode_sqrtsp", gating="sqrtsoftplus",
                                                 routed_scale=2.5, zipf_alpha=0.05)
