@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of one MoE FFN layer forward on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--m M]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--m M] [--launch eager|graph]
 
 A step is one full layer forward (router, gating + top-k, sort by expert,
 [fp8 activation quantisation,] gate/up + SwiGLU, down, combine) over one batch
@@ -54,6 +54,9 @@ def parse():
     ap.add_argument("--kernel-events", choices=("timed", "off"), default="timed",
                     help="timed: record HIP events around the dominant kernel inside the timed "
                          "steps (its duration for the roofline); off: time it in a separate loop")
+    ap.add_argument("--launch", choices=("eager", "graph"), default="eager",
+                    help="graph: each weight copy's layer forward (with its timing events) is "
+                         "captured once in a HIP graph and the timed steps replay the graphs")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="before the timed region, run one plain device copy of this many MiB "
                          "(a known-size reference for HBM byte counters)")
@@ -226,7 +229,25 @@ def main():
 
     for i in range(args.warmup):
         step(i)
-    kev = [dom_events() for _ in range(args.steps)] if args.kernel_events == "timed" else None
+    graphs = None
+    if args.launch == "graph":
+        # one graph per weight copy; the library's one-time set-up ran eagerly
+        # in the warm-up steps.  Event nodes inside a replayed graph do not
+        # bracket the kernels on this stack (an 84 us kernel read 4.5 us), so
+        # the graphs carry no events and the dominant kernel is timed by the
+        # stage-event loop below
+        kev = None
+        torch.cuda.synchronize()
+        graphs = []
+        for c in range(copies):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                layers[c](x, out=out, topk_idx=idx, topk_w=tw)
+            graphs.append(g)
+        for i in range(args.warmup):
+            graphs[i % copies].replay()
+    else:
+        kev = [dom_events() for _ in range(args.steps)] if args.kernel_events == "timed" else None
     torch.cuda.synchronize()
     # ---- timed region: exactly K steps ----
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -234,7 +255,10 @@ def main():
     t0 = time.perf_counter()
     ev0.record(stream)
     for i in range(args.steps):
-        step(i, debug=None if kev is None else {"events": kev[i]})
+        if graphs is not None:
+            graphs[i % copies].replay()
+        else:
+            step(i, debug=None if kev is None else {"events": kev[i]})
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -274,7 +298,7 @@ def main():
                                f"k={wl.topk} I={wl.inter} I_s={wl.shared_inter} "
                                f"{wl.dtype} {wl.gating}",
                    "path": path, "active_experts": D, "weight_copies": copies,
-                   "launch": "eager"},
+                   "launch": args.launch},
         "layer": {"gbps": gb, "hbm_frac": gb / HBM_PEAK_GBPS, "tflops": tf,
                   "mfma_frac": tf / MFMA_PEAK_TFLOPS[wl.dtype],
                   "algorithmic_bytes": cnt["bytes"], "algorithmic_flops": cnt["flops"],
@@ -288,7 +312,10 @@ def main():
                      "frac": dom_tflops / mfma_peak if mfma_bound else dom_gbps / HBM_PEAK_GBPS,
                      "traffic": recorded_traffic(wl.name, m, dom, path),
                      "traffic_unit": "HBM bytes per launch, read + written (rocprofv3 counters)",
-                     "bytes_per_launch": cnt[dom]["bytes"], "us_per_launch": dom_ms * 1e3},
+                     "bytes_per_launch": cnt[dom]["bytes"], "us_per_launch": dom_ms * 1e3,
+                     "timing": ("HIP events around the kernel inside the timed steps"
+                                if dom_timed_ms is not None else
+                                "HIP events around the kernel in a separate eager loop")},
     }
     if not args.no_cpu_baseline:
         sample = args.cpu_sample or min(m, 64)
