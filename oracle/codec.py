@@ -20,6 +20,9 @@ Definitions written from the formats themselves:
   the magnitudes are 0, 0.5, 1, 1.5, 2, 3, 4, 6.  An E8M0 scale byte ``e`` is
   the power of two ``2**(e - 127)`` (255 is NaN).  Element j of a row is
   stored in byte j // 2, the even element in the low nibble.
+* MXFP8 (OCP Microscaling, FP8 E4M3 elements with an E8M0 scale shared by
+  32 consecutive elements): one e4m3fn byte per element, scaled by
+  ``2**(e - 127)``.
 """
 from __future__ import annotations
 
@@ -173,3 +176,9 @@ def mxfp4_decode(packed: np.ndarray, scales: np.ndarray, block: int = 32) -> np.
     p = np.asarray(packed, dtype=np.uint8)
     codes = np.stack([p & 0xF, p >> 4], axis=-1).reshape(p.shape[0], -1)
     return e2m1_decode(codes) * np.repeat(e8m0_decode(scales), block, axis=1)
+
+
+def mxfp8_decode(codes: np.ndarray, scales: np.ndarray, block: int = 32) -> np.ndarray:
+    """MXFP8 matrix -> exact float64 values: ``codes [rows, cols]`` e4m3fn
+    bytes, ``scales [rows, cols/block]`` E8M0 bytes."""
+    return e4m3_decode(codes) * np.repeat(e8m0_decode(scales), block, axis=1)

@@ -24,7 +24,7 @@ def _round_h(a: np.ndarray, dtype: str, block: int) -> np.ndarray:
     """Round a ``[..., I]`` SwiGLU output to the down operand format."""
     if dtype == "f32":
         return a
-    if dtype in ("bf16", "mxfp4"):
+    if dtype in ("bf16", "mxfp4", "mxfp8"):
         return bf16_round(a)
     flat = a.reshape(-1, a.shape[-1]).astype(np.float32)
     codes, scales = e4m3_quantize_rows(flat, block)

@@ -50,7 +50,7 @@ from dataclasses import dataclass
 import numpy as np
 
 from .codec import (bf16_decode, bf16_round, dequant_blocks,
-                    e4m3_decode, e4m3_quantize_rows, mxfp4_decode)
+                    e4m3_decode, e4m3_quantize_rows, mxfp4_decode, mxfp8_decode)
 
 
 @dataclass
@@ -61,7 +61,7 @@ class LayerSpec:
     topk: int
     inter: int
     shared_inter: int
-    dtype: str            # "f32" | "bf16" | "fp8" | "mxfp4" (weights; x, h, y bf16)
+    dtype: str            # "f32" | "bf16" | "fp8" | "mxfp4" | "mxfp8" (MX: weights only; x, h, y bf16)
     gating: str           # "softmax" | "sigmoid" | "sqrtsoftplus"
     routed_scale: float = 1.0
     renormalize: bool = True
@@ -87,6 +87,8 @@ def weight_values(w, scale, dtype: str, block: int) -> np.ndarray:
         return bf16_decode(w.view(np.uint16) if w.dtype != np.uint16 else w)
     if dtype == "mxfp4":
         return mxfp4_decode(w.view(np.uint8), np.asarray(scale).view(np.uint8), 32)
+    if dtype == "mxfp8":
+        return mxfp8_decode(w.view(np.uint8), np.asarray(scale).view(np.uint8), 32)
     return dequant_blocks(w.view(np.uint8), np.asarray(scale, np.float32), block)
 
 
@@ -198,7 +200,7 @@ def round_intermediate(a: np.ndarray, dtype: str, block: int):
     """
     if dtype == "f32":
         return a, None, None
-    if dtype in ("bf16", "mxfp4"):   # MXFP4 weights: bf16 intermediate
+    if dtype in ("bf16", "mxfp4", "mxfp8"):   # MX weights: bf16 intermediate
         return bf16_round(a), None, None
     codes, scales = e4m3_quantize_rows(a.astype(np.float32), block)
     vals = e4m3_decode(codes) * np.repeat(scales.astype(np.float64), block, axis=1)

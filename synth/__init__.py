@@ -37,8 +37,10 @@ scale per 32 consecutive elements of a row, along K): shared exponent
 ``X = floor(log2(amax)) - 2`` (2 = the element format's largest exponent),
 scale byte ``X + 127``, elements rounded to the nearest of 0, 0.5, 1, 1.5,
 2, 3, 4, 6 (ties to the even code) after division by ``2**X``, saturating
-at 6; two elements per byte, the even one in the low nibble.  The layer
-receives codes and scales as given.
+at 6; two elements per byte, the even one in the low nibble.  MXFP8 weights
+(FP8 E4M3 elements, E8M0 scale per 32 along K): ``X = floor(log2(amax)) -
+8``, elements = torch's float8_e4m3fn cast of the quotient clamped to 448.
+The layer receives codes and scales as given.
 """
 from __future__ import annotations
 
@@ -62,7 +64,7 @@ class Workload:
     topk: int              # k
     inter: int             # I (per routed expert)
     shared_inter: int      # I_s, 0 = no shared expert
-    dtype: str             # "f32" | "bf16" | "fp8" | "mxfp4" (weights)
+    dtype: str             # "f32" | "bf16" | "fp8" | "mxfp4" | "mxfp8" (weights)
     gating: str            # "softmax" | "sigmoid" | "sqrtsoftplus"
     routed_scale: float    # multiplier after renormalisation
     seed: int
@@ -105,6 +107,9 @@ WORKLOADS: dict[str, Workload] = {
     # The decode layer with MXFP4 expert weights (same x and router draws).
     "decode_mxfp4": Workload("decode_mxfp4", m=16, hidden=2048, experts=128,
                              topk=8, inter=768, shared_inter=0, dtype="mxfp4",
+                             gating="softmax", routed_scale=1.0, seed=2),
+    "decode_mxfp8": Workload("decode_mxfp8", m=16, hidden=2048, experts=128,
+                             topk=8, inter=768, shared_inter=0, dtype="mxfp8",
                              gating="softmax", routed_scale=1.0, seed=2),
     # Prefill bf16 layer with one unweighted shared expert (I_s = 2048).
     "prefill_bf16": Workload("prefill_bf16", m=1024, hidden=2048,
@@ -212,6 +217,19 @@ def _mx_fp4(w: torch.Tensor) -> tuple[torch.Tensor, torch.Tensor]:
     return packed.contiguous(), (X + 127).to(torch.uint8).contiguous()
 
 
+def _mx_fp8(w: torch.Tensor) -> tuple[torch.Tensor, torch.Tensor]:
+    """Store a 2-D fp32 matrix as MXFP8 codes (e4m3fn bytes) and E8M0 scale
+    bytes (one per 32 consecutive elements of a row)."""
+    r, c = w.shape
+    wb = w.reshape(r, c // 32, 32)
+    amax = wb.abs().amax(dim=-1)
+    X = torch.floor(torch.log2(amax.clamp_min(2.0 ** -126))) - 8
+    X = torch.where(amax > 0, X, torch.full_like(X, -127.0)).clamp(-127.0, 127.0)
+    q = (wb / torch.exp2(X)[..., None]).clamp(-448.0, 448.0)
+    codes = q.to(torch.float8_e4m3fn).view(torch.uint8).reshape(r, c)
+    return codes.contiguous(), (X + 127).to(torch.uint8).contiguous()
+
+
 def _draw_matrix(seed: int, rows: int, cols: int, device) -> torch.Tensor:
     g = torch.Generator(device=device)
     g.manual_seed(seed)
@@ -226,6 +244,8 @@ def _store_weight(w: torch.Tensor, dtype: str, block: int):
         return w.to(torch.bfloat16), None
     if dtype == "mxfp4":
         return _mx_fp4(w)
+    if dtype == "mxfp8":
+        return _mx_fp8(w)
     return _block_fp8(w, block)
 
 
@@ -248,12 +268,12 @@ def make_inputs(wl: Workload, device="cpu", m: int | None = None) -> dict:
     out["bias"] = None if b is None else torch.from_numpy(b).to(device)
     E, H, I = wl.experts, wl.hidden, wl.inter
     wdt = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8,
-           "mxfp4": torch.uint8}[wl.dtype]
+           "mxfp4": torch.uint8, "mxfp8": torch.uint8}[wl.dtype]
     pk = 2 if wl.dtype == "mxfp4" else 1     # elements per stored byte along K
     w13 = torch.empty((E, 2 * I, H // pk), dtype=wdt, device=device)
     w2 = torch.empty((E, H, I // pk), dtype=wdt, device=device)
     s13 = s2 = None
-    if wl.dtype == "mxfp4":
+    if wl.dtype in ("mxfp4", "mxfp8"):
         s13 = torch.empty((E, 2 * I, H // 32), dtype=torch.uint8, device=device)
         s2 = torch.empty((E, H, I // 32), dtype=torch.uint8, device=device)
     if wl.dtype == "fp8":

@@ -213,3 +213,38 @@ def test_synth_mxfp4_storage_is_nearest_with_saturation():
             got = np.abs(v[r, 32 * b:32 * b + 32]) / 2.0 ** X
             assert np.array_equal(got, near)
             assert np.all(np.sign(v[r, 32 * b:32 * b + 32]) * np.sign(blk) >= 0)
+
+
+def test_mxfp8_decode_applies_one_scale_per_32_elements():
+    from oracle.codec import e4m3_decode, mxfp8_decode
+    codes = (np.arange(64, dtype=np.uint8) * 3).reshape(1, 64)
+    codes[codes & 0x7F == 0x7F] = 0                  # no NaN codes
+    scales = np.array([[127 - 4, 127 + 5]], np.uint8)
+    v = mxfp8_decode(codes, scales)
+    want = e4m3_decode(codes[0]) * np.where(np.arange(64) < 32, 2.0 ** -4, 2.0 ** 5)
+    assert np.array_equal(v[0], want)
+
+
+def test_synth_mxfp8_storage_is_nearest_e4m3_of_the_quotient():
+    """Brute force over all finite e4m3 magnitudes: the stored code is a
+    nearest one to v / 2**X (X = floor(log2(amax)) - 8, the quotient of the
+    block maximum lands in [256, 512) and saturates at 448)."""
+    import torch
+    import synth
+    from oracle.codec import e4m3_decode, mxfp8_decode
+    g = torch.Generator().manual_seed(4)
+    w = torch.randn((6, 128), generator=g) * 0.02
+    codes, sc = synth._mx_fp8(w)
+    v = mxfp8_decode(codes.numpy(), sc.numpy())
+    grid = np.unique(np.abs(e4m3_decode(np.arange(256, dtype=np.uint8))))
+    grid = grid[np.isfinite(grid)]
+    wn = w.double().numpy()
+    for r in range(6):
+        for b in range(4):
+            blk = wn[r, 32 * b:32 * b + 32]
+            X = np.floor(np.log2(np.abs(blk).max())) - 8
+            assert sc.numpy()[r, b] == X + 127
+            q = np.minimum(np.abs(blk.astype(np.float32) / np.float32(2.0 ** X)), 448.0)
+            got = np.abs(v[r, 32 * b:32 * b + 32]) / 2.0 ** X
+            dist = np.abs(q[:, None] - grid[None, :])
+            assert np.all(np.abs(q - got) <= dist.min(axis=1) + 1e-12)

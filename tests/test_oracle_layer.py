@@ -43,6 +43,8 @@ def _values(wl, inp):
             return a.astype(np.float64)
         if wl.dtype == "bf16":
             return bf16_decode(a)
+        if wl.dtype == "mxfp8":
+            return e4m3_decode(a) * np.exp2(np.repeat(to_np(s).astype(np.float64) - 127.0, 32, axis=-1))
         if wl.dtype == "mxfp4":
             # unpacked here with shifts on the stacked array and a lookup
             # table of the element values, independently of mxfp4_decode
@@ -172,7 +174,9 @@ def _mxfp4_workloads(n=10):
     return out
 
 
-@pytest.mark.parametrize("wl", _mxfp4_workloads(), ids=lambda w: w.name)
+@pytest.mark.parametrize("wl", _mxfp4_workloads() + [
+    w.replace(name=w.name.replace("mx", "mx8_"), dtype="mxfp8") for w in _mxfp4_workloads(6)],
+    ids=lambda w: w.name)
 def test_mxfp4_layers_sparse_equals_dense(wl):
     inp = synth.make_inputs(wl)
     r = _oracle(wl, inp)
