@@ -33,8 +33,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0
 # MXFP4 weights are converted to bf16 in registers and multiplied on the
 # bf16 MFMA
-MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3, "mxfp4": 2500.0}
-COMPUTE_DTYPE = {"mxfp4": "bf16"}
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3, "mxfp4": 2500.0, "mxfp8": 2500.0}
+COMPUTE_DTYPE = {"mxfp4": "bf16", "mxfp8": "bf16"}
 METRIC = "MoE layer tokens/s; prefill TFLOP/s vs MFMA peak; decode GB/s vs HBM peak"
 
 
@@ -64,7 +64,7 @@ def parse():
 
 
 def esz(dtype):
-    return {"f32": 4, "bf16": 2, "fp8": 1, "mxfp4": 0.5}[dtype]
+    return {"f32": 4, "bf16": 2, "fp8": 1, "mxfp4": 0.5, "mxfp8": 1}[dtype]
 
 
 # Source files of each expert-kernel family: HBM byte counters recorded in
@@ -108,13 +108,13 @@ def layer_counts(wl, m, D):
     ae = 4 if wl.dtype == "f32" else 2              # x / out / y element bytes
     if wl.dtype == "fp8":
         sc = lambda r, c: (r // 128) * (c // 128) * 4     # fp32 per 128x128 block
-    elif wl.dtype == "mxfp4":
+    elif wl.dtype in ("mxfp4", "mxfp8"):
         sc = lambda r, c: r * (c // 32)                    # E8M0 byte per 32 along K
     else:
         sc = lambda r, c: 0
     w13 = D * (2 * I * H * we + sc(2 * I, H)) + (2 * Is * H * we + sc(2 * Is, H) if Is else 0)
     w2 = D * (H * I * we + sc(H, I)) + (H * Is * we + sc(H, Is) if Is else 0)
-    hb = {"f32": 4, "bf16": 2, "fp8": 1, "mxfp4": 2}[wl.dtype]   # h element bytes
+    hb = {"f32": 4, "bf16": 2, "fp8": 1, "mxfp4": 2, "mxfp8": 2}[wl.dtype]   # h element bytes
     h_bytes = (te * I + m * Is) * hb + ((te * I + m * Is) // 128 * 4 if wl.dtype == "fp8" else 0)
     x_in = m * H * (1 + 4 / 128 if wl.dtype == "fp8" else ae)
     y_bytes = (te + (m if Is else 0)) * H * ae

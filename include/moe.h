@@ -51,8 +51,16 @@ typedef struct moe_plan_s *moe_plan_t;
  * in the low nibble), with one E8M0 scale byte 2^(e - 127) per 32 consecutive
  * elements of a row; scale bytes 0 and 255 are not supported.  The MX
  * elements are the "block-scaled" weight format of page 1 (its NVFP4 W4A4
- * MoE) on gfx950's own FP4 conversion; x, h and out stay bf16. */
-typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2, MOE_MXFP4 = 3 } moe_dtype_t;
+ * MoE) on gfx950's own FP4 conversion; x, h and out stay bf16.  MOE_MXFP8
+ * (expert weights only) is OCP Microscaling FP8: one e4m3fn byte per element
+ * with the same E8M0 scale per 32 elements along K. */
+typedef enum {
+  MOE_F32 = 0,
+  MOE_BF16 = 1,
+  MOE_FP8_E4M3 = 2,
+  MOE_MXFP4 = 3,
+  MOE_MXFP8 = 4
+} moe_dtype_t;
 
 /* Gating (page 3, step 2 "Batched topK dispatch": softmax, sigmoid with a
  * correction bias, sqrtsoftplus with a correction bias, softmax with a
@@ -76,7 +84,7 @@ typedef enum {
   MOE_PATH_AUTO = 0,
   MOE_PATH_SIMPLE = 1,   /* fp32 VALU kernels, any dtype */
   MOE_PATH_GROUPED = 2,  /* MFMA grouped GEMM, bf16 / fp8 */
-  MOE_PATH_SMALL_M = 3   /* weight-streaming path, bf16 / MXFP4, m <= 16 */
+  MOE_PATH_SMALL_M = 3   /* weight-streaming path, bf16 / MXFP4 / MXFP8, m <= 16 */
 } moe_path_t;
 
 typedef enum {
@@ -98,7 +106,7 @@ typedef struct {
   int32_t renormalize;   /* 1: divide the k selected weights by their sum */
   float routed_scale;    /* multiplier applied after renormalisation */
   int32_t weight_dtype;  /* moe_dtype_t.  F32 => x/out are fp32;
-                            BF16, FP8_E4M3 or MXFP4 => x/out are bf16 */
+                            BF16, FP8_E4M3, MXFP4 or MXFP8 => x/out are bf16 */
   int32_t path;          /* moe_path_t */
 } moe_config_t;
 
@@ -107,7 +115,8 @@ typedef struct {
  * w2  [H, I_s].  fp8: w13_scale [2*I_s/128, H/128], w2_scale [H/128, I_s/128]
  * fp32 per 128x128 block (value = code * scale); MXFP4: w13 [2*I_s, H/2] and
  * w2 [H, I_s/2] bytes, w13_scale [2*I_s, H/32] and w2_scale [H, I_s/32] E8M0
- * bytes; NULL otherwise.
+ * bytes; MXFP8: w13 [2*I_s, H] and w2 [H, I_s] bytes with the same scales;
+ * NULL otherwise.
  * gate [H] in the format of x (fp32 or bf16), or NULL: when set, the shared
  * row of token t is added with weight sigmoid(x[t] . gate) (fp32 dot product
  * of the unquantised input; page 3, step 8, the shared-expert blend),
@@ -162,9 +171,9 @@ typedef struct {
  * Errors: MOE_ERR_INVALID_ARG for non-positive sizes, topk outside
  * [1, min(E,32)], E > 1024, unknown enums; MOE_ERR_UNSUPPORTED for fp8 with
  * H, I or I_s not multiples of 128, bf16/fp8 with H, I or I_s not multiples
- * of 32, MXFP4 with H, I or I_s not multiples of 256, with max_tokens above
- * 16 or with a path other than AUTO / SMALL_M (MXFP4 runs on the m <= 16
- * weight-streaming path only), SMALL_M forced with fp8/fp32 weights, or
+ * of 32, MXFP4 (MXFP8) with H, I or I_s not multiples of 256 (128), with
+ * max_tokens above 16 or with a path other than AUTO / SMALL_M (the MX
+ * formats run on the m <= 16 weight-streaming path only), SMALL_M forced with fp8/fp32 weights, or
  * sizes whose operands
  * reach 2 GiB (max_tokens * topk * max(H, I, I_s) elements, or one expert's
  * 2 * max(I, I_s) * H weight elements, at 2 bytes per bf16/fp8 element and 4
@@ -193,9 +202,10 @@ size_t moe_workspace_bytes(moe_plan_t plan, int32_t m);
  *   router_bias[E]        fp32 selection-only bias, or NULL (any gating).
  *   w13_scale  [E, 2I/128, H/128], w2_scale [E, H/128, I/128]: fp32 block
  *                         scales for FP8 weights; [E, 2I, H/32] and
- *                         [E, H, I/32] E8M0 bytes for MXFP4 weights (then
- *                         experts_w13 is [E, 2I, H/2] and experts_w2
- *                         [E, H, I/2] bytes); NULL otherwise.
+ *                         [E, H, I/32] E8M0 bytes for MXFP4 / MXFP8
+ *                         weights (then experts_w13 is [E, 2I, H/2] and
+ *                         experts_w2 [E, H, I/2] bytes for MXFP4, [E, 2I, H]
+ *                         and [E, H, I] bytes for MXFP8); NULL otherwise.
  *   workspace  device buffer of >= moe_workspace_bytes(plan, m) bytes,
  *              256-byte aligned; its contents need not be initialised.
  * Every pointer must be 16-byte aligned.  FP8: activations are quantised

@@ -12,11 +12,11 @@ import os
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libmoe.so")
 
-F32, BF16, FP8_E4M3, MXFP4 = 0, 1, 2, 3
+F32, BF16, FP8_E4M3, MXFP4, MXFP8 = 0, 1, 2, 3, 4
 GATE_SOFTMAX, GATE_SIGMOID, GATE_SQRTSOFTPLUS = 0, 1, 2
 PATHS = {"auto": 0, "simple": 1, "grouped": 2, "small_m": 3}
 PATH_NAMES = {v: k for k, v in PATHS.items()}
-DTYPES = {"f32": F32, "bf16": BF16, "fp8": FP8_E4M3, "mxfp4": MXFP4}
+DTYPES = {"f32": F32, "bf16": BF16, "fp8": FP8_E4M3, "mxfp4": MXFP4, "mxfp8": MXFP8}
 GATINGS = {"softmax": GATE_SOFTMAX, "sigmoid": GATE_SIGMOID,
            "sqrtsoftplus": GATE_SQRTSOFTPLUS}
 

@@ -14,9 +14,10 @@ constexpr int kWave = 64;
 constexpr int kQBlock = 128;       // fp8 block edge (weights 128x128, rows x 128)
 constexpr float kE4M3Max = 448.0f;
 
-// Storage-format tags used as template parameters (kMXFP4: OCP MX FP4 E2M1
-// weights with an E8M0 scale per 32 elements along K; activations bf16).
-enum : int { kF32 = 0, kBF16 = 1, kFP8 = 2, kMXFP4 = 3 };
+// Storage-format tags used as template parameters (kMXFP4 / kMXFP8: OCP MX
+// FP4 E2M1 / FP8 E4M3 weights with an E8M0 scale per 32 elements along K;
+// activations bf16).
+enum : int { kF32 = 0, kBF16 = 1, kFP8 = 2, kMXFP4 = 3, kMXFP8 = 4 };
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 

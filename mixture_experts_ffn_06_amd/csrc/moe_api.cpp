@@ -40,7 +40,9 @@ bool aligned(const void *p, size_t a) {
 int resolve_path(const moe_config_t &c, int m) {
   if (c.path != MOE_PATH_AUTO) return c.path;
   if (c.weight_dtype == MOE_F32) return MOE_PATH_SIMPLE;
-  if ((c.weight_dtype == MOE_BF16 || c.weight_dtype == MOE_MXFP4) && m <= 16) return MOE_PATH_SMALL_M;
+  if ((c.weight_dtype == MOE_BF16 || c.weight_dtype == MOE_MXFP4 || c.weight_dtype == MOE_MXFP8) &&
+      m <= 16)
+    return MOE_PATH_SMALL_M;
   return MOE_PATH_GROUPED;
 }
 
@@ -122,7 +124,7 @@ int check_cfg(const moe_config_t &c) {
   if (c.num_experts > 1024) return MOE_ERR_INVALID_ARG;
   if (c.topk > c.num_experts || c.topk > 32) return MOE_ERR_INVALID_ARG;
   if (c.gating < MOE_GATE_SOFTMAX || c.gating > MOE_GATE_SQRTSOFTPLUS) return MOE_ERR_INVALID_ARG;
-  if (c.weight_dtype < MOE_F32 || c.weight_dtype > MOE_MXFP4) return MOE_ERR_INVALID_ARG;
+  if (c.weight_dtype < MOE_F32 || c.weight_dtype > MOE_MXFP8) return MOE_ERR_INVALID_ARG;
   if (c.path < MOE_PATH_AUTO || c.path > MOE_PATH_SMALL_M) return MOE_ERR_INVALID_ARG;
   if (!(c.routed_scale == c.routed_scale)) return MOE_ERR_INVALID_ARG;  // NaN
   if (c.hidden % 8) return MOE_ERR_UNSUPPORTED;
@@ -134,13 +136,13 @@ int check_cfg(const moe_config_t &c) {
     return MOE_ERR_UNSUPPORTED;
   if (c.weight_dtype == MOE_F32 && c.path != MOE_PATH_AUTO && c.path != MOE_PATH_SIMPLE)
     return MOE_ERR_UNSUPPORTED;
-  if (c.path == MOE_PATH_SMALL_M && c.weight_dtype != MOE_BF16 && c.weight_dtype != MOE_MXFP4)
-    return MOE_ERR_UNSUPPORTED;
-  // MXFP4 runs on the weight-streaming path only: one stage is 256 K
-  // elements, batches of at most 16 tokens
-  if (c.weight_dtype == MOE_MXFP4 &&
-      (c.hidden % 256 || c.inter % 256 || c.shared_inter % 256 || c.max_tokens > 16 ||
-       (c.path != MOE_PATH_AUTO && c.path != MOE_PATH_SMALL_M)))
+  const bool mx = c.weight_dtype == MOE_MXFP4 || c.weight_dtype == MOE_MXFP8;
+  if (c.path == MOE_PATH_SMALL_M && c.weight_dtype != MOE_BF16 && !mx) return MOE_ERR_UNSUPPORTED;
+  // the MX formats run on the weight-streaming path only: one stage is 256
+  // (FP4) or 128 (FP8) K elements, batches of at most 16 tokens
+  const int mx_k = c.weight_dtype == MOE_MXFP4 ? 256 : 128;
+  if (mx && (c.hidden % mx_k || c.inter % mx_k || c.shared_inter % mx_k || c.max_tokens > 16 ||
+             (c.path != MOE_PATH_AUTO && c.path != MOE_PATH_SMALL_M)))
     return MOE_ERR_UNSUPPORTED;
   // the expert kernels address each operand (token rows, the sorted h / y
   // rows, one expert's weight matrix) with 32-bit byte offsets
@@ -164,7 +166,8 @@ int run_forward(moe_plan_t plan, int32_t m, const void *x, const void *router_w,
   if (m < 0 || m > c.max_tokens || topk != c.topk) return MOE_ERR_INVALID_ARG;
   if (m == 0) return MOE_OK;
   const bool fp8 = c.weight_dtype == MOE_FP8_E4M3;
-  const bool scaled = fp8 || c.weight_dtype == MOE_MXFP4;   // block scales given
+  const bool mx = c.weight_dtype == MOE_MXFP4 || c.weight_dtype == MOE_MXFP8;
+  const bool scaled = fp8 || mx;   // block scales given
   const void *need[] = {x, router_w, w13, w2, out, topk_idx, topk_w, ws};
   for (const void *q : need)
     if (!q || !aligned(q, 16)) return MOE_ERR_INVALID_ARG;
@@ -196,7 +199,8 @@ int run_forward(moe_plan_t plan, int32_t m, const void *x, const void *router_w,
   d.Is = c.shared_inter; d.k = c.topk; d.te = m * c.topk;
   d.wdt = c.weight_dtype == MOE_F32 ? moe::kF32
         : fp8 ? moe::kFP8
-        : c.weight_dtype == MOE_MXFP4 ? moe::kMXFP4 : moe::kBF16;
+        : c.weight_dtype == MOE_MXFP4 ? moe::kMXFP4
+        : c.weight_dtype == MOE_MXFP8 ? moe::kMXFP8 : moe::kBF16;
   d.gating = c.gating; d.renorm = c.renormalize ? 1 : 0; d.scale = c.routed_scale;
   moe::Inputs in;
   in.x = x; in.router_w = router_w; in.w13 = w13; in.w2 = w2;

@@ -241,32 +241,43 @@ __global__ __launch_bounds__(kSmBlockWaves * kWave) void sm_kernel(Dims d, Input
 }
 
 // ---------------------------------------------------------------------------
-// MXFP4 weights (OCP MX: FP4 E2M1 elements, one E8M0 scale per 32 elements
-// of a row along K; tokens and h stay bf16).  Same items, K split and
-// two-slot ring as sm_kernel with NBLK = 2; a stage is 128 bytes = 256 K
-// elements of each of the item's 32 weight rows (four 1 KB direct loads of 8
-// whole rows each, pieces swizzled per row) plus the rows' 8 scale bytes (one
-// 4-byte direct load per lane).  Lane group g = lane / 16 takes the K
-// elements [64 g, 64 g + 64) of a stage -- 32 contiguous bytes of its row,
-// eight elements per MFMA step -- and reads the token row to match (any split
-// of K over the lanes gives the same product when A and B share it).  The
-// weights become bf16 in registers by the scaled fp4 -> bf16 conversion, which
-// multiplies by 2 to the power of the scale operand's exponent: with the scale
+// MX weights (OCP Microscaling: FP4 E2M1 or FP8 E4M3 elements, one E8M0
+// scale per 32 elements of a row along K; tokens and h stay bf16).  Same
+// items, K split and two-slot ring as sm_kernel with NBLK = 2; a stage is 128
+// bytes of each of the item's 32 weight rows (256 K elements of FP4, 128 of
+// FP8; four 1 KB direct loads of 8 whole rows each, pieces swizzled per row)
+// plus the rows' scale bytes for those K elements (8 or 4 per row, one 4-byte
+// direct load per lane).  Lane group g = lane / 16 takes 32 contiguous bytes
+// of its row per stage -- K elements [64 g, 64 g + 64) for FP4, [32 g, 32 g +
+// 32) for FP8, eight per MFMA step -- and reads its token row to match (any
+// split of K over the lanes gives the same product when A and B share it).
+// The weights become bf16 in registers by gfx950's scaled conversions, which
+// multiply by 2 to the power of the scale operand's exponent: with the scale
 // 2^(e - 127) built from the E8M0 byte that is exact.  The MFMA is the bf16
 // 16x16x32 of the bf16 path.
-constexpr int kFp4Run = 128;                            // fp4 bytes per row per stage
-constexpr int kFp4StageK = 2 * kFp4Run;                 // K elements per stage
-constexpr int kFp4Rows = 32;                            // weight rows per item
-constexpr int kFp4WBytes = kFp4Rows * kFp4Run;          // weight bytes per stage
-constexpr int kFp4SBytes = kFp4Rows * kFp4StageK / 32;  // scale bytes per stage
-constexpr int kFp4Stage = kFp4WBytes + kFp4SBytes;
-constexpr int kFp4WaveLds = 2 * kFp4Stage;
-constexpr int kFp4Lds = kSmBlockWaves * kFp4WaveLds;
-static_assert(kFp4WaveLds >= 2 * kWave * 16, "partial sums fit the ring");
+constexpr int kMxRun = 128;                         // weight bytes per row per stage
+constexpr int kMxRows = 32;                         // weight rows per item
+constexpr int kMxWBytes = kMxRows * kMxRun;         // weight bytes per stage
+constexpr int kMxSBytes = 256;                      // scale area per stage
+constexpr int kMxStage = kMxWBytes + kMxSBytes;
+constexpr int kMxWaveLds = 2 * kMxStage;
+constexpr int kMxLds = kSmBlockWaves * kMxWaveLds;
+static_assert(kMxWaveLds >= 2 * kWave * 16, "partial sums fit the ring");
+
+template <int FMT>
+struct MxCfg {
+  static constexpr bool F4 = FMT == kMXFP4;
+  static constexpr int KPS = F4 ? 2 * kMxRun : kMxRun;   // K elements per stage
+  static constexpr int SSTEPS = KPS / 32;                 // MFMA steps per stage
+  static constexpr int SPR = KPS / 32;                    // scale bytes per row per stage
+  static constexpr int ABYTES = KPS / 4 * 2;              // token bytes per lane group per stage
+  static_assert(FMT == kMXFP4 || FMT == kMXFP8, "MX formats");
+};
 
 // The lane's stage operands: pieces p0, p1 of its row in blocks 0 and 1 and
-// the two blocks' 8 scale bytes of the row, read and waited for together.
-__device__ __forceinline__ void fp4_stage_reads(uint32_t p0, uint32_t p1, uint32_t ps, u32x4_t &b0,
+// the two blocks' scale bytes of the row (FP4: 8 per row, FP8: 4), read and
+// waited for together.
+__device__ __forceinline__ void mx4_stage_reads(uint32_t p0, uint32_t p1, uint32_t ps, u32x4_t &b0,
                                                 u32x4_t &b1, u32x4_t &b2, u32x4_t &b3, u32x2_t &s0,
                                                 u32x2_t &s1) {
   asm volatile(
@@ -278,7 +289,21 @@ __device__ __forceinline__ void fp4_stage_reads(uint32_t p0, uint32_t p1, uint32
       "ds_read_b64 %5, %8 offset:%10\n"
       "s_waitcnt lgkmcnt(0)"
       : "=&v"(b0), "=&v"(b1), "=&v"(b2), "=&v"(b3), "=&v"(s0), "=&v"(s1)
-      : "v"(p0), "v"(p1), "v"(ps), "i"(16 * kFp4Run), "i"(16 * 8));
+      : "v"(p0), "v"(p1), "v"(ps), "i"(16 * kMxRun), "i"(16 * 8));
+}
+__device__ __forceinline__ void mx8_stage_reads(uint32_t p0, uint32_t p1, uint32_t ps, u32x4_t &b0,
+                                                u32x4_t &b1, u32x4_t &b2, u32x4_t &b3, uint32_t &s0,
+                                                uint32_t &s1) {
+  asm volatile(
+      "ds_read_b128 %0, %6\n"
+      "ds_read_b128 %1, %7\n"
+      "ds_read_b128 %2, %6 offset:%9\n"
+      "ds_read_b128 %3, %7 offset:%9\n"
+      "ds_read_b32 %4, %8\n"
+      "ds_read_b32 %5, %8 offset:%10\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(b0), "=&v"(b1), "=&v"(b2), "=&v"(b3), "=&v"(s0), "=&v"(s1)
+      : "v"(p0), "v"(p1), "v"(ps), "i"(16 * kMxRun), "i"(16 * 4));
 }
 
 // Eight e2m1 codes (one 32-bit word, the even element in the low nibble of
@@ -292,12 +317,24 @@ __device__ __forceinline__ bf16x8_t fp4x8_to_bf16(uint32_t word, uint32_t e) {
   return bf16x8_t{q0[0], q0[1], q1[0], q1[1], q2[0], q2[1], q3[0], q3[1]};
 }
 
-template <int MODE>
-__global__ __launch_bounds__(kSmBlockWaves * kWave) void sm_fp4_kernel(Dims d, Inputs in, Work w, int ks) {
+// Eight e4m3 codes (two 32-bit words, lowest byte first) times 2^(e - 127),
+// as bf16.
+__device__ __forceinline__ bf16x8_t fp8x8_to_bf16(uint32_t lo, uint32_t hi, uint32_t e) {
+  const float sc = __uint_as_float(e << 23);
+  const bf16x2_t q0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, sc, false);
+  const bf16x2_t q1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, sc, true);
+  const bf16x2_t q2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, sc, false);
+  const bf16x2_t q3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, sc, true);
+  return bf16x8_t{q0[0], q0[1], q1[0], q1[1], q2[0], q2[1], q3[0], q3[1]};
+}
+
+template <int MODE, int FMT>
+__global__ __launch_bounds__(kSmBlockWaves * kWave) void sm_mx_kernel(Dims d, Inputs in, Work w, int ks) {
+  using C = MxCfg<FMT>;
   constexpr int CW = MODE == kSmGateUp ? 16 : 32;   // output columns per item
   extern __shared__ __align__(1024) uint8_t lds[];
   const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6);
-  uint8_t *ring = lds + wave * kFp4WaveLds;
+  uint8_t *ring = lds + wave * kMxWaveLds;
   const int item = uniform(blockIdx.x * (kSmBlockWaves / ks) + wave / ks);
   const int kp = uniform(wave % ks);
 
@@ -330,7 +367,8 @@ __global__ __launch_bounds__(kSmBlockWaves * kWave) void sm_fp4_kernel(Dims d, I
     c0 = cg * CW;
     ncol = MODE == kSmGateUp ? inter : d.H;
     const int K = MODE == kSmGateUp ? d.H : inter;
-    const int abytes = K * 2, wbytes = K / 2, sbytes = K / 32;   // per token / weight row
+    // bytes per token / weight / scale row
+    const int abytes = K * 2, wbytes = C::F4 ? K / 2 : K, sbytes = K / 32;
 
     const int r = lane & 15, g = lane >> 4;
     const int ar = min(r, rows - 1);   // rows past the slot's end repeat its last row
@@ -343,16 +381,16 @@ __global__ __launch_bounds__(kSmBlockWaves * kWave) void sm_fp4_kernel(Dims d, I
       Ab = static_cast<const uint8_t *>(in.x);
       aoff = static_cast<uint32_t>(tok) * abytes;
       const size_t eo = shared ? 0 : static_cast<size_t>(e) * 2 * d.I;   // first weight row
-      Wb = static_cast<const uint8_t *>(shared ? in.sw13 : in.w13) + eo * (d.H / 2);
+      Wb = static_cast<const uint8_t *>(shared ? in.sw13 : in.w13) + eo * (C::F4 ? d.H / 2 : d.H);
       Sb = s13 + eo * (d.H / 32);
     } else {
       Ab = static_cast<const uint8_t *>(shared ? w.h_sh : w.h);
       aoff = static_cast<uint32_t>(seg0 + ar) * abytes;
       const size_t eo = shared ? 0 : static_cast<size_t>(e) * d.H;
-      Wb = static_cast<const uint8_t *>(shared ? in.sw2 : in.w2) + eo * (d.I / 2);
+      Wb = static_cast<const uint8_t *>(shared ? in.sw2 : in.w2) + eo * (C::F4 ? d.I / 2 : d.I);
       Sb = s2 + eo * (d.I / 32);
     }
-    aoff += g * 128;   // the lane's 64 K elements of each stage, in bf16
+    aoff += g * C::ABYTES;   // the lane group's K elements of each stage, in bf16
     // First weight row of block j (blocks past the last column read row 0
     // and store nothing).
     auto wrow = [&](int j) -> int {
@@ -369,49 +407,67 @@ __global__ __launch_bounds__(kSmBlockWaves * kWave) void sm_fp4_kernel(Dims d, I
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int row = (q % 2) * 8 + lane / 8;
-      qoff[q] = static_cast<uint32_t>(wrow(q / 2) + row) * wbytes + sm_swz<kFp4Run>(lane % 8, row) * 16;
+      qoff[q] = static_cast<uint32_t>(wrow(q / 2) + row) * wbytes + sm_swz<kMxRun>(lane % 8, row) * 16;
     }
-    // scales: lane l fetches 4 of the 8 scale bytes of item row l / 2
-    const int srow = lane >> 1;
-    const uint32_t soff = static_cast<uint32_t>(wrow(srow / 16) + srow % 16) * sbytes + (lane & 1) * 4;
+    // scales: FP4 lane l fetches 4 of the 8 bytes of item row l / 2; FP8 lane
+    // l the 4 bytes of item row l % 32 (lanes 32-63 repeat rows 0-31 into the
+    // unused upper half of the scale area)
+    const int srow = C::F4 ? lane >> 1 : lane & 31;
+    const uint32_t soff = static_cast<uint32_t>(wrow(srow / 16) + srow % 16) * sbytes + (C::F4 ? (lane & 1) * 4 : 0);
 
-    const int nst_all = K / kFp4StageK;
+    const int nst_all = K / C::KPS;
     const int st0 = uniform(nst_all * kp / ks), st1 = uniform(nst_all * (kp + 1) / ks);
-    uint4 aA[8], aB[8];
-    auto issue = [&](int st, int sl, uint4 (&A)[8]) {
-      uint8_t *slot = ring + sl * kFp4Stage;
-      const uint32_t kw = static_cast<uint32_t>(st) * kFp4Run;
+    uint4 aA[C::SSTEPS], aB[C::SSTEPS];
+    auto issue = [&](int st, int sl, uint4 (&A)[C::SSTEPS]) {
+      uint8_t *slot = ring + sl * kMxStage;
+      const uint32_t kw = static_cast<uint32_t>(st) * kMxRun;
 #pragma unroll
       for (int q = 0; q < 4; ++q) dma16_to_lds(Wb + (qoff[q] + kw), slot + q * 1024);
-      dma4_to_lds(Sb + (soff + static_cast<uint32_t>(st) * 8), slot + kFp4WBytes);
-      const uint32_t ka = static_cast<uint32_t>(st) * kFp4StageK * 2;
+      dma4_to_lds(Sb + (soff + static_cast<uint32_t>(st) * C::SPR), slot + kMxWBytes);
+      const uint32_t ka = static_cast<uint32_t>(st) * C::KPS * 2;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) A[i] = *reinterpret_cast<const uint4 *>(Ab + (aoff + ka) + i * 16);
+      for (int i = 0; i < C::SSTEPS; ++i) A[i] = *reinterpret_cast<const uint4 *>(Ab + (aoff + ka) + i * 16);
     };
     // lane reads logical pieces 2 g, 2 g + 1 of row r in both blocks and the
-    // row's scale bytes 2 g, 2 g + 1 (the 32-element blocks of its K range)
-    const uint32_t pp0 = static_cast<uint32_t>(r * kFp4Run + sm_swz<kFp4Run>(2 * g, r) * 16);
-    const uint32_t pp1 = static_cast<uint32_t>(r * kFp4Run + sm_swz<kFp4Run>(2 * g + 1, r) * 16);
-    const int sh = (2 * g % 4) * 8;    // bit offset of scale byte 2 g in its word
-    auto compute = [&](int sl, const uint4 (&A)[8]) {
-      const uint8_t *slot = ring + sl * kFp4Stage;
+    // row's scale bytes for its K elements
+    const uint32_t pp0 = static_cast<uint32_t>(r * kMxRun + sm_swz<kMxRun>(2 * g, r) * 16);
+    const uint32_t pp1 = static_cast<uint32_t>(r * kMxRun + sm_swz<kMxRun>(2 * g + 1, r) * 16);
+    auto compute = [&](int sl, const uint4 (&A)[C::SSTEPS]) {
+      const uint8_t *slot = ring + sl * kMxStage;
       const uint32_t base = lds_off(slot);
       u32x4_t b0, b1, b2, b3;
-      u32x2_t q0, q1;
-      fp4_stage_reads(base + pp0, base + pp1, base + kFp4WBytes + r * 8, b0, b1, b2, b3, q0, q1);
-      const uint32_t sw0 = g < 2 ? q0.x : q0.y, sw1 = g < 2 ? q1.x : q1.y;
-      const uint32_t e0[2] = {(sw0 >> sh) & 0xffu, (sw0 >> (sh + 8)) & 0xffu};
-      const uint32_t e1[2] = {(sw1 >> sh) & 0xffu, (sw1 >> (sh + 8)) & 0xffu};
-      const uint32_t w0[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
-      const uint32_t w1[8] = {b2.x, b2.y, b2.z, b2.w, b3.x, b3.y, b3.z, b3.w};
+      if constexpr (C::F4) {
+        // scale bytes 2 g (steps 0-3) and 2 g + 1 (steps 4-7) of the row's 8
+        u32x2_t q0, q1;
+        mx4_stage_reads(base + pp0, base + pp1, base + kMxWBytes + r * 8, b0, b1, b2, b3, q0, q1);
+        const int sh = (2 * g % 4) * 8;
+        const uint32_t sw0 = g < 2 ? q0.x : q0.y, sw1 = g < 2 ? q1.x : q1.y;
+        const uint32_t e0[2] = {(sw0 >> sh) & 0xffu, (sw0 >> (sh + 8)) & 0xffu};
+        const uint32_t e1[2] = {(sw1 >> sh) & 0xffu, (sw1 >> (sh + 8)) & 0xffu};
+        const uint32_t w0[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+        const uint32_t w1[8] = {b2.x, b2.y, b2.z, b2.w, b3.x, b3.y, b3.z, b3.w};
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const bf16x8_t a = __builtin_bit_cast(bf16x8_t, A[i]);
-        acc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, fp4x8_to_bf16(w0[i], e0[i / 4]), acc[0], 0, 0, 0);
-        acc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, fp4x8_to_bf16(w1[i], e1[i / 4]), acc[1], 0, 0, 0);
+        for (int i = 0; i < 8; ++i) {
+          const bf16x8_t a = __builtin_bit_cast(bf16x8_t, A[i]);
+          acc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, fp4x8_to_bf16(w0[i], e0[i / 4]), acc[0], 0, 0, 0);
+          acc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, fp4x8_to_bf16(w1[i], e1[i / 4]), acc[1], 0, 0, 0);
+        }
+      } else {
+        // scale byte g of the row's 4 covers all of the lane's 32 elements
+        uint32_t q0, q1;
+        mx8_stage_reads(base + pp0, base + pp1, base + kMxWBytes + r * 4, b0, b1, b2, b3, q0, q1);
+        const uint32_t e0 = (q0 >> (8 * g)) & 0xffu, e1 = (q1 >> (8 * g)) & 0xffu;
+        const uint32_t w0[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+        const uint32_t w1[8] = {b2.x, b2.y, b2.z, b2.w, b3.x, b3.y, b3.z, b3.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const bf16x8_t a = __builtin_bit_cast(bf16x8_t, A[i]);
+          acc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, fp8x8_to_bf16(w0[2 * i], w0[2 * i + 1], e0), acc[0], 0, 0, 0);
+          acc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, fp8x8_to_bf16(w1[2 * i], w1[2 * i + 1], e1), acc[1], 0, 0, 0);
+        }
       }
     };
-    constexpr int LPS = 4 + 1 + 8;   // vector-memory ops per stage
+    constexpr int LPS = 4 + 1 + C::SSTEPS;   // vector-memory ops per stage
     const int n = st1 - st0;
     if (n > 0) {
       issue(st0, 0, aA);
@@ -437,7 +493,7 @@ __global__ __launch_bounds__(kSmBlockWaves * kWave) void sm_fp4_kernel(Dims d, I
     __syncthreads();
     if (kp != 0) return;
     for (int q = 1; q < ks; ++q) {
-      const f32x4_t *other = reinterpret_cast<const f32x4_t *>(lds + (wave + q) * kFp4WaveLds);
+      const f32x4_t *other = reinterpret_cast<const f32x4_t *>(lds + (wave + q) * kMxWaveLds);
 #pragma unroll
       for (int j = 0; j < 2; ++j) acc[j] += other[j * kWave + lane];
     }
@@ -527,18 +583,18 @@ static hipError_t sm_launch(const Dims &d, const Inputs &in, const Work &w, hipS
   return hipGetLastError();
 }
 
-// MXFP4 launch: the item count, K split and grid of sm_launch.
-template <int MODE>
-static hipError_t sm_fp4_launch(const Dims &d, const Inputs &in, const Work &w, hipStream_t s) {
+// MX launch: the item count, K split and grid of sm_launch.
+template <int MODE, int FMT>
+static hipError_t sm_mx_launch(const Dims &d, const Inputs &in, const Work &w, hipStream_t s) {
   constexpr int CW = MODE == kSmGateUp ? 16 : 32;
-  auto kern = sm_fp4_kernel<MODE>;
+  auto kern = sm_mx_kernel<MODE, FMT>;
   static int blocks_per_cu = 0;
   if (blocks_per_cu == 0) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kFp4Lds);
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kMxLds);
     if (e != hipSuccess) return e;
     int nb = 0;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kern, kSmBlockWaves * kWave, kFp4Lds);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kern, kSmBlockWaves * kWave, kMxLds);
     if (e != hipSuccess) return e;
     if (nb < 1) return hipErrorInvalidConfiguration;
     blocks_per_cu = nb;
@@ -550,17 +606,17 @@ static hipError_t sm_fp4_launch(const Dims &d, const Inputs &in, const Work &w, 
   const long items = static_cast<long>(slots) * ipr + ips;
   const long cap = static_cast<long>(sm_cus()) * blocks_per_cu * kSmBlockWaves;
   const int kmin = MODE == kSmGateUp ? d.H : (d.Is > 0 && d.Is < d.I ? d.Is : d.I);
-  const int nst = kmin / kFp4StageK;
+  const int nst = kmin / MxCfg<FMT>::KPS;
   const int ks = sm_pick_ks(items, cap, nst);
   const long per_block = kSmBlockWaves / ks;
   const long grid = (items + per_block - 1) / per_block;
-  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(kSmBlockWaves * kWave), kFp4Lds, s,
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(kSmBlockWaves * kWave), kMxLds, s,
                      d, in, w, ks);
   return hipGetLastError();
 }
 
-// H, I multiples of 32 and m <= 16 are checked by the caller (MXFP4: H, I and
-// I_s multiples of 256, one stage).  A stage moves
+// H, I multiples of 32 and m <= 16 are checked by the caller (MX formats: H,
+// I and I_s multiples of one stage's K, 256 for FP4 and 128 for FP8).  A stage moves
 // RUN contiguous bytes of each row: 256 when K is a multiple of 128 (longer
 // runs stream faster), else 128 or 64.
 template <int MODE, int NBLK>
@@ -572,13 +628,15 @@ static hipError_t sm_dispatch(const Dims &d, const Inputs &in, const Work &w, hi
 
 hipError_t launch_small_m_gateup(const Dims &d, const Inputs &in, const Work &w,
                                  hipStream_t s) {
-  if (d.wdt == kMXFP4) return sm_fp4_launch<kSmGateUp>(d, in, w, s);
+  if (d.wdt == kMXFP4) return sm_mx_launch<kSmGateUp, kMXFP4>(d, in, w, s);
+  if (d.wdt == kMXFP8) return sm_mx_launch<kSmGateUp, kMXFP8>(d, in, w, s);
   return sm_dispatch<kSmGateUp, 2>(d, in, w, s, d.H);   // 16 h columns per item
 }
 
 hipError_t launch_small_m_down(const Dims &d, const Inputs &in, const Work &w,
                                hipStream_t s) {
-  if (d.wdt == kMXFP4) return sm_fp4_launch<kSmDown>(d, in, w, s);
+  if (d.wdt == kMXFP4) return sm_mx_launch<kSmDown, kMXFP4>(d, in, w, s);
+  if (d.wdt == kMXFP8) return sm_mx_launch<kSmDown, kMXFP8>(d, in, w, s);
   // K is I for routed slots and I_s for the shared one: stages fit both
   const int kg = d.Is > 0 ? (d.I % 128 == 0 && d.Is % 128 == 0 ? 128 : (d.I % 64 == 0 && d.Is % 64 == 0 ? 64 : 32))
                           : d.I;

@@ -44,10 +44,10 @@ from tests.conftest import oracle_inputs, to_np
 
 NEAR_TIE = 1e-5
 W_TOL = 1e-5
-# MXFP4 weights are exact in bf16 and multiplied on the bf16 MFMA: the bf16
+# MXFP4 / MXFP8 weights are exact in bf16 and multiplied on the bf16 MFMA: the bf16
 # bounds apply
-OUT_TOL = {"f32": 1e-4, "bf16": 2e-2, "fp8": 4e-2, "mxfp4": 2e-2}
-L2_TOL = {"f32": 1e-5, "bf16": 5e-3, "fp8": 8e-3, "mxfp4": 5e-3}
+OUT_TOL = {"f32": 1e-4, "bf16": 2e-2, "fp8": 4e-2, "mxfp4": 2e-2, "mxfp8": 2e-2}
+L2_TOL = {"f32": 1e-5, "bf16": 5e-3, "fp8": 8e-3, "mxfp4": 5e-3, "mxfp8": 5e-3}
 H_SCALE_TOL = 1e-3     # relative, GPU h scale vs the oracle's amax / 448
 H_SLACK = 1e-3         # of the code range (448), beyond one e4m3 step
 H_FLIP_FRAC = 1e-2     # codes allowed to differ from the nearest one

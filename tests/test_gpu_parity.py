@@ -251,6 +251,17 @@ def test_mxfp4_shared_gated_small(m):
     run_case(MX_SMALL, path="small_m", m=m)
 
 
+@pytest.mark.parametrize("m", [1, 4, 16])
+def test_decode_mxfp8(m):
+    run_case(synth.WORKLOADS["decode_mxfp8"], path="small_m", m=m)
+
+
+@pytest.mark.parametrize("m", [1, 7, 16])
+def test_mxfp8_shared_gated_small(m):
+    run_case(MX_SMALL.replace(name="mx8_small", dtype="mxfp8", inter=384, shared_inter=128),
+             path="small_m", m=m)
+
+
 def test_mxfp4_k_equals_E():
     wl = synth.Workload("mx_keqE", m=9, hidden=256, experts=4, topk=4, inter=512,
                         shared_inter=0, dtype="mxfp4", gating="softmax",
