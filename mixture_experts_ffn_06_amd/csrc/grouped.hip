@@ -102,7 +102,14 @@ struct GroupedArgs {
   Work w;
   int ntile_routed;   // N tiles of a routed expert
   int ntile_shared;   // N tiles of the shared expert
-  int interleave;     // 1: shared-expert units spread evenly among the routed ones (bf16)
+  int order;          // kOrderGroups, kOrderInterleaveShared or kOrderSharedFirst (bf16)
+};
+
+// Order in which the persistent blocks take the units.
+enum : int {
+  kOrderGroups = 0,            // routed experts in order, then the shared expert
+  kOrderInterleaveShared = 1,  // shared-expert units spread evenly among the routed ones
+  kOrderSharedFirst = 2        // shared-expert units first (longest first when I_s > I)
 };
 
 template <int DT, int MODE, int NB, int WN, int WM, int MBW, int DEPTH, int STAGE_K>
@@ -172,19 +179,25 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void grouped_kernel(GroupedArgs a)
     // side on one L2.
     const int u = r * P + xcd * per_xcd + slot;
     if (u >= total) continue;
-    // With interleave, position u runs unit uu: the S shared-expert units
-    // (last in group order) are spread evenly over the positions, so their
-    // cache-served weight reads share each round with the HBM-bound routed
-    // units instead of forming a last round of their own.  Positions p where
-    // floor((p+1) S / total) steps up take shared unit floor(p S / total);
-    // the others take routed unit p - floor(p S / total).
+    // Position u runs unit uu.  The S shared-expert units are last in group
+    // order.  kOrderInterleaveShared spreads them evenly over the positions,
+    // so their cache-served weight reads share each round with the HBM-bound
+    // routed units instead of forming a last round of their own: positions p
+    // where floor((p+1) S / total) steps up take shared unit
+    // floor(p S / total), the others routed unit p - floor(p S / total).
+    // kOrderSharedFirst runs them first, so that longer units (K = I_s > I in
+    // the down product) do not form the tail.  (fp8 kernels: compiled out.)
     int uu = u;
-    if (DT == kBF16 && a.interleave) {   // (fp8 kernels: compiled out)
+    if (DT == kBF16 && a.order != kOrderGroups) {
       const int S = d.Is > 0 ? total - uoff[d.E] : 0;
       if (S > 0 && S < total) {
-        const int before = static_cast<int>(static_cast<long>(u) * S / total);
-        const int next = static_cast<int>(static_cast<long>(u + 1) * S / total);
-        uu = next > before ? (total - S) + before : u - before;
+        if (a.order == kOrderSharedFirst) {
+          uu = u < S ? (total - S) + u : u - S;
+        } else {
+          const int before = static_cast<int>(static_cast<long>(u) * S / total);
+          const int next = static_cast<int>(static_cast<long>(u + 1) * S / total);
+          uu = next > before ? (total - S) + before : u - before;
+        }
       }
     }
     // ---- decode the unit (all values block-uniform) ----
@@ -674,14 +687,14 @@ static bool big_tiles(const Dims &d) { return d.te > 96 * d.E; }
 
 hipError_t launch_grouped_gateup(const Dims &d, const Inputs &in,
                                  const Work &w, hipStream_t s) {
-  GroupedArgs ga{d, in, w, 0, 0, 0};
+  GroupedArgs ga{d, in, w, 0, 0, kOrderGroups};
   if (d.wdt == kBF16) {
     // 256-row tiles (64 h columns, 2 x 4 waves) when experts average more
     // than 96 rows, else 96-row tiles (128 h columns, 4 column waves), with
     // the shared-expert units interleaved (prefill gate/up 243 -> 212 us;
     // the same order made the down and the fp8 gate/up slower)
     if (big_tiles(d)) return launch_one<kBF16, kGateUp, 4, 2, 4, 4, 4, 64>(ga, s);
-    ga.interleave = 1;
+    ga.order = kOrderInterleaveShared;
     return launch_one<kBF16, kGateUp, 4, 4, 1, 6, 4, 64>(ga, s);
   }
   // fp8: 128 h columns = one h scale group (4 column waves x 2 gate + 2 up
@@ -692,9 +705,11 @@ hipError_t launch_grouped_gateup(const Dims &d, const Inputs &in,
 
 hipError_t launch_grouped_down(const Dims &d, const Inputs &in, const Work &w,
                                hipStream_t s) {
-  const GroupedArgs ga{d, in, w, 0, 0, 0};
+  GroupedArgs ga{d, in, w, 0, 0, kOrderGroups};
   if (d.wdt == kBF16) {
     if (big_tiles(d)) return launch_one<kBF16, kDown, 4, 4, 2, 4, 3, 64>(ga, s);   // 128 rows x 256 columns, 8 waves
+    // 96-row tiles, shared-expert units first (prefill down 143 -> 136 us)
+    ga.order = kOrderSharedFirst;
     return launch_one<kBF16, kDown, 4, 4, 1, 6, 4, 64>(ga, s);
   }
   // 192 (128) rows x 256 columns, 8 waves
