@@ -277,6 +277,11 @@ def main():
     stage_ms /= args.steps
 
     D = int(torch.unique(idx).numel())
+    per_expert = torch.bincount(idx.flatten().long(), minlength=wl.experts)
+    routing = {"active_experts": D,
+               "empty_experts": int((per_expert == 0).sum()),
+               "max_expert_share": float(per_expert.max()) / float(idx.numel()),
+               "max_expert_rows": int(per_expert.max())}
     cnt = layer_counts(wl, m, D)
     gb = cnt["bytes"] / (ms_per_step * 1e-3) / 1e9
     tf = cnt["flops"] / (ms_per_step * 1e-3) / 1e12
@@ -297,7 +302,7 @@ def main():
         "config": {"workload": f"{wl.name}: m={m} H={wl.hidden} E={wl.experts} "
                                f"k={wl.topk} I={wl.inter} I_s={wl.shared_inter} "
                                f"{wl.dtype} {wl.gating}",
-                   "path": path, "active_experts": D, "weight_copies": copies,
+                   "path": path, "active_experts": D, "routing": routing, "weight_copies": copies,
                    "launch": args.launch},
         "layer": {"gbps": gb, "hbm_frac": gb / HBM_PEAK_GBPS, "tflops": tf,
                   "mfma_frac": tf / MFMA_PEAK_TFLOPS[wl.dtype],
