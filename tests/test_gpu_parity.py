@@ -148,6 +148,18 @@ def test_sigmoid_bias_bf16(path):
     run_case(SIGMOID_BF16, path=path, m=16 if path == "small_m" else None)
 
 
+MAX_EK = synth.Workload("max_E_k", m=20, hidden=256, experts=1024, topk=32, inter=128,
+                        shared_inter=64, dtype="bf16", gating="sigmoid", routed_scale=2.5,
+                        seed=46, zipf_alpha=0.05)
+
+
+@pytest.mark.parametrize("path", ["grouped", "small_m", "simple"])
+def test_max_experts_and_topk(path):
+    """E = 1024 and k = 32, the plan's limits: 16 experts per lane in the
+    top-k, the fused routing kernel of small batches near its LDS bound."""
+    run_case(MAX_EK, path=path, m=16 if path == "small_m" else None)
+
+
 def test_k_equals_E():
     wl = synth.Workload("k_eq_E", m=40, hidden=128, experts=4, topk=4, inter=64,
                         shared_inter=0, dtype="bf16", gating="softmax",
