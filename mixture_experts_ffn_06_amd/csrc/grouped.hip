@@ -34,6 +34,7 @@
 //    row scale * weight block scale) is added to the fp32 accumulator.
 #include "common.h"
 #include "kernels.h"
+#include "launch.h"
 #include "lds.h"
 
 namespace moe {
@@ -646,37 +647,18 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void grouped_kernel(GroupedArgs a)
   }
 }
 
-static int cu_count() {
-  static int cus = 0;
-  if (cus == 0) {
-    int dev = 0;
-    (void)hipGetDevice(&dev);
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-      cus = 256;
-  }
-  return cus;
-}
-
 template <int DT, int MODE, int NB, int WN, int WM, int MBW, int DEPTH, int STAGE_K>
 static hipError_t launch_one(GroupedArgs ga, hipStream_t s) {
   using C = GCfg<DT, MODE, NB, WN, WM, MBW, DEPTH, STAGE_K>;
   auto kern = grouped_kernel<DT, MODE, NB, WN, WM, MBW, DEPTH, STAGE_K>;
-  static int blocks_per_cu = 0;
-  if (blocks_per_cu == 0) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
-    if (e != hipSuccess) return e;
-    int nb = 0;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kern, C::THREADS, C::LDS_BYTES);
-    if (e != hipSuccess) return e;
-    if (nb < 1) return hipErrorInvalidConfiguration;
-    blocks_per_cu = nb;
-  }
+  static const KernelSetup su = kernel_setup(reinterpret_cast<const void *>(kern), C::THREADS, C::LDS_BYTES);
+  if (su.err != hipSuccess) return su.err;
+  const int blocks_per_cu = su.blocks_per_cu;
   const int ncols_r = MODE == kGateUp ? ga.d.I : ga.d.H;
   const int ncols_s = MODE == kGateUp ? ga.d.Is : ga.d.H;
   ga.ntile_routed = (ncols_r + C::NCOLS - 1) / C::NCOLS;
   ga.ntile_shared = (ncols_s + C::NCOLS - 1) / C::NCOLS;
-  const int grid = (cu_count() * blocks_per_cu + 7) / 8 * 8;
+  const int grid = (device_cus() * blocks_per_cu + 7) / 8 * 8;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(C::THREADS), C::LDS_BYTES, s, ga);
   return hipGetLastError();
 }

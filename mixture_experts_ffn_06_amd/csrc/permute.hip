@@ -18,6 +18,7 @@
 // Everything stays inside one block: no grid-wide hand-off, no atomics.
 #include "common.h"
 #include "kernels.h"
+#include "launch.h"
 #include "routing.h"
 
 namespace moe {
@@ -88,16 +89,15 @@ __global__ __launch_bounds__(kPermThreads) void permute_scatter_kernel(
 hipError_t launch_permute(const Dims &d, const int *topk_idx, const Work &w,
                           hipStream_t s) {
   const size_t lds = static_cast<size_t>(kPermWaves) * d.E * sizeof(int);
-  static bool attr = false;
-  if (!attr) {
+  static const hipError_t su = [] {
     for (const void *k : {reinterpret_cast<const void *>(permute_kernel),
                           reinterpret_cast<const void *>(permute_scatter_kernel)}) {
-      hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                         kPermWaves * 1024 * static_cast<int>(sizeof(int)));
+      const hipError_t e = lds_setup(k, kPermWaves * 1024 * static_cast<int>(sizeof(int)));
       if (e != hipSuccess) return e;
     }
-    attr = true;
-  }
+    return hipSuccess;
+  }();
+  if (su != hipSuccess) return su;
   const int nblk = permute_chunks(d.te), chunk = perm_chunk(d.te);
   if (nblk == 0) {
     hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(kPermThreads), lds, s, topk_idx,

@@ -12,6 +12,7 @@
 // routed scaling factor.
 #include "common.h"
 #include "kernels.h"
+#include "launch.h"
 #include "routing.h"
 
 namespace moe {
@@ -253,14 +254,9 @@ hipError_t launch_topk_permute(const Dims &d, const Inputs &in, const Work &w, i
   const int ks = router_splits(d);
 #define MOE_FUSED_CASE(N)                                                                      \
   if (epl <= N) {                                                                              \
-    static bool attr = false;                                                                  \
-    if (!attr) {                                                                               \
-      const hipError_t e = hipFuncSetAttribute(                                                \
-          reinterpret_cast<const void *>(topk_permute_kernel<N>),                              \
-          hipFuncAttributeMaxDynamicSharedMemorySize, 144 << 10);                              \
-      if (e != hipSuccess) return e;                                                           \
-      attr = true;                                                                             \
-    }                                                                                          \
+    static const hipError_t su =                                                               \
+        lds_setup(reinterpret_cast<const void *>(topk_permute_kernel<N>), 144 << 10);         \
+    if (su != hipSuccess) return su;                                                           \
     hipLaunchKernelGGL(topk_permute_kernel<N>, dim3(1), dim3(kFusedThreads), lds, s, d, in, w, \
                        ks, topk_idx, topk_w);                                                  \
     return hipGetLastError();                                                                  \

@@ -24,6 +24,7 @@
 // grid is sized so that every item is resident at once.
 #include "common.h"
 #include "kernels.h"
+#include "launch.h"
 #include "lds.h"
 
 namespace moe {
@@ -525,17 +526,6 @@ __global__ __launch_bounds__(kSmBlockWaves * kWave) void sm_mx_kernel(Dims d, In
   }
 }
 
-static int sm_cus() {
-  static int cus = 0;
-  if (cus == 0) {
-    int dev = 0;
-    (void)hipGetDevice(&dev);
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-      cus = 256;
-  }
-  return cus;
-}
-
 // Grid for the largest possible item count (the number of slots is only
 // known on the device: items past it exit at once).  KS, the waves per item
 // (each streams 1/KS of K, partial sums meet in LDS), is at least 2 whenever
@@ -555,23 +545,15 @@ static hipError_t sm_launch(const Dims &d, const Inputs &in, const Work &w, hipS
   using C = SmCfg<NBLK, RUN, DEPTH>;
   constexpr int CW = MODE == kSmGateUp ? 16 * NBLK / 2 : 16 * NBLK;
   auto kern = sm_kernel<MODE, NBLK, RUN, DEPTH>;
-  static int blocks_per_cu = 0;
-  if (blocks_per_cu == 0) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
-    if (e != hipSuccess) return e;
-    int nb = 0;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kern, kSmBlockWaves * kWave, C::LDS);
-    if (e != hipSuccess) return e;
-    if (nb < 1) return hipErrorInvalidConfiguration;
-    blocks_per_cu = nb;
-  }
+  static const KernelSetup su = kernel_setup(reinterpret_cast<const void *>(kern), kSmBlockWaves * kWave, C::LDS);
+  if (su.err != hipSuccess) return su.err;
+  const int blocks_per_cu = su.blocks_per_cu;
   const int slots = d.te < d.E ? d.te : d.E;
   const int ncol_r = MODE == kSmGateUp ? d.I : d.H;
   const int ipr = (ncol_r + CW - 1) / CW;
   const int ips = d.Is > 0 ? ((MODE == kSmGateUp ? d.Is : d.H) + CW - 1) / CW : 0;
   const long items = static_cast<long>(slots) * ipr + ips;
-  const long cap = static_cast<long>(sm_cus()) * blocks_per_cu * kSmBlockWaves;
+  const long cap = static_cast<long>(device_cus()) * blocks_per_cu * kSmBlockWaves;
   // K stages of the shortest item (the shared expert's down K is I_s)
   const int kmin = MODE == kSmGateUp ? d.H : (d.Is > 0 && d.Is < d.I ? d.Is : d.I);
   const int nst = kmin * 2 / RUN;
@@ -588,23 +570,15 @@ template <int MODE, int FMT>
 static hipError_t sm_mx_launch(const Dims &d, const Inputs &in, const Work &w, hipStream_t s) {
   constexpr int CW = MODE == kSmGateUp ? 16 : 32;
   auto kern = sm_mx_kernel<MODE, FMT>;
-  static int blocks_per_cu = 0;
-  if (blocks_per_cu == 0) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kMxLds);
-    if (e != hipSuccess) return e;
-    int nb = 0;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kern, kSmBlockWaves * kWave, kMxLds);
-    if (e != hipSuccess) return e;
-    if (nb < 1) return hipErrorInvalidConfiguration;
-    blocks_per_cu = nb;
-  }
+  static const KernelSetup su = kernel_setup(reinterpret_cast<const void *>(kern), kSmBlockWaves * kWave, kMxLds);
+  if (su.err != hipSuccess) return su.err;
+  const int blocks_per_cu = su.blocks_per_cu;
   const int slots = d.te < d.E ? d.te : d.E;
   const int ncol_r = MODE == kSmGateUp ? d.I : d.H;
   const int ipr = (ncol_r + CW - 1) / CW;
   const int ips = d.Is > 0 ? ((MODE == kSmGateUp ? d.Is : d.H) + CW - 1) / CW : 0;
   const long items = static_cast<long>(slots) * ipr + ips;
-  const long cap = static_cast<long>(sm_cus()) * blocks_per_cu * kSmBlockWaves;
+  const long cap = static_cast<long>(device_cus()) * blocks_per_cu * kSmBlockWaves;
   const int kmin = MODE == kSmGateUp ? d.H : (d.Is > 0 && d.Is < d.I ? d.Is : d.I);
   const int nst = kmin / MxCfg<FMT>::KPS;
   const int ks = sm_pick_ks(items, cap, nst);
