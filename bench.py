@@ -291,8 +291,10 @@ def main():
     # the kernel's bound: whichever of its bytes and flops takes longer at peak
     mfma_peak = MFMA_PEAK_TFLOPS[wl.dtype]
     mfma_bound = cnt[dom]["flops"] / (mfma_peak * 1e12) > cnt[dom]["bytes"] / (HBM_PEAK_GBPS * 1e9)
-    kernel_names = {"small_m": "sm_kernel<gateup>", "grouped": "grouped_kernel<gateup>",
-                    "simple": "simple_gateup_kernel"}
+    kernel_names = {"small_m": ("sm_mx_kernel<gateup, MXFP4>" if wl.dtype == "mxfp4" else
+                                "sm_mx_kernel<gateup, MXFP8>" if wl.dtype == "mxfp8" else
+                                "sm_kernel<gateup>"),
+                    "grouped": "grouped_kernel<gateup>", "simple": "simple_gateup_kernel"}
     path = layers[0].plan.path_for(m)
     result = {
         "metric": METRIC, "value": m / (ms_per_step * 1e-3), "unit": "tokens/s",
