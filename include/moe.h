@@ -78,7 +78,7 @@ typedef enum {
 } moe_gating_t;
 
 /* Expert-path choice.  AUTO: fp32 weights -> SIMPLE; m <= 16 -> SMALL_M;
- * otherwise GROUPED.  The others force a path (for testing; every path
+ * otherwise GROUPED (MXFP4 / MXFP8 weights: SIMPLE).  The others force a path (for testing; every path
  * computes the same layer). */
 typedef enum {
   MOE_PATH_AUTO = 0,
@@ -171,9 +171,9 @@ typedef struct {
  * Errors: MOE_ERR_INVALID_ARG for non-positive sizes, topk outside
  * [1, min(E,32)], E > 1024, unknown enums; MOE_ERR_UNSUPPORTED for fp8 with
  * H, I or I_s not multiples of 128, bf16/fp8 with H, I or I_s not multiples
- * of 32, MXFP4 (MXFP8) with H, I or I_s not multiples of 256 (128), with
- * max_tokens above 16 or with a path other than AUTO / SMALL_M (the MX
- * formats run on the m <= 16 weight-streaming path only), SMALL_M forced with fp8/fp32 weights, or
+ * of 32, MXFP4 (MXFP8) with H, I or I_s not multiples of 256 (128) or the
+ * GROUPED path forced (the MX formats run on the weight-streaming path up to
+ * 16 tokens and on the VALU path above), SMALL_M forced with fp8/fp32 weights, or
  * sizes whose operands
  * reach 2 GiB (max_tokens * topk * max(H, I, I_s) elements, or one expert's
  * 2 * max(I, I_s) * H weight elements, at 2 bytes per bf16/fp8 element and 4

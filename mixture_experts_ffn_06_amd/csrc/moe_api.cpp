@@ -43,6 +43,8 @@ int resolve_path(const moe_config_t &c, int m) {
   if ((c.weight_dtype == MOE_BF16 || c.weight_dtype == MOE_MXFP4 || c.weight_dtype == MOE_MXFP8) &&
       m <= 16)
     return MOE_PATH_SMALL_M;
+  // MX weights above 16 tokens: the VALU path (no grouped MX GEMM)
+  if (c.weight_dtype == MOE_MXFP4 || c.weight_dtype == MOE_MXFP8) return MOE_PATH_SIMPLE;
   return MOE_PATH_GROUPED;
 }
 
@@ -138,11 +140,11 @@ int check_cfg(const moe_config_t &c) {
     return MOE_ERR_UNSUPPORTED;
   const bool mx = c.weight_dtype == MOE_MXFP4 || c.weight_dtype == MOE_MXFP8;
   if (c.path == MOE_PATH_SMALL_M && c.weight_dtype != MOE_BF16 && !mx) return MOE_ERR_UNSUPPORTED;
-  // the MX formats run on the weight-streaming path only: one stage is 256
-  // (FP4) or 128 (FP8) K elements, batches of at most 16 tokens
+  // the MX formats run on the weight-streaming path (one stage is 256 (FP4)
+  // or 128 (FP8) K elements) up to 16 tokens and on the VALU path above;
+  // there is no grouped MX GEMM
   const int mx_k = c.weight_dtype == MOE_MXFP4 ? 256 : 128;
-  if (mx && (c.hidden % mx_k || c.inter % mx_k || c.shared_inter % mx_k || c.max_tokens > 16 ||
-             (c.path != MOE_PATH_AUTO && c.path != MOE_PATH_SMALL_M)))
+  if (mx && (c.hidden % mx_k || c.inter % mx_k || c.shared_inter % mx_k || c.path == MOE_PATH_GROUPED))
     return MOE_ERR_UNSUPPORTED;
   // the expert kernels address each operand (token rows, the sorted h / y
   // rows, one expert's weight matrix) with 32-bit byte offsets

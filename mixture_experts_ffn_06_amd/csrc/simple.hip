@@ -8,6 +8,11 @@
 // (the two-level fp32 block-scale accumulation of forward_prefill.rs, page 3,
 // notes on the ported fp8 grouped GEMM).
 //
+// MX weights (OCP MXFP4 / MXFP8, E8M0 scale per 32 elements along K) are
+// decoded element by element here (code value times 2^(e - 127), exact in
+// fp32); their x, h and y are bf16 as on the bf16 path.  This is the MX
+// formats' path for batches of more than 16 tokens.
+//
 // Rows are in sorted order: routed rows s in [0, te) belong to the expert e
 // with offsets[e] <= s < offsets[e+1] and to token sorted_pair[s] / k; the
 // shared expert's rows follow as s = te + t.
@@ -23,6 +28,27 @@ __device__ __forceinline__ int expert_of_row(const int *offsets, int E, int s) {
     if (offsets[mid] <= s) lo = mid; else hi = mid - 1;
   }
   return lo;
+}
+
+constexpr bool is_mx(int dt) { return dt == kMXFP4 || dt == kMXFP8; }
+
+// Weight element k of row `row` of an MX matrix with K columns: packed
+// codes (two e2m1 per byte, even element in the low nibble, or one e4m3 per
+// byte) and one E8M0 scale byte per 32 elements of a row.
+template <int DT>
+__device__ __forceinline__ float mx_weight(const void *w, const uint8_t *sc, size_t row, int K, int k) {
+  const uint8_t *b = static_cast<const uint8_t *>(w);
+  float v;
+  if constexpr (DT == kMXFP4) {
+    const uint8_t byte = b[row * (K / 2) + k / 2];
+    const uint32_t c = (k & 1) ? (byte >> 4) : (byte & 0xfu);
+    const uint32_t e = (c >> 1) & 3u, mt = c & 1u;
+    const float mag = e == 0 ? 0.5f * static_cast<float>(mt) : ldexpf(1.0f + 0.5f * static_cast<float>(mt), static_cast<int>(e) - 1);
+    v = (c & 8u) ? -mag : mag;
+  } else {
+    v = fp8_to_f32(b[row * K + k]);
+  }
+  return ldexpf(v, static_cast<int>(sc[row * (K / 32) + k / 32]) - 127);
 }
 
 struct RowInfo {
@@ -41,16 +67,24 @@ template <int DT>
 __device__ __forceinline__ RowInfo row_info(const Dims &d, const Inputs &in,
                                             const Work &w, int s) {
   RowInfo r;
-  constexpr int B = StorageBytes<DT>::value;
+  // bytes per weight element (MXFP4: half a byte, counted per expert below)
+  constexpr int B = is_mx(DT) ? 2 : StorageBytes<DT>::value;   // h element bytes
   const int yb = DT == kF32 ? 4 : 2;
   if (s < d.te) {
     const int e = expert_of_row(w.offsets, d.E, s);
     r.t = w.sorted_pair[s] / d.k;
     r.inter = d.I;
-    r.w13 = static_cast<const char *>(in.w13) + static_cast<size_t>(e) * 2 * d.I * d.H * B;
-    r.w2 = static_cast<const char *>(in.w2) + static_cast<size_t>(e) * d.H * d.I * B;
-    r.s13 = DT == kFP8 ? in.w13_scale + static_cast<size_t>(e) * (2 * d.I / kQBlock) * (d.H / kQBlock) : nullptr;
-    r.s2 = DT == kFP8 ? in.w2_scale + static_cast<size_t>(e) * (d.H / kQBlock) * (d.I / kQBlock) : nullptr;
+    const size_t ew = static_cast<size_t>(2) * d.I * d.H;   // w13 (and w2) elements per expert
+    const size_t ewb = DT == kMXFP4 ? ew / 2 : (is_mx(DT) ? ew : ew * StorageBytes<DT>::value);
+    r.w13 = static_cast<const char *>(in.w13) + static_cast<size_t>(e) * ewb;
+    r.w2 = static_cast<const char *>(in.w2) + static_cast<size_t>(e) * (ewb / 2);
+    if constexpr (is_mx(DT)) {   // E8M0 scale bytes, one per 32 elements
+      r.s13 = reinterpret_cast<const float *>(reinterpret_cast<const uint8_t *>(in.w13_scale) + static_cast<size_t>(e) * (ew / 32));
+      r.s2 = reinterpret_cast<const float *>(reinterpret_cast<const uint8_t *>(in.w2_scale) + static_cast<size_t>(e) * (ew / 64));
+    } else {
+      r.s13 = DT == kFP8 ? in.w13_scale + static_cast<size_t>(e) * (2 * d.I / kQBlock) * (d.H / kQBlock) : nullptr;
+      r.s2 = DT == kFP8 ? in.w2_scale + static_cast<size_t>(e) * (d.H / kQBlock) * (d.I / kQBlock) : nullptr;
+    }
     r.h = static_cast<char *>(w.h) + static_cast<size_t>(s) * d.I * B;
     r.hs = DT == kFP8 ? w.h_scale + static_cast<size_t>(s) * (d.I / kQBlock) : nullptr;
     r.y = static_cast<char *>(w.y) + static_cast<size_t>(s) * d.H * yb;
@@ -81,7 +115,14 @@ __global__ __launch_bounds__(128) void simple_gateup_kernel(Dims d, Inputs in, W
   float g = 0.f, u = 0.f;
   if (valid) {
     const size_t rg = static_cast<size_t>(c) * H, ru = static_cast<size_t>(r.inter + c) * H;
-    if constexpr (DT == kFP8) {
+    if constexpr (is_mx(DT)) {
+      const uint8_t *sc = reinterpret_cast<const uint8_t *>(r.s13);
+      for (int h = 0; h < H; ++h) {
+        const float a = load_as_f32<kBF16>(in.x, static_cast<size_t>(r.t) * H + h);
+        g = fmaf(a, mx_weight<DT>(r.w13, sc, c, H, h), g);
+        u = fmaf(a, mx_weight<DT>(r.w13, sc, r.inter + c, H, h), u);
+      }
+    } else if constexpr (DT == kFP8) {
       const uint8_t *xa = w.xq + static_cast<size_t>(r.t) * H;
       const float *sa = w.sx + static_cast<size_t>(r.t) * (H / kQBlock);
       const int kb_n = H / kQBlock;
@@ -109,7 +150,7 @@ __global__ __launch_bounds__(128) void simple_gateup_kernel(Dims d, Inputs in, W
   const float hv = silu(g) * u;
   if constexpr (DT == kF32) {
     if (valid) static_cast<float *>(r.h)[c] = hv;
-  } else if constexpr (DT == kBF16) {
+  } else if constexpr (DT == kBF16 || is_mx(DT)) {
     if (valid) static_cast<uint16_t *>(r.h)[c] = f32_to_bf16(hv);
   } else {
     const float wm = wave_max(fabsf(hv));
@@ -133,7 +174,11 @@ __global__ __launch_bounds__(256) void simple_down_kernel(Dims d, Inputs in, Wor
   const int K = r.inter;
   const size_t rw = static_cast<size_t>(n) * K;
   float acc = 0.f;
-  if constexpr (DT == kFP8) {
+  if constexpr (is_mx(DT)) {
+    const uint8_t *sc = reinterpret_cast<const uint8_t *>(r.s2);
+    for (int j = 0; j < K; ++j)
+      acc = fmaf(load_as_f32<kBF16>(r.h, j), mx_weight<DT>(r.w2, sc, n, K, j), acc);
+  } else if constexpr (DT == kFP8) {
     const int kb_n = K / kQBlock;
     for (int kb = 0; kb < kb_n; ++kb) {
       float p = 0.f;
@@ -179,6 +224,8 @@ hipError_t launch_simple_gateup(const Dims &d, const Inputs &in, const Work &w,
   switch (d.wdt) {
     case kF32: return simple_gateup<kF32>(d, in, w, s);
     case kBF16: return simple_gateup<kBF16>(d, in, w, s);
+    case kMXFP4: return simple_gateup<kMXFP4>(d, in, w, s);
+    case kMXFP8: return simple_gateup<kMXFP8>(d, in, w, s);
     default: return simple_gateup<kFP8>(d, in, w, s);
   }
 }
@@ -188,6 +235,8 @@ hipError_t launch_simple_down(const Dims &d, const Inputs &in, const Work &w,
   switch (d.wdt) {
     case kF32: return simple_down<kF32>(d, in, w, s);
     case kBF16: return simple_down<kBF16>(d, in, w, s);
+    case kMXFP4: return simple_down<kMXFP4>(d, in, w, s);
+    case kMXFP8: return simple_down<kMXFP8>(d, in, w, s);
     default: return simple_down<kFP8>(d, in, w, s);
   }
 }

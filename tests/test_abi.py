@@ -46,10 +46,9 @@ def _cfg(**kw):
     # operands of 2 GiB or more (32-bit byte offsets in the expert kernels)
     (dict(hidden=8192, max_tokens=65536, topk=2), 2),
     # MXFP4: weight-streaming path only (m <= 16), K in stages of 256
-    (dict(weight_dtype="mxfp4", max_tokens=17), 2), (dict(weight_dtype="mxfp4", inter=128, max_tokens=16), 2),
-    (dict(weight_dtype="mxfp4", path="grouped", max_tokens=16), 2),
-    (dict(weight_dtype="mxfp4", path="simple", max_tokens=16), 2), (dict(weight_dtype=5), 1),
-    (dict(weight_dtype="mxfp8", max_tokens=17), 2), (dict(weight_dtype="mxfp8", inter=64, max_tokens=16), 2),
+    (dict(weight_dtype="mxfp4", inter=128, max_tokens=16), 2),
+    (dict(weight_dtype="mxfp4", path="grouped", max_tokens=16), 2), (dict(weight_dtype=5), 1),
+    (dict(weight_dtype="mxfp8", inter=64, max_tokens=16), 2),
     (dict(hidden=32768, inter=32768, max_tokens=16), 2),
 ])
 def test_plan_rejects_bad_configs(kw, status):
@@ -68,6 +67,7 @@ def test_plan_accepts_and_reports_paths_and_workspace():
     assert moe.MoePlan(**_cfg(weight_dtype="fp8")).path_for(4) == "grouped"
     assert moe.MoePlan(**_cfg(weight_dtype="mxfp4", inter=256, max_tokens=16)).path_for(16) == "small_m"
     assert moe.MoePlan(**_cfg(weight_dtype="mxfp8", inter=128, max_tokens=16)).path_for(3) == "small_m"
+    assert moe.MoePlan(**_cfg(weight_dtype="mxfp4", inter=256, max_tokens=64)).path_for(17) == "simple"
     assert lib().moe_workspace_bytes(None, 4) == 0
 
 

@@ -274,6 +274,14 @@ def test_mxfp8_shared_gated_small(m):
              path="small_m", m=m)
 
 
+@pytest.mark.parametrize("fmt", ["mxfp4", "mxfp8"])
+def test_mx_above_16_tokens_on_the_valu_path(fmt):
+    """Above 16 tokens MX weights run on the fp32 VALU path (AUTO), which
+    also serves as a cross-check of the MX decode at small sizes."""
+    wl = MX_SMALL.replace(name=f"{fmt}_valu", m=40, dtype=fmt)
+    run_case(wl, path="simple")
+
+
 def test_mxfp4_k_equals_E():
     wl = synth.Workload("mx_keqE", m=9, hidden=256, experts=4, topk=4, inter=512,
                         shared_inter=0, dtype="mxfp4", gating="softmax",
