@@ -1,0 +1,71 @@
+"""The LDS-ring kernels never touch a register an un-waited asm LDS read
+will still write.
+
+Compiles the kernels that issue inline-asm LDS reads (grouped GEMM, small-m
+weight streaming) to gfx950 assembly with the library's own flags and scans
+it; the scanner itself is checked on hand-written snippets first.
+"""
+import os
+import shutil
+import subprocess
+from concurrent.futures import ThreadPoolExecutor
+
+import pytest
+
+from mixture_experts_ffn_06_amd import build as B
+
+from tests.asm_lds_hazards import scan
+
+SAFE = """
+_Zkern:
+	;;#ASMSTART
+	ds_read_b128 v[4:7], v1 offset:0
+	;;#ASMEND
+	;;#ASMSTART
+	ds_read_b128 v[8:11], v1 offset:16
+	;;#ASMEND
+	v_add_u32_e32 v2, v3, v12
+	s_waitcnt lgkmcnt(0)
+	v_mfma_f32_16x16x32_bf16 a[0:3], v[4:7], v[8:11], a[0:3]
+	s_endpgm
+"""
+
+# a copy of an in-flight destination before the wait
+HAZARD_COPY = SAFE.replace("v_add_u32_e32 v2, v3, v12", "v_accvgpr_write_b32 a9, v6")
+# an in-flight destination reused as the next read's address
+HAZARD_ADDR = SAFE.replace("ds_read_b128 v[8:11], v1 offset:16", "ds_read_b128 v[8:11], v5 offset:16")
+# a wait for only some of the reads does not clear them
+HAZARD_PARTIAL = SAFE.replace("s_waitcnt lgkmcnt(0)", "s_waitcnt lgkmcnt(1)")
+
+
+def test_scanner_on_snippets():
+    h, n, f = scan(SAFE)
+    assert (h, n, f) == ([], 2, 1)
+    h, _, _ = scan(HAZARD_COPY)
+    assert [x[3] for x in h] == [("v", 6)]
+    h, _, _ = scan(HAZARD_ADDR)
+    assert [x[3] for x in h] == [("v", 5)]
+    h, _, _ = scan(HAZARD_PARTIAL)
+    assert {x[3] for x in h} == {("v", r) for r in range(4, 12)}
+
+
+def _asm(src: str) -> str:
+    flags = [f for f in B.FLAGS if f != "-fPIC"]
+    r = subprocess.run([B.HIPCC, *flags, "-x", "hip", "--cuda-device-only", "-S",
+                        os.path.join(B.CSRC, src), "-o", "-"],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc -S failed on {src}:\n{r.stderr}")
+    return r.stdout
+
+
+@pytest.mark.skipif(not os.path.exists(B.HIPCC) and shutil.which("hipcc") is None,
+                    reason="hipcc not installed")
+def test_ring_kernels_have_no_lds_read_hazards():
+    srcs = ["grouped.hip", "small_m.hip"]
+    with ThreadPoolExecutor(len(srcs)) as ex:
+        texts = list(ex.map(_asm, srcs))
+    for src, text in zip(srcs, texts):
+        hazards, n_reads, n_fn = scan(text)
+        assert n_fn > 0 and n_reads > 100, (src, n_fn, n_reads)
+        assert not hazards, f"{src}: {hazards[:5]}"
