@@ -248,10 +248,16 @@ __global__ __launch_bounds__(kSmBlockWaves * kWave) void sm_kernel(Dims d, Input
 // bytes of each of the item's 32 weight rows (256 K elements of FP4, 128 of
 // FP8; four 1 KB direct loads of 8 whole rows each, pieces swizzled per row)
 // plus the rows' scale bytes for those K elements (8 or 4 per row, one 4-byte
-// direct load per lane).  Lane group g = lane / 16 takes 32 contiguous bytes
-// of its row per stage -- K elements [64 g, 64 g + 64) for FP4, [32 g, 32 g +
-// 32) for FP8, eight per MFMA step -- and reads its token row to match (any
-// split of K over the lanes gives the same product when A and B share it).
+// direct load per lane).  In MFMA step i of a stage, lane group g = lane / 16
+// takes K elements [32 i + 8 g, 32 i + 8 g + 8): each token-row load then
+// covers 64 contiguous bytes of every token (the four groups side by side,
+// as in the bf16 kernel), the lane's weight bytes for the step are 4-byte
+// word g of 16-byte piece i of its row (FP4) or the 8 bytes at 8 (g % 2) in
+// piece 2 i + g / 2 (FP8), read from LDS, and all 32 K elements of a step
+// share one E8M0 scale byte of the row (any split of K over the lanes gives
+// the same product when A and B share it).  Giving each lane 32 contiguous
+// weight bytes instead made every token-row load touch 64 separate cache
+// lines, which cost about 15 % of the kernel time.
 // The weights become bf16 in registers by gfx950's scaled conversions, which
 // multiply by 2 to the power of the scale operand's exponent: with the scale
 // 2^(e - 127) built from the E8M0 byte that is exact.  The MFMA is the bf16
@@ -271,41 +277,21 @@ struct MxCfg {
   static constexpr int KPS = F4 ? 2 * kMxRun : kMxRun;   // K elements per stage
   static constexpr int SSTEPS = KPS / 32;                 // MFMA steps per stage
   static constexpr int SPR = KPS / 32;                    // scale bytes per row per stage
-  static constexpr int ABYTES = KPS / 4 * 2;              // token bytes per lane group per stage
   static_assert(FMT == kMXFP4 || FMT == kMXFP8, "MX formats");
 };
 
-// The lane's stage operands: pieces p0, p1 of its row in blocks 0 and 1 and
-// the two blocks' scale bytes of the row (FP4: 8 per row, FP8: 4), read and
-// waited for together.
-__device__ __forceinline__ void mx4_stage_reads(uint32_t p0, uint32_t p1, uint32_t ps, u32x4_t &b0,
-                                                u32x4_t &b1, u32x4_t &b2, u32x4_t &b3, u32x2_t &s0,
-                                                u32x2_t &s1) {
-  asm volatile(
-      "ds_read_b128 %0, %6\n"
-      "ds_read_b128 %1, %7\n"
-      "ds_read_b128 %2, %6 offset:%9\n"
-      "ds_read_b128 %3, %7 offset:%9\n"
-      "ds_read_b64 %4, %8\n"
-      "ds_read_b64 %5, %8 offset:%10\n"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(b0), "=&v"(b1), "=&v"(b2), "=&v"(b3), "=&v"(s0), "=&v"(s1)
-      : "v"(p0), "v"(p1), "v"(ps), "i"(16 * kMxRun), "i"(16 * 8));
+// LDS reads issued without waiting (the stage's reads are waited for
+// together; mx_tie after that wait keeps every use of a result behind it).
+template <int O>
+__device__ __forceinline__ void mx_issue_b32(uint32_t p, uint32_t &v) {
+  asm volatile("ds_read_b32 %0, %1 offset:%2" : "=v"(v) : "v"(p), "i"(O));
 }
-__device__ __forceinline__ void mx8_stage_reads(uint32_t p0, uint32_t p1, uint32_t ps, u32x4_t &b0,
-                                                u32x4_t &b1, u32x4_t &b2, u32x4_t &b3, uint32_t &s0,
-                                                uint32_t &s1) {
-  asm volatile(
-      "ds_read_b128 %0, %6\n"
-      "ds_read_b128 %1, %7\n"
-      "ds_read_b128 %2, %6 offset:%9\n"
-      "ds_read_b128 %3, %7 offset:%9\n"
-      "ds_read_b32 %4, %8\n"
-      "ds_read_b32 %5, %8 offset:%10\n"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(b0), "=&v"(b1), "=&v"(b2), "=&v"(b3), "=&v"(s0), "=&v"(s1)
-      : "v"(p0), "v"(p1), "v"(ps), "i"(16 * kMxRun), "i"(16 * 4));
+template <int O>
+__device__ __forceinline__ void mx_issue_b64(uint32_t p, u32x2_t &v) {
+  asm volatile("ds_read_b64 %0, %1 offset:%2" : "=v"(v) : "v"(p), "i"(O));
 }
+__device__ __forceinline__ void mx_tie(uint32_t &v) { asm volatile("" : "+v"(v)); }
+__device__ __forceinline__ void mx_tie(u32x2_t &v) { asm volatile("" : "+v"(v)); }
 
 // Eight e2m1 codes (one 32-bit word, the even element in the low nibble of
 // each byte) times 2^(e - 127), as bf16.
@@ -329,8 +315,10 @@ __device__ __forceinline__ bf16x8_t fp8x8_to_bf16(uint32_t lo, uint32_t hi, uint
   return bf16x8_t{q0[0], q0[1], q1[0], q1[1], q2[0], q2[1], q3[0], q3[1]};
 }
 
+// At least four waves per SIMD (128 registers): the LDS of four blocks fits
+// a CU, and without the bound the FP4 kernels took 163 registers (three).
 template <int MODE, int FMT>
-__global__ __launch_bounds__(kSmBlockWaves * kWave) void sm_mx_kernel(Dims d, Inputs in, Work w, int ks) {
+__global__ __launch_bounds__(kSmBlockWaves * kWave, 4) void sm_mx_kernel(Dims d, Inputs in, Work w, int ks) {
   using C = MxCfg<FMT>;
   constexpr int CW = MODE == kSmGateUp ? 16 : 32;   // output columns per item
   extern __shared__ __align__(1024) uint8_t lds[];
@@ -391,7 +379,7 @@ __global__ __launch_bounds__(kSmBlockWaves * kWave) void sm_mx_kernel(Dims d, In
       Wb = static_cast<const uint8_t *>(shared ? in.sw2 : in.w2) + eo * (C::F4 ? d.I / 2 : d.I);
       Sb = s2 + eo * (d.I / 32);
     }
-    aoff += g * C::ABYTES;   // the lane group's K elements of each stage, in bf16
+    aoff += g * 16;   // the lane group's 8 K elements of each step, in bf16
     // First weight row of block j (blocks past the last column read row 0
     // and store nothing).
     auto wrow = [&](int j) -> int {
@@ -427,44 +415,70 @@ __global__ __launch_bounds__(kSmBlockWaves * kWave) void sm_mx_kernel(Dims d, In
       dma4_to_lds(Sb + (soff + static_cast<uint32_t>(st) * C::SPR), slot + kMxWBytes);
       const uint32_t ka = static_cast<uint32_t>(st) * C::KPS * 2;
 #pragma unroll
-      for (int i = 0; i < C::SSTEPS; ++i) A[i] = *reinterpret_cast<const uint4 *>(Ab + (aoff + ka) + i * 16);
+      for (int i = 0; i < C::SSTEPS; ++i) A[i] = *reinterpret_cast<const uint4 *>(Ab + (aoff + ka) + i * 64);
     };
-    // lane reads logical pieces 2 g, 2 g + 1 of row r in both blocks and the
-    // row's scale bytes for its K elements
-    const uint32_t pp0 = static_cast<uint32_t>(r * kMxRun + sm_swz<kMxRun>(2 * g, r) * 16);
-    const uint32_t pp1 = static_cast<uint32_t>(r * kMxRun + sm_swz<kMxRun>(2 * g + 1, r) * 16);
+    // the lane's weight bytes of step i: FP4 word g of logical piece i of row
+    // r, FP8 the 8 bytes at 8 (g % 2) of logical piece 2 i + g / 2 (block 1
+    // is 16 rows further on); its scale bytes: the row's SPR bytes
+    uint32_t boff[C::SSTEPS];
+#pragma unroll
+    for (int i = 0; i < C::SSTEPS; ++i)
+      boff[i] = C::F4 ? static_cast<uint32_t>(r * kMxRun + sm_swz<kMxRun>(i, r) * 16 + 4 * g)
+                      : static_cast<uint32_t>(r * kMxRun + sm_swz<kMxRun>(2 * i + g / 2, r) * 16 + 8 * (g % 2));
+    const uint32_t srd = static_cast<uint32_t>(kMxWBytes + r * C::SPR);
     auto compute = [&](int sl, const uint4 (&A)[C::SSTEPS]) {
-      const uint8_t *slot = ring + sl * kMxStage;
-      const uint32_t base = lds_off(slot);
-      u32x4_t b0, b1, b2, b3;
+      const uint32_t base = lds_off(ring + sl * kMxStage);
+      constexpr int B1 = 16 * kMxRun;   // block 1
       if constexpr (C::F4) {
-        // scale bytes 2 g (steps 0-3) and 2 g + 1 (steps 4-7) of the row's 8
+        uint32_t w0[8], w1[8];
         u32x2_t q0, q1;
-        mx4_stage_reads(base + pp0, base + pp1, base + kMxWBytes + r * 8, b0, b1, b2, b3, q0, q1);
-        const int sh = (2 * g % 4) * 8;
-        const uint32_t sw0 = g < 2 ? q0.x : q0.y, sw1 = g < 2 ? q1.x : q1.y;
-        const uint32_t e0[2] = {(sw0 >> sh) & 0xffu, (sw0 >> (sh + 8)) & 0xffu};
-        const uint32_t e1[2] = {(sw1 >> sh) & 0xffu, (sw1 >> (sh + 8)) & 0xffu};
-        const uint32_t w0[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
-        const uint32_t w1[8] = {b2.x, b2.y, b2.z, b2.w, b3.x, b3.y, b3.z, b3.w};
+        static_for<0, 8>([&](auto ic) {
+          constexpr int i = decltype(ic)::value;
+          mx_issue_b32<0>(base + boff[i], w0[i]);
+          mx_issue_b32<B1>(base + boff[i], w1[i]);
+        });
+        mx_issue_b64<0>(base + srd, q0);
+        mx_issue_b64<16 * 8>(base + srd, q1);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        static_for<0, 8>([&](auto ic) {
+          mx_tie(w0[decltype(ic)::value]);
+          mx_tie(w1[decltype(ic)::value]);
+        });
+        mx_tie(q0);
+        mx_tie(q1);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
+          // scale byte i of the row's 8 covers step i
+          const uint32_t e0 = ((i < 4 ? q0.x : q0.y) >> (8 * (i % 4))) & 0xffu;
+          const uint32_t e1 = ((i < 4 ? q1.x : q1.y) >> (8 * (i % 4))) & 0xffu;
           const bf16x8_t a = __builtin_bit_cast(bf16x8_t, A[i]);
-          acc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, fp4x8_to_bf16(w0[i], e0[i / 4]), acc[0], 0, 0, 0);
-          acc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, fp4x8_to_bf16(w1[i], e1[i / 4]), acc[1], 0, 0, 0);
+          acc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, fp4x8_to_bf16(w0[i], e0), acc[0], 0, 0, 0);
+          acc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, fp4x8_to_bf16(w1[i], e1), acc[1], 0, 0, 0);
         }
       } else {
-        // scale byte g of the row's 4 covers all of the lane's 32 elements
+        u32x2_t w0[4], w1[4];
         uint32_t q0, q1;
-        mx8_stage_reads(base + pp0, base + pp1, base + kMxWBytes + r * 4, b0, b1, b2, b3, q0, q1);
-        const uint32_t e0 = (q0 >> (8 * g)) & 0xffu, e1 = (q1 >> (8 * g)) & 0xffu;
-        const uint32_t w0[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
-        const uint32_t w1[8] = {b2.x, b2.y, b2.z, b2.w, b3.x, b3.y, b3.z, b3.w};
+        static_for<0, 4>([&](auto ic) {
+          constexpr int i = decltype(ic)::value;
+          mx_issue_b64<0>(base + boff[i], w0[i]);
+          mx_issue_b64<B1>(base + boff[i], w1[i]);
+        });
+        mx_issue_b32<0>(base + srd, q0);
+        mx_issue_b32<16 * 4>(base + srd, q1);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        static_for<0, 4>([&](auto ic) {
+          mx_tie(w0[decltype(ic)::value]);
+          mx_tie(w1[decltype(ic)::value]);
+        });
+        mx_tie(q0);
+        mx_tie(q1);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
+          // scale byte i of the row's 4 covers step i
+          const uint32_t e0 = (q0 >> (8 * i)) & 0xffu, e1 = (q1 >> (8 * i)) & 0xffu;
           const bf16x8_t a = __builtin_bit_cast(bf16x8_t, A[i]);
-          acc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, fp8x8_to_bf16(w0[2 * i], w0[2 * i + 1], e0), acc[0], 0, 0, 0);
-          acc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, fp8x8_to_bf16(w1[2 * i], w1[2 * i + 1], e1), acc[1], 0, 0, 0);
+          acc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, fp8x8_to_bf16(w0[i].x, w0[i].y, e0), acc[0], 0, 0, 0);
+          acc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, fp8x8_to_bf16(w1[i].x, w1[i].y, e1), acc[1], 0, 0, 0);
         }
       }
     };
@@ -565,7 +579,8 @@ static hipError_t sm_launch(const Dims &d, const Inputs &in, const Work &w, hipS
   return hipGetLastError();
 }
 
-// MX launch: the item count, K split and grid of sm_launch.
+// MX launch: the item count and grid of sm_launch; the K split of sm_launch
+// except for short gate/up items.
 template <int MODE, int FMT>
 static hipError_t sm_mx_launch(const Dims &d, const Inputs &in, const Work &w, hipStream_t s) {
   constexpr int CW = MODE == kSmGateUp ? 16 : 32;
@@ -581,7 +596,10 @@ static hipError_t sm_mx_launch(const Dims &d, const Inputs &in, const Work &w, h
   const long cap = static_cast<long>(device_cus()) * blocks_per_cu * kSmBlockWaves;
   const int kmin = MODE == kSmGateUp ? d.H : (d.Is > 0 && d.Is < d.I ? d.Is : d.I);
   const int nst = kmin / MxCfg<FMT>::KPS;
-  const int ks = sm_pick_ks(items, cap, nst);
+  // gate/up items of at most 8 stages (MXFP4 at K = 2048) keep one wave:
+  // splitting them left each wave four stages (34.6-34.9 against 35.1-35.6 us
+  // at 16 tokens)
+  const int ks = MODE == kSmGateUp && nst <= 8 ? 1 : sm_pick_ks(items, cap, nst);
   const long per_block = kSmBlockWaves / ks;
   const long grid = (items + per_block - 1) / per_block;
   hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(kSmBlockWaves * kWave), kMxLds, s,
