@@ -274,6 +274,19 @@ def test_mxfp8_shared_gated_small(m):
              path="small_m", m=m)
 
 
+# Long rows (H = 4096, I = I_s = 1536): gate/up items of 16 (MXFP4) and 32
+# (MXFP8) stages split over four waves, down items of 6 and 12 stages split
+# over two and four waves; the decode-size layers keep one wave per MXFP4
+# gate/up item.
+MX_WIDE = MX_SMALL.replace(name="mx_wide", hidden=4096, experts=8, topk=2, inter=1536,
+                           shared_inter=1536)
+
+
+@pytest.mark.parametrize("fmt,m", [("mxfp4", 16), ("mxfp4", 5), ("mxfp8", 16)])
+def test_mx_long_rows_split_over_waves(fmt, m):
+    run_case(MX_WIDE.replace(name=f"{fmt}_wide", dtype=fmt), path="small_m", m=m)
+
+
 @pytest.mark.parametrize("fmt", ["mxfp4", "mxfp8"])
 def test_mx_above_16_tokens_on_the_valu_path(fmt):
     """Above 16 tokens MX weights run on the fp32 VALU path (AUTO), which
