@@ -244,11 +244,11 @@ __global__ __launch_bounds__(kSmBlockWaves * kWave) void sm_kernel(Dims d, Input
 // ---------------------------------------------------------------------------
 // MX weights (OCP Microscaling: FP4 E2M1 or FP8 E4M3 elements, one E8M0
 // scale per 32 elements of a row along K; tokens and h stay bf16).  Same
-// items, K split and two-slot ring as sm_kernel with NBLK = 2; a stage is 128
-// bytes of each of the item's 32 weight rows (256 K elements of FP4, 128 of
-// FP8; four 1 KB direct loads of 8 whole rows each, pieces swizzled per row)
-// plus the rows' scale bytes for those K elements (8 or 4 per row, one 4-byte
-// direct load per lane).  In MFMA step i of a stage, lane group g = lane / 16
+// items, K split and two-slot ring as sm_kernel, with NB = 2 or 4 blocks of
+// 16 weight rows per item; a stage is 128 bytes of each of the item's 16 NB
+// weight rows (256 K elements of FP4, 128 of FP8; 2 NB 1 KB direct loads of 8
+// whole rows each, pieces swizzled per row) plus the rows' scale bytes for
+// those K elements (8 or 4 per row, 4-byte direct loads).  In MFMA step i of a stage, lane group g = lane / 16
 // takes K elements [32 i + 8 g, 32 i + 8 g + 8): each token-row load then
 // covers 64 contiguous bytes of every token (the four groups side by side,
 // as in the bf16 kernel), the lane's weight bytes for the step are 4-byte
@@ -262,22 +262,26 @@ __global__ __launch_bounds__(kSmBlockWaves * kWave) void sm_kernel(Dims d, Input
 // multiply by 2 to the power of the scale operand's exponent: with the scale
 // 2^(e - 127) built from the E8M0 byte that is exact.  The MFMA is the bf16
 // 16x16x32 of the bf16 path.
-constexpr int kMxRun = 128;                         // weight bytes per row per stage
-constexpr int kMxRows = 32;                         // weight rows per item
-constexpr int kMxWBytes = kMxRows * kMxRun;         // weight bytes per stage
-constexpr int kMxSBytes = 256;                      // scale area per stage
-constexpr int kMxStage = kMxWBytes + kMxSBytes;
-constexpr int kMxWaveLds = 2 * kMxStage;
-constexpr int kMxLds = kSmBlockWaves * kMxWaveLds;
-static_assert(kMxWaveLds >= 2 * kWave * 16, "partial sums fit the ring");
+constexpr int kMxRun = 128;   // weight bytes per row per stage
 
-template <int FMT>
+// NB blocks of 16 weight rows per item (gate/up: NB/2 of w1 and the matching
+// NB/2 of w3).
+template <int FMT, int NB>
 struct MxCfg {
   static constexpr bool F4 = FMT == kMXFP4;
   static constexpr int KPS = F4 ? 2 * kMxRun : kMxRun;   // K elements per stage
   static constexpr int SSTEPS = KPS / 32;                 // MFMA steps per stage
   static constexpr int SPR = KPS / 32;                    // scale bytes per row per stage
+  static constexpr int ROWS = 16 * NB;                    // weight rows per item
+  static constexpr int WBYTES = ROWS * kMxRun;            // weight bytes per stage
+  static constexpr int SBYTES = ROWS * 8;                 // scale area per stage (FP8 fills half)
+  static constexpr int STAGE = WBYTES + SBYTES;
+  static constexpr int WAVE_LDS = 2 * STAGE;
+  static constexpr int LDS = kSmBlockWaves * WAVE_LDS;
+  static constexpr int NSD = F4 ? NB / 2 : 1;             // 4-byte scale loads per lane per stage
   static_assert(FMT == kMXFP4 || FMT == kMXFP8, "MX formats");
+  static_assert(NB == 2 || NB == 4, "items of 2 or 4 blocks");
+  static_assert(WAVE_LDS >= NB * kWave * 16, "partial sums fit the ring");
 };
 
 // LDS reads issued without waiting (the stage's reads are waited for
@@ -315,15 +319,16 @@ __device__ __forceinline__ bf16x8_t fp8x8_to_bf16(uint32_t lo, uint32_t hi, uint
   return bf16x8_t{q0[0], q0[1], q1[0], q1[1], q2[0], q2[1], q3[0], q3[1]};
 }
 
-// At least four waves per SIMD (128 registers): the LDS of four blocks fits
-// a CU, and without the bound the FP4 kernels took 163 registers (three).
-template <int MODE, int FMT>
-__global__ __launch_bounds__(kSmBlockWaves * kWave, 4) void sm_mx_kernel(Dims d, Inputs in, Work w, int ks) {
-  using C = MxCfg<FMT>;
-  constexpr int CW = MODE == kSmGateUp ? 16 : 32;   // output columns per item
+// Waves per SIMD that the LDS allows (NB = 2: four blocks per CU, NB = 4:
+// two); without the bound the NB = 2 FP4 kernels took 163 registers (three
+// waves).
+template <int MODE, int FMT, int NB>
+__global__ __launch_bounds__(kSmBlockWaves * kWave, NB == 2 ? 4 : 2) void sm_mx_kernel(Dims d, Inputs in, Work w, int ks) {
+  using C = MxCfg<FMT, NB>;
+  constexpr int CW = MODE == kSmGateUp ? 8 * NB : 16 * NB;   // output columns per item
   extern __shared__ __align__(1024) uint8_t lds[];
   const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6);
-  uint8_t *ring = lds + wave * kMxWaveLds;
+  uint8_t *ring = lds + wave * C::WAVE_LDS;
   const int item = uniform(blockIdx.x * (kSmBlockWaves / ks) + wave / ks);
   const int kp = uniform(wave % ks);
 
@@ -334,7 +339,9 @@ __global__ __launch_bounds__(kSmBlockWaves * kWave, 4) void sm_mx_kernel(Dims d,
   const int ips = d.Is > 0 ? ((MODE == kSmGateUp ? d.Is : d.H) + CW - 1) / CW : 0;
   const bool live = item < na * ipr + ips;
 
-  f32x4_t acc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+  f32x4_t acc[NB];
+#pragma unroll
+  for (int j = 0; j < NB; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   int seg0 = 0, rows = 0, inter = 0, c0 = 0, ncol = 0;
   bool shared = false;
   if (live) {
@@ -384,105 +391,114 @@ __global__ __launch_bounds__(kSmBlockWaves * kWave, 4) void sm_mx_kernel(Dims d,
     // and store nothing).
     auto wrow = [&](int j) -> int {
       if (MODE == kSmGateUp) {
-        const int c = c0;
-        return c < ncol ? (j == 0 ? c : inter + c) : 0;
+        const int c = c0 + 16 * (j % (NB / 2));
+        return c < ncol ? (j < NB / 2 ? c : inter + c) : 0;
       }
       const int c = c0 + 16 * j;
       return c < ncol ? c : 0;
     };
     // Direct load q covers item rows 8 q .. 8 q + 7 (block q / 2); the lane
     // fetches logical piece sm_swz(lane % 8, row) of its row.
-    uint32_t qoff[4];
+    uint32_t qoff[2 * NB];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < 2 * NB; ++q) {
       const int row = (q % 2) * 8 + lane / 8;
       qoff[q] = static_cast<uint32_t>(wrow(q / 2) + row) * wbytes + sm_swz<kMxRun>(lane % 8, row) * 16;
     }
-    // scales: FP4 lane l fetches 4 of the 8 bytes of item row l / 2; FP8 lane
-    // l the 4 bytes of item row l % 32 (lanes 32-63 repeat rows 0-31 into the
-    // unused upper half of the scale area)
-    const int srow = C::F4 ? lane >> 1 : lane & 31;
-    const uint32_t soff = static_cast<uint32_t>(wrow(srow / 16) + srow % 16) * sbytes + (C::F4 ? (lane & 1) * 4 : 0);
+    // scales, item row s at byte SPR s of the scale area: FP4 load q has lane
+    // l fetch 4 of the 8 bytes of item row 32 q + l / 2; FP8 lane l the 4
+    // bytes of item row l % ROWS (with 32 rows, lanes 32-63 repeat rows 0-31
+    // into the unused upper half of the area)
+    uint32_t soff[C::NSD];
+#pragma unroll
+    for (int q = 0; q < C::NSD; ++q) {
+      const int srow = C::F4 ? 32 * q + (lane >> 1) : lane % C::ROWS;
+      soff[q] = static_cast<uint32_t>(wrow(srow / 16) + srow % 16) * sbytes + (C::F4 ? (lane & 1) * 4 : 0);
+    }
 
     const int nst_all = K / C::KPS;
     const int st0 = uniform(nst_all * kp / ks), st1 = uniform(nst_all * (kp + 1) / ks);
     uint4 aA[C::SSTEPS], aB[C::SSTEPS];
     auto issue = [&](int st, int sl, uint4 (&A)[C::SSTEPS]) {
-      uint8_t *slot = ring + sl * kMxStage;
+      uint8_t *slot = ring + sl * C::STAGE;
       const uint32_t kw = static_cast<uint32_t>(st) * kMxRun;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) dma16_to_lds(Wb + (qoff[q] + kw), slot + q * 1024);
-      dma4_to_lds(Sb + (soff + static_cast<uint32_t>(st) * C::SPR), slot + kMxWBytes);
+      for (int q = 0; q < 2 * NB; ++q) dma16_to_lds(Wb + (qoff[q] + kw), slot + q * 1024);
+#pragma unroll
+      for (int q = 0; q < C::NSD; ++q)
+        dma4_to_lds(Sb + (soff[q] + static_cast<uint32_t>(st) * C::SPR), slot + C::WBYTES + q * 256);
       const uint32_t ka = static_cast<uint32_t>(st) * C::KPS * 2;
 #pragma unroll
       for (int i = 0; i < C::SSTEPS; ++i) A[i] = *reinterpret_cast<const uint4 *>(Ab + (aoff + ka) + i * 64);
     };
     // the lane's weight bytes of step i: FP4 word g of logical piece i of row
-    // r, FP8 the 8 bytes at 8 (g % 2) of logical piece 2 i + g / 2 (block 1
-    // is 16 rows further on); its scale bytes: the row's SPR bytes
+    // r, FP8 the 8 bytes at 8 (g % 2) of logical piece 2 i + g / 2 (block j
+    // is 16 j rows further on); its scale bytes: the row's SPR bytes
     uint32_t boff[C::SSTEPS];
 #pragma unroll
     for (int i = 0; i < C::SSTEPS; ++i)
       boff[i] = C::F4 ? static_cast<uint32_t>(r * kMxRun + sm_swz<kMxRun>(i, r) * 16 + 4 * g)
                       : static_cast<uint32_t>(r * kMxRun + sm_swz<kMxRun>(2 * i + g / 2, r) * 16 + 8 * (g % 2));
-    const uint32_t srd = static_cast<uint32_t>(kMxWBytes + r * C::SPR);
+    const uint32_t srd = static_cast<uint32_t>(C::WBYTES + r * C::SPR);
     auto compute = [&](int sl, const uint4 (&A)[C::SSTEPS]) {
-      const uint32_t base = lds_off(ring + sl * kMxStage);
-      constexpr int B1 = 16 * kMxRun;   // block 1
+      const uint32_t base = lds_off(ring + sl * C::STAGE);
       if constexpr (C::F4) {
-        uint32_t w0[8], w1[8];
-        u32x2_t q0, q1;
-        static_for<0, 8>([&](auto ic) {
-          constexpr int i = decltype(ic)::value;
-          mx_issue_b32<0>(base + boff[i], w0[i]);
-          mx_issue_b32<B1>(base + boff[i], w1[i]);
+        uint32_t wv[NB][8];
+        u32x2_t q[NB];
+        static_for<0, NB>([&](auto jc) {
+          constexpr int j = decltype(jc)::value;
+          static_for<0, 8>([&](auto ic) {
+            constexpr int i = decltype(ic)::value;
+            mx_issue_b32<j * 16 * kMxRun>(base + boff[i], wv[j][i]);
+          });
+          mx_issue_b64<j * 16 * 8>(base + srd, q[j]);
         });
-        mx_issue_b64<0>(base + srd, q0);
-        mx_issue_b64<16 * 8>(base + srd, q1);
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        static_for<0, 8>([&](auto ic) {
-          mx_tie(w0[decltype(ic)::value]);
-          mx_tie(w1[decltype(ic)::value]);
+        static_for<0, NB>([&](auto jc) {
+          constexpr int j = decltype(jc)::value;
+          static_for<0, 8>([&](auto ic) { mx_tie(wv[j][decltype(ic)::value]); });
+          mx_tie(q[j]);
         });
-        mx_tie(q0);
-        mx_tie(q1);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          // scale byte i of the row's 8 covers step i
-          const uint32_t e0 = ((i < 4 ? q0.x : q0.y) >> (8 * (i % 4))) & 0xffu;
-          const uint32_t e1 = ((i < 4 ? q1.x : q1.y) >> (8 * (i % 4))) & 0xffu;
           const bf16x8_t a = __builtin_bit_cast(bf16x8_t, A[i]);
-          acc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, fp4x8_to_bf16(w0[i], e0), acc[0], 0, 0, 0);
-          acc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, fp4x8_to_bf16(w1[i], e1), acc[1], 0, 0, 0);
+#pragma unroll
+          for (int j = 0; j < NB; ++j) {
+            // scale byte i of the row's 8 covers step i
+            const uint32_t e = ((i < 4 ? q[j].x : q[j].y) >> (8 * (i % 4))) & 0xffu;
+            acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, fp4x8_to_bf16(wv[j][i], e), acc[j], 0, 0, 0);
+          }
         }
       } else {
-        u32x2_t w0[4], w1[4];
-        uint32_t q0, q1;
-        static_for<0, 4>([&](auto ic) {
-          constexpr int i = decltype(ic)::value;
-          mx_issue_b64<0>(base + boff[i], w0[i]);
-          mx_issue_b64<B1>(base + boff[i], w1[i]);
+        u32x2_t wv[NB][4];
+        uint32_t q[NB];
+        static_for<0, NB>([&](auto jc) {
+          constexpr int j = decltype(jc)::value;
+          static_for<0, 4>([&](auto ic) {
+            constexpr int i = decltype(ic)::value;
+            mx_issue_b64<j * 16 * kMxRun>(base + boff[i], wv[j][i]);
+          });
+          mx_issue_b32<j * 16 * 4>(base + srd, q[j]);
         });
-        mx_issue_b32<0>(base + srd, q0);
-        mx_issue_b32<16 * 4>(base + srd, q1);
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        static_for<0, 4>([&](auto ic) {
-          mx_tie(w0[decltype(ic)::value]);
-          mx_tie(w1[decltype(ic)::value]);
+        static_for<0, NB>([&](auto jc) {
+          constexpr int j = decltype(jc)::value;
+          static_for<0, 4>([&](auto ic) { mx_tie(wv[j][decltype(ic)::value]); });
+          mx_tie(q[j]);
         });
-        mx_tie(q0);
-        mx_tie(q1);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          // scale byte i of the row's 4 covers step i
-          const uint32_t e0 = (q0 >> (8 * i)) & 0xffu, e1 = (q1 >> (8 * i)) & 0xffu;
           const bf16x8_t a = __builtin_bit_cast(bf16x8_t, A[i]);
-          acc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, fp8x8_to_bf16(w0[i].x, w0[i].y, e0), acc[0], 0, 0, 0);
-          acc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, fp8x8_to_bf16(w1[i].x, w1[i].y, e1), acc[1], 0, 0, 0);
+#pragma unroll
+          for (int j = 0; j < NB; ++j) {
+            // scale byte i of the row's 4 covers step i
+            const uint32_t e = (q[j] >> (8 * i)) & 0xffu;
+            acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, fp8x8_to_bf16(wv[j][i].x, wv[j][i].y, e), acc[j], 0, 0, 0);
+          }
         }
       }
     };
-    constexpr int LPS = 4 + 1 + C::SSTEPS;   // vector-memory ops per stage
+    constexpr int LPS = 2 * NB + C::NSD + C::SSTEPS;   // vector-memory ops per stage
     const int n = st1 - st0;
     if (n > 0) {
       issue(st0, 0, aA);
@@ -504,13 +520,13 @@ __global__ __launch_bounds__(kSmBlockWaves * kWave, 4) void sm_mx_kernel(Dims d,
   if (ks > 1) {
     f32x4_t *part = reinterpret_cast<f32x4_t *>(ring);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) part[j * kWave + lane] = acc[j];
+    for (int j = 0; j < NB; ++j) part[j * kWave + lane] = acc[j];
     __syncthreads();
     if (kp != 0) return;
     for (int q = 1; q < ks; ++q) {
-      const f32x4_t *other = reinterpret_cast<const f32x4_t *>(lds + (wave + q) * kMxWaveLds);
+      const f32x4_t *other = reinterpret_cast<const f32x4_t *>(lds + (wave + q) * C::WAVE_LDS);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) acc[j] += other[j * kWave + lane];
+      for (int j = 0; j < NB; ++j) acc[j] += other[j * kWave + lane];
     }
   }
   if (!live) return;
@@ -522,8 +538,13 @@ __global__ __launch_bounds__(kSmBlockWaves * kWave, 4) void sm_mx_kernel(Dims d,
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = (lane >> 4) * 4 + i;
-      if (row < rows && c0 < ncol)
-        h[static_cast<size_t>(row) * inter + c0 + cl] = f32_to_bf16(silu(acc[0][i]) * acc[1][i]);
+      if (row < rows) {
+#pragma unroll
+        for (int j = 0; j < NB / 2; ++j)
+          if (c0 + 16 * j < ncol)
+            h[static_cast<size_t>(row) * inter + c0 + 16 * j + cl] =
+                f32_to_bf16(silu(acc[j][i]) * acc[j + NB / 2][i]);
+      }
     }
   } else {
     uint16_t *y = static_cast<uint16_t *>(shared ? w.y_sh : w.y) + static_cast<size_t>(seg0) * d.H;
@@ -532,7 +553,7 @@ __global__ __launch_bounds__(kSmBlockWaves * kWave, 4) void sm_mx_kernel(Dims d,
       const int row = (lane >> 4) * 4 + i;
       if (row < rows) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < NB; ++j)
           if (c0 + 16 * j < ncol)
             y[static_cast<size_t>(row) * d.H + c0 + 16 * j + cl] = f32_to_bf16(acc[j][i]);
       }
@@ -579,13 +600,22 @@ static hipError_t sm_launch(const Dims &d, const Inputs &in, const Work &w, hipS
   return hipGetLastError();
 }
 
+// Blocks of 16 weight rows per MX item.  Four halve the token-row loads per
+// weight byte, which helps where they are heaviest, the MXFP4 gate/up (8 KB
+// of token rows per 4 KB weight stage with two blocks; 16 tokens: 33.1-33.4
+// against 34.6-35.6 us); with two blocks per CU instead of four the MXFP4
+// down (19.3-19.7 -> 20.8-21.1 us) and both MXFP8 kernels were slower.
+template <int MODE, int FMT>
+constexpr int mx_blocks() { return MODE == kSmGateUp && FMT == kMXFP4 ? 4 : 2; }
+
 // MX launch: the item count and grid of sm_launch; the K split of sm_launch
 // except for short gate/up items.
-template <int MODE, int FMT>
+template <int MODE, int FMT, int NB>
 static hipError_t sm_mx_launch(const Dims &d, const Inputs &in, const Work &w, hipStream_t s) {
-  constexpr int CW = MODE == kSmGateUp ? 16 : 32;
-  auto kern = sm_mx_kernel<MODE, FMT>;
-  static const KernelSetup su = kernel_setup(reinterpret_cast<const void *>(kern), kSmBlockWaves * kWave, kMxLds);
+  using C = MxCfg<FMT, NB>;
+  constexpr int CW = MODE == kSmGateUp ? 8 * NB : 16 * NB;
+  auto kern = sm_mx_kernel<MODE, FMT, NB>;
+  static const KernelSetup su = kernel_setup(reinterpret_cast<const void *>(kern), kSmBlockWaves * kWave, C::LDS);
   if (su.err != hipSuccess) return su.err;
   const int blocks_per_cu = su.blocks_per_cu;
   const int slots = d.te < d.E ? d.te : d.E;
@@ -595,14 +625,14 @@ static hipError_t sm_mx_launch(const Dims &d, const Inputs &in, const Work &w, h
   const long items = static_cast<long>(slots) * ipr + ips;
   const long cap = static_cast<long>(device_cus()) * blocks_per_cu * kSmBlockWaves;
   const int kmin = MODE == kSmGateUp ? d.H : (d.Is > 0 && d.Is < d.I ? d.Is : d.I);
-  const int nst = kmin / MxCfg<FMT>::KPS;
+  const int nst = kmin / C::KPS;
   // gate/up items of at most 8 stages (MXFP4 at K = 2048) keep one wave:
   // splitting them left each wave four stages (34.6-34.9 against 35.1-35.6 us
   // at 16 tokens)
   const int ks = MODE == kSmGateUp && nst <= 8 ? 1 : sm_pick_ks(items, cap, nst);
   const long per_block = kSmBlockWaves / ks;
   const long grid = (items + per_block - 1) / per_block;
-  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(kSmBlockWaves * kWave), kMxLds, s,
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(kSmBlockWaves * kWave), C::LDS, s,
                      d, in, w, ks);
   return hipGetLastError();
 }
@@ -620,15 +650,15 @@ static hipError_t sm_dispatch(const Dims &d, const Inputs &in, const Work &w, hi
 
 hipError_t launch_small_m_gateup(const Dims &d, const Inputs &in, const Work &w,
                                  hipStream_t s) {
-  if (d.wdt == kMXFP4) return sm_mx_launch<kSmGateUp, kMXFP4>(d, in, w, s);
-  if (d.wdt == kMXFP8) return sm_mx_launch<kSmGateUp, kMXFP8>(d, in, w, s);
+  if (d.wdt == kMXFP4) return sm_mx_launch<kSmGateUp, kMXFP4, mx_blocks<kSmGateUp, kMXFP4>()>(d, in, w, s);
+  if (d.wdt == kMXFP8) return sm_mx_launch<kSmGateUp, kMXFP8, mx_blocks<kSmGateUp, kMXFP8>()>(d, in, w, s);
   return sm_dispatch<kSmGateUp, 2>(d, in, w, s, d.H);   // 16 h columns per item
 }
 
 hipError_t launch_small_m_down(const Dims &d, const Inputs &in, const Work &w,
                                hipStream_t s) {
-  if (d.wdt == kMXFP4) return sm_mx_launch<kSmDown, kMXFP4>(d, in, w, s);
-  if (d.wdt == kMXFP8) return sm_mx_launch<kSmDown, kMXFP8>(d, in, w, s);
+  if (d.wdt == kMXFP4) return sm_mx_launch<kSmDown, kMXFP4, mx_blocks<kSmDown, kMXFP4>()>(d, in, w, s);
+  if (d.wdt == kMXFP8) return sm_mx_launch<kSmDown, kMXFP8, mx_blocks<kSmDown, kMXFP8>()>(d, in, w, s);
   // K is I for routed slots and I_s for the shared one: stages fit both
   const int kg = d.Is > 0 ? (d.I % 128 == 0 && d.Is % 128 == 0 ? 128 : (d.I % 64 == 0 && d.Is % 64 == 0 ? 64 : 32))
                           : d.I;
