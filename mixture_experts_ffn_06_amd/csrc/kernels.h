@@ -17,7 +17,7 @@ struct Dims {
   int Is;       // shared intermediate (0 = none)
   int k;        // top-k
   int te;       // m * k
-  int wdt;      // weight storage: kF32 / kBF16 / kFP8
+  int wdt;      // weight storage: kF32 / kBF16 / kFP8 / kMXFP4 / kMXFP8
   int gating;   // 0 softmax, 1 sigmoid, 2 sqrtsoftplus
   int renorm;   // 1: renormalise the selected weights
   float scale;  // routed scaling factor
@@ -29,13 +29,13 @@ struct Inputs {
   const void *router_w;    // [E,H]
   const void *w13;         // [E,2I,H]
   const void *w2;          // [E,H,I]
-  const float *w13_scale;  // [E,2I/128,H/128] (fp8)
-  const float *w2_scale;   // [E,H/128,I/128]  (fp8)
+  const float *w13_scale;  // fp8: [E,2I/128,H/128] floats; MX: [E,2I,H/32] E8M0 bytes
+  const float *w2_scale;   // fp8: [E,H/128,I/128] floats;  MX: [E,H,I/32] E8M0 bytes
   const float *bias;       // [E] or null
   const void *sw13;        // shared [2Is,H]
   const void *sw2;         // shared [H,Is]
-  const float *sw13_scale; // [2Is/128,H/128]
-  const float *sw2_scale;  // [H/128,Is/128]
+  const float *sw13_scale; // [2Is/128,H/128] (MX: [2Is,H/32] bytes)
+  const float *sw2_scale;  // [H/128,Is/128]  (MX: [H,Is/32] bytes)
   const void *sgate;       // [H] shared-expert gate vector (format of x) or null
 };
 
@@ -94,10 +94,10 @@ hipError_t launch_quant_x(const Dims &d, const Inputs &in, const Work &w,
 // simple.hip (fp32 VALU, any storage format)
 hipError_t launch_simple_gateup(const Dims &d, const Inputs &in, const Work &w, hipStream_t s);
 hipError_t launch_simple_down(const Dims &d, const Inputs &in, const Work &w, hipStream_t s);
-// grouped.hip (MFMA grouped GEMM, bf16 / fp8)
+// grouped.hip (MFMA grouped GEMM, bf16 / fp8 weights)
 hipError_t launch_grouped_gateup(const Dims &d, const Inputs &in, const Work &w, hipStream_t s);
 hipError_t launch_grouped_down(const Dims &d, const Inputs &in, const Work &w, hipStream_t s);
-// small_m.hip (weight streaming for m <= 16, bf16)
+// small_m.hip (weight streaming for m <= 16; bf16, MXFP4 and MXFP8 weights)
 hipError_t launch_small_m_gateup(const Dims &d, const Inputs &in, const Work &w, hipStream_t s);
 hipError_t launch_small_m_down(const Dims &d, const Inputs &in, const Work &w, hipStream_t s);
 

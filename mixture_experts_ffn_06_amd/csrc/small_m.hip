@@ -21,7 +21,8 @@
 // fragments are read back from LDS (16-byte pieces XOR-swizzled per row so
 // those reads are bank-conflict free).  The slot's <= 16 token rows (A, read
 // from L2) go straight to registers, one stage ahead like the weights.  The
-// grid is sized so that every item is resident at once.
+// grid covers the largest item count the routing allows (the live count is
+// only known on the device; waves past it exit at once).
 #include "common.h"
 #include "kernels.h"
 #include "launch.h"
