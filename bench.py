@@ -182,6 +182,8 @@ def main():
 
     wl = synth.WORKLOADS[args.workload]
     m = args.m or wl.m
+    if m > wl.m:   # a larger batch: the same recipe with more tokens drawn
+        wl = wl.replace(m=m)
     dev = torch.device("cuda:0")
     inp = synth.make_inputs(wl, device=dev, m=m)
     wbytes = sum(v.numel() * v.element_size() for k, v in inp.items()

@@ -37,14 +37,22 @@ bool aligned(const void *p, size_t a) {
   return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0;
 }
 
+// Most tokens the weight-streaming path takes: bf16 weights 16 (one block of
+// 16 rows per expert); MX weights kMxStreamMaxTokens (blocks of 16 rows, each
+// streaming its expert's weights once).
+constexpr int kMxStreamMaxTokens = 128;
+
+bool is_mx(int weight_dtype) { return weight_dtype == MOE_MXFP4 || weight_dtype == MOE_MXFP8; }
+
+int small_m_limit(const moe_config_t &c) { return is_mx(c.weight_dtype) ? kMxStreamMaxTokens : 16; }
+
 int resolve_path(const moe_config_t &c, int m) {
   if (c.path != MOE_PATH_AUTO) return c.path;
   if (c.weight_dtype == MOE_F32) return MOE_PATH_SIMPLE;
-  if ((c.weight_dtype == MOE_BF16 || c.weight_dtype == MOE_MXFP4 || c.weight_dtype == MOE_MXFP8) &&
-      m <= 16)
+  if ((c.weight_dtype == MOE_BF16 || is_mx(c.weight_dtype)) && m <= small_m_limit(c))
     return MOE_PATH_SMALL_M;
-  // MX weights above 16 tokens: the VALU path (no grouped MX GEMM)
-  if (c.weight_dtype == MOE_MXFP4 || c.weight_dtype == MOE_MXFP8) return MOE_PATH_SIMPLE;
+  // MX weights above that: the VALU path (no grouped MX GEMM)
+  if (is_mx(c.weight_dtype)) return MOE_PATH_SIMPLE;
   return MOE_PATH_GROUPED;
 }
 
@@ -192,7 +200,7 @@ int run_forward(moe_plan_t plan, int32_t m, const void *x, const void *router_w,
     if (shared->gate && !aligned(shared->gate, 16)) return MOE_ERR_INVALID_ARG;
   }
   const int path = resolve_path(c, m);
-  if (path == MOE_PATH_SMALL_M && m > 16) return MOE_ERR_UNSUPPORTED;
+  if (path == MOE_PATH_SMALL_M && m > small_m_limit(c)) return MOE_ERR_UNSUPPORTED;
   const Layout L = layout(*plan, m);
   if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
 

@@ -256,11 +256,14 @@ def make_inputs(wl: Workload, device="cpu", m: int | None = None) -> dict:
     ``w13_scale [E,2I/128,H/128]`` / ``w2_scale [E,H/128,I/128]`` (fp8 only),
     ``shared_w13 [2Is,H]``, ``shared_w2 [H,Is]`` (+ scales), ``shared_gate
     [H]`` (activation format), ``bias [E]``.
-    Absent entries are None.  ``m`` takes a prefix of the token draw.
+    Absent entries are None.  ``m`` takes a prefix of the token draw (at most
+    ``wl.m`` tokens: a larger batch is a workload of its own, ``wl.replace(m=...)``).
     """
     device = torch.device(device)
     x = draw_x(wl)
     if m is not None:
+        if m > wl.m:
+            raise ValueError(f"{wl.name}: m = {m} exceeds the workload's {wl.m} tokens")
         x = x[:m]
     out = {"x": _store_act(x, wl.act_dtype, device),
            "router_w": _store_act(draw_router(wl), wl.act_dtype, device)}

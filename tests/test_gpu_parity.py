@@ -287,6 +287,18 @@ def test_mx_long_rows_split_over_waves(fmt, m):
     run_case(MX_WIDE.replace(name=f"{fmt}_wide", dtype=fmt), path="small_m", m=m)
 
 
+@pytest.mark.parametrize("fmt,m", [("mxfp4", 40), ("mxfp4", 128), ("mxfp8", 33)])
+def test_mx_above_16_tokens_on_the_streaming_path(fmt, m):
+    """Above 16 tokens the MX streaming kernels take each expert's rows in
+    blocks of 16 (33 tokens: a last block of one shared-expert row)."""
+    run_case(MX_SMALL.replace(name=f"{fmt}_rows", m=m, dtype=fmt), path="small_m")
+
+
+def test_decode_mxfp4_128_tokens_sampled():
+    wl = synth.WORKLOADS["decode_mxfp4"].replace(name="decode_mxfp4_128", m=128)
+    run_case(wl, path="small_m", tokens=_sample(128), lazy=True)
+
+
 @pytest.mark.parametrize("fmt", ["mxfp4", "mxfp8"])
 def test_mx_above_16_tokens_on_the_valu_path(fmt):
     """Above 16 tokens MX weights run on the fp32 VALU path (AUTO), which

@@ -62,3 +62,14 @@ def test_inputs_are_deterministic_and_shaped(dt):
         assert tuple(a["w13_scale"].shape) == (3, 2, 2)
         assert tuple(a["w2_scale"].shape) == (3, 2, 1)
         assert tuple(a["shared_w2_scale"].shape) == (2, 1)
+
+
+def test_token_prefix_never_exceeds_the_draw():
+    """A prefix of the token draw has at most the workload's tokens; a
+    larger batch is drawn as a workload of its own."""
+    wl = synth.WORKLOADS["tiny_f32"]
+    assert synth.make_inputs(wl, m=wl.m - 1)["x"].shape[0] == wl.m - 1
+    with pytest.raises(ValueError):
+        synth.make_inputs(wl, m=wl.m + 1)
+    big = wl.replace(m=wl.m + 5)
+    assert synth.make_inputs(big)["x"].shape[0] == wl.m + 5
