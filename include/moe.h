@@ -78,14 +78,14 @@ typedef enum {
 } moe_gating_t;
 
 /* Expert-path choice.  AUTO: fp32 weights -> SIMPLE; bf16 weights: m <= 16
- * -> SMALL_M, else GROUPED; MXFP4 / MXFP8 weights: m <= 128 -> SMALL_M, else
+ * -> SMALL_M, else GROUPED; MXFP4 / MXFP8 weights: m <= 1024 -> SMALL_M, else
  * SIMPLE; fp8 weights: GROUPED.  The others force a path (for testing; every path
  * computes the same layer). */
 typedef enum {
   MOE_PATH_AUTO = 0,
   MOE_PATH_SIMPLE = 1,   /* fp32 VALU kernels, any dtype */
   MOE_PATH_GROUPED = 2,  /* MFMA grouped GEMM, bf16 / fp8 */
-  MOE_PATH_SMALL_M = 3   /* weight-streaming path: bf16 m <= 16, MXFP4 / MXFP8 m <= 128 */
+  MOE_PATH_SMALL_M = 3   /* weight-streaming path: bf16 m <= 16, MXFP4 / MXFP8 m <= 1024 */
 } moe_path_t;
 
 typedef enum {
@@ -174,7 +174,7 @@ typedef struct {
  * H, I or I_s not multiples of 128, bf16/fp8 with H, I or I_s not multiples
  * of 32, MXFP4 (MXFP8) with H, I or I_s not multiples of 256 (128) or the
  * GROUPED path forced (the MX formats run on the weight-streaming path up to
- * 128 tokens and on the VALU path above), SMALL_M forced with fp8/fp32 weights, or
+ * 1024 tokens and on the VALU path above), SMALL_M forced with fp8/fp32 weights, or
  * sizes whose operands
  * reach 2 GiB (max_tokens * topk * max(H, I, I_s) elements, or one expert's
  * 2 * max(I, I_s) * H weight elements, at 2 bytes per bf16/fp8 element and 4

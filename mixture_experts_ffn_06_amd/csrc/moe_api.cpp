@@ -39,8 +39,11 @@ bool aligned(const void *p, size_t a) {
 
 // Most tokens the weight-streaming path takes: bf16 weights 16 (one block of
 // 16 rows per expert); MX weights kMxStreamMaxTokens (blocks of 16 rows, each
-// streaming its expert's weights once).
-constexpr int kMxStreamMaxTokens = 128;
+// streaming its expert's weights once; the blocks of one expert run side by
+// side, so the repeats are mostly served from cache).  With no grouped MX
+// GEMM the alternative is the VALU path (MXFP4, 64 tokens: 59.5 ms against
+// 0.14 ms); at 1024 tokens MXFP4 runs at 2.0 M tokens/s.
+constexpr int kMxStreamMaxTokens = 1024;
 
 bool is_mx(int weight_dtype) { return weight_dtype == MOE_MXFP4 || weight_dtype == MOE_MXFP8; }
 

@@ -294,9 +294,12 @@ def test_mx_above_16_tokens_on_the_streaming_path(fmt, m):
     run_case(MX_SMALL.replace(name=f"{fmt}_rows", m=m, dtype=fmt), path="small_m")
 
 
-def test_decode_mxfp4_128_tokens_sampled():
-    wl = synth.WORKLOADS["decode_mxfp4"].replace(name="decode_mxfp4_128", m=128)
-    run_case(wl, path="small_m", tokens=_sample(128), lazy=True)
+@pytest.mark.parametrize("fmt,m", [("mxfp4", 128), ("mxfp4", 1024), ("mxfp8", 300)])
+def test_mx_streaming_many_tokens_sampled(fmt, m):
+    """Full-size MX layers at prefill-sized batches (up to 64 row blocks per
+    expert), checked on sampled tokens."""
+    wl = synth.WORKLOADS[f"decode_{fmt}"].replace(name=f"decode_{fmt}_{m}", m=m)
+    run_case(wl, path="small_m", tokens=_sample(m), lazy=True)
 
 
 @pytest.mark.parametrize("fmt", ["mxfp4", "mxfp8"])
