@@ -1,4 +1,6 @@
-// Small-m (m <= 16) expert path: stream each selected expert's weights once.
+// Small-batch expert path: stream each selected expert's weights once per
+// block of 16 of its rows (bf16 weights: m <= 16, one block; MX weights: up to
+// 1024 tokens, ceil(rows / 16) blocks).
 //
 // With at most 16 tokens every expert holds at most 16 rows, so the work is
 // a bandwidth-bound GEMV over the selected experts' weights (forward.rs,
