@@ -1,6 +1,6 @@
 // Small-batch expert path: stream each selected expert's weights once per
-// block of 16 of its rows (bf16 weights: m <= 16, one block; MX weights: up to
-// 1024 tokens, ceil(rows / 16) blocks).
+// block of 16 of its rows (bf16 weights up to 128 tokens, MX weights up to
+// 1024; an expert of r rows takes ceil(r / 16) blocks).
 //
 // With at most 16 tokens every expert holds at most 16 rows, so the work is
 // a bandwidth-bound GEMV over the selected experts' weights (forward.rs,
@@ -69,34 +69,46 @@ __global__ __launch_bounds__(kSmBlockWaves * kWave) void sm_kernel(Dims d, Input
   const int item = uniform(blockIdx.x * (kSmBlockWaves / ks) + wave / ks);
   const int kp = uniform(wave % ks);
 
-  // ---- the item: slot and column group ----
+  // ---- the item: slot, block of 16 rows and column group ----
+  // Items (slot, row block rb, column group) run column groups fastest; a
+  // slot has nrb = ceil(m / 16) row blocks (an expert holds at most m rows),
+  // and row blocks past a slot's rows exit at once.
   const int na = uniform(*w.nactive);
   const int ncol_r = MODE == kSmGateUp ? d.I : d.H;
   const int ipr = (ncol_r + CW - 1) / CW;                  // items per routed slot
   const int ips = d.Is > 0 ? ((MODE == kSmGateUp ? d.Is : d.H) + CW - 1) / CW : 0;
-  const bool live = item < na * ipr + ips;
+  const int nrb = (d.m + 15) >> 4;
 
   f32x4_t acc[NBLK];
 #pragma unroll
   for (int j = 0; j < NBLK; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  int seg0 = 0, rows = 0, inter = 0, c0 = 0, ncol = 0;
+  int seg0 = 0, rows = 0, inter = 0, c0 = 0, ncol = 0, e = 0, cg = 0;
   bool shared = false;
-  if (live) {
-    int e, cg;
-    if (item < na * ipr) {
-      const int slot = item / ipr;
-      cg = item - slot * ipr;
+  if (item < (na * ipr + ips) * nrb) {
+    int rb;
+    if (item < na * nrb * ipr) {
+      const int sr = item / ipr;
+      cg = item - sr * ipr;
+      const int slot = sr / nrb;
+      rb = sr - slot * nrb;
       e = uniform(w.active[slot]);
       seg0 = uniform(w.offsets[e]);
-      rows = uniform(w.offsets[e + 1]) - seg0;   // <= m <= 16
+      rows = uniform(w.offsets[e + 1]) - seg0;
       inter = d.I;
     } else {
       shared = true;
       e = d.E;
-      cg = item - na * ipr;
+      const int t = item - na * nrb * ipr;
+      rb = t / ips;
+      cg = t - rb * ips;
       rows = d.m;
       inter = d.Is;
     }
+    seg0 = uniform(seg0 + 16 * rb);
+    rows = uniform(min(16, rows - 16 * rb));
+  }
+  const bool live = rows > 0;
+  if (live) {
     c0 = cg * CW;
     ncol = MODE == kSmGateUp ? inter : d.H;
     const int K = MODE == kSmGateUp ? d.H : inter;
@@ -109,7 +121,7 @@ __global__ __launch_bounds__(kSmBlockWaves * kWave) void sm_kernel(Dims d, Input
     const uint8_t *Ab, *Wb;
     uint32_t aoff;
     if (MODE == kSmGateUp) {
-      const int tok = shared ? ar : w.sorted_pair[seg0 + ar] / d.k;
+      const int tok = shared ? seg0 + ar : w.sorted_pair[seg0 + ar] / d.k;
       Ab = static_cast<const uint8_t *>(in.x);
       aoff = static_cast<uint32_t>(tok) * kbytes;
       Wb = shared ? static_cast<const uint8_t *>(in.sw13)
@@ -602,7 +614,7 @@ static hipError_t sm_launch(const Dims &d, const Inputs &in, const Work &w, hipS
   const int ncol_r = MODE == kSmGateUp ? d.I : d.H;
   const int ipr = (ncol_r + CW - 1) / CW;
   const int ips = d.Is > 0 ? ((MODE == kSmGateUp ? d.Is : d.H) + CW - 1) / CW : 0;
-  const long items = static_cast<long>(slots) * ipr + ips;
+  const long items = (static_cast<long>(slots) * ipr + ips) * ((d.m + 15) / 16);
   const long cap = static_cast<long>(device_cus()) * blocks_per_cu * kSmBlockWaves;
   // K stages of the shortest item (the shared expert's down K is I_s)
   const int kmin = MODE == kSmGateUp ? d.H : (d.Is > 0 && d.Is < d.I ? d.Is : d.I);

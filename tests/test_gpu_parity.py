@@ -143,6 +143,20 @@ def test_small_m_with_shared_expert(m):
     run_case(RAGGED_BF16, path="small_m", m=m)
 
 
+@pytest.mark.parametrize("wl", [RAGGED_BF16.replace(name="ragged_bf16_40", m=40),
+                                RAGGED_BF16.replace(name="ragged_bf16_128", m=128),
+                                SIGMOID_BF16], ids=["ragged40", "ragged128", "sigmoid77"])
+def test_small_m_above_16_tokens(wl):
+    """bf16 weights above 16 tokens stream each expert's rows in blocks of
+    16 (the shared expert's 40 or 77 rows: a partial last block)."""
+    run_case(wl, path="small_m")
+
+
+def test_decode_bf16_64_tokens_small_m_sampled():
+    wl = synth.WORKLOADS["decode_bf16"].replace(name="decode_bf16_64", m=64)
+    run_case(wl, path="small_m", tokens=_sample(64), lazy=True)
+
+
 @pytest.mark.parametrize("path", ["grouped", "small_m"])
 def test_sigmoid_bias_bf16(path):
     run_case(SIGMOID_BF16, path=path, m=16 if path == "small_m" else None)
