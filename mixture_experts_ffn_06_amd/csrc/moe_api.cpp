@@ -42,7 +42,8 @@ bool aligned(const void *p, size_t a) {
 // side by side, so the repeats are mostly served from cache): bf16 weights
 // kBf16StreamMaxTokens, where the grouped MFMA path takes over (bf16 layer of
 // 128 experts, 2048 x 768: 32 tokens 154 K against 118 K tokens/s, 64 tokens
-// 267 K against 212 K, 128 tokens 440 K against 407 K); MX weights
+// 267 K against 212 K, 128 tokens 440 K against 407 K; 192 tokens: 562 K
+// against 620 K, the repeated down streams cost more than they save); MX weights
 // kMxStreamMaxTokens.  With no grouped MX
 // GEMM the alternative is the VALU path (MXFP4, 64 tokens: 59.5 ms against
 // 0.14 ms); at 1024 tokens MXFP4 runs at 2.0 M tokens/s.
