@@ -13,13 +13,6 @@ import numpy as np
 from .codec import bf16_round, e4m3_decode, e4m3_quantize_rows
 
 
-def _store_y(y: np.ndarray, dtype: str) -> np.ndarray:
-    """Down outputs are kept in bf16 (fp32 for the fp32 layer)."""
-    if dtype == "f32":
-        return y.astype(np.float32).astype(np.float64)
-    return bf16_round(y)
-
-
 def _round_h(a: np.ndarray, dtype: str, block: int) -> np.ndarray:
     """Round a ``[..., I]`` SwiGLU output to the down operand format."""
     if dtype == "f32":
@@ -93,14 +86,14 @@ def dense_forward(xt: np.ndarray, logits: np.ndarray, k: int, gating: str,
     u = np.einsum("th,eih->tei", xt, W13[:, inter:, :])
     a = g / (1.0 + np.exp(-g)) * u
     a = _round_h(a, dtype, block)
-    y = _store_y(np.einsum("tei,ehi->teh", a, W2), dtype)
+    y = np.einsum("tei,ehi->teh", a, W2)     # down outputs enter the reduce unrounded
     out = np.einsum("te,teh->th", M, y)
     if shared is not None and shared_inter > 0:
         S13, S2 = shared
         gs = xt @ S13[:shared_inter].T
         us = xt @ S13[shared_inter:].T
         hs = _round_h(gs / (1.0 + np.exp(-gs)) * us, dtype, block)
-        ys = _store_y(hs @ S2.T, dtype)
+        ys = hs @ S2.T
         if gate is not None:
             ys = ys / (1.0 + np.exp(-(x_gate @ gate)))[:, None]
         out = out + ys

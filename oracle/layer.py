@@ -16,10 +16,10 @@ notes of the repository):
 * softmax gating ranks the softmax probabilities over all E experts and the
   k selected ones are divided by their sum (``norm_topk_prob``, page 3,
   top-k dispatch);
-* sigmoid gating ranks ``sigmoid(l) + bias`` (bias selects only, page 3,
-  "the bias selects experts, weights gather pre-bias scores"), weights are
-  the unbiased sigmoid scores renormalised then multiplied by the routed
-  scaling factor;
+* sigmoid gating ranks ``sigmoid(l) + bias`` (page 3, top-k dispatch: the
+  bias only chooses the experts, the weights are taken from the scores
+  before it), weights are the unbiased sigmoid scores renormalised then
+  multiplied by the routed scaling factor;
 * sqrtsoftplus gating (page 3, top-k dispatch: the DeepSeek-V4 scoring
   function, with the same correction bias) scores ``sqrt(softplus(l))``
   with ``softplus(l) = ln(1 + e^l)`` and is otherwise handled like sigmoid;
@@ -30,10 +30,14 @@ notes of the repository):
 * SwiGLU is ``silu(w1 x) * (w3 x)`` with no clamp; the expert intermediate is
   rounded to the GEMM operand format (bf16, or fp8 per row per 128 columns)
   before the down product;
-* each expert's down output is stored in bf16 before the unpermute and
-  weighted reduce (page 3: the grouped prefill bodies all write the same
-  sorted BF16 ``expert_down_out``), for the shared expert too; the fp32
-  layer keeps it in fp32;
+* each expert's down output enters the weighted reduce unrounded: only the
+  operands of the two expert products (x or its fp8 codes, the weights, the
+  rounded intermediate) and the layer output are rounded.  The storage of
+  the per-pair down output between the two steps is accumulator precision,
+  which the output tolerance covers (page 3 keeps it in BF16; one BF16 step
+  of a stored row is a 0.4 % change of a summand, which next to an output
+  that cancels to a tenth of the output rms reads as a several-percent
+  output error, so the reduce takes fp32 rows);
 * the shared expert is added with weight 1 (page 2, ``MoeV41::forward``:
   routed and shared rows are summed into one fp32 accumulator, cleared first),
   or, when the layer has a shared-expert gate vector g, with weight
@@ -61,7 +65,7 @@ class LayerSpec:
     topk: int
     inter: int
     shared_inter: int
-    dtype: str            # "f32" | "bf16" | "fp8" | "mxfp4" | "mxfp8" (MX: weights only; x, h, y bf16)
+    dtype: str            # "f32" | "bf16" | "fp8" | "mxfp4" | "mxfp8" (MX: weights only; x and h bf16)
     gating: str           # "softmax" | "sigmoid" | "sqrtsoftplus"
     routed_scale: float = 1.0
     renormalize: bool = True
@@ -207,40 +211,26 @@ def round_intermediate(a: np.ndarray, dtype: str, block: int):
     return vals, codes, scales
 
 
-def round_down_output(y: np.ndarray, dtype: str) -> np.ndarray:
-    """Storage of an expert's down output before the combine: bf16 (fp32
-    for the fp32 layer)."""
-    if dtype == "f32":
-        return y.astype(np.float32).astype(np.float64)
-    return bf16_round(y)
-
-
 def expert_mlp(a_rows: np.ndarray, w13: np.ndarray, w2: np.ndarray,
-               inter: int, dtype: str, block: int, h_given=None):
+               inter: int, dtype: str, block: int):
     """SwiGLU expert on rows ``a_rows [n, H]`` with exact fp64 weights.
 
     ``w13 [2I, H]`` holds w1 (gate) in rows [0, I) and w3 (up) in [I, 2I);
-    ``w2 [H, I]``.  Returns ``(y [n, H] as stored, h values [n, I], h codes,
+    ``w2 [H, I]``.  Returns ``(y [n, H] unrounded, h values [n, I], h codes,
     h scales, h before rounding)``.
-
-    ``h_given [n, I]``: rounded intermediate values decided elsewhere (the
-    fp8 codes times scales of another implementation); the down product and
-    the storage of y then start from them.
     """
     g = a_rows @ w13[:inter].T
     u = a_rows @ w13[inter:].T
     h = silu(g) * u
     hv, hc, hs = round_intermediate(h, dtype, block)
-    if h_given is not None:
-        hv = np.asarray(h_given, dtype=np.float64)
-    return round_down_output(hv @ w2.T, dtype), hv, hc, hs, h
+    return hv @ w2.T, hv, hc, hs, h
 
 
 # ------------------------------------------------------------------ all ---
 
 def forward(spec: LayerSpec, x, router_w, w13, w2, w13_scale=None,
             w2_scale=None, shared=None, bias=None, tokens=None,
-            idx_override=None, keep_h=False, h_override=None) -> dict:
+            idx_override=None, keep_h=False) -> dict:
     """Oracle forward of the layer.
 
     ``x [m,H]``: bf16 bit patterns (uint16) or fp32.  ``router_w [E,H]``
@@ -257,11 +247,7 @@ def forward(spec: LayerSpec, x, router_w, w13, w2, w13_scale=None,
     probabilities at those indices).  ``keep_h``: also return, per pair p
     (routed) and per token (shared), the intermediate before rounding
     (``h_pre``, ``h_sh_pre``), its rounded values (``h``, ``h_sh``) and, for
-    fp8, its scales (``h_scale``, ``h_sh_scale``).  ``h_override``: a pair
-    ``(routed [te, I] by pair, shared [m, I_s] by token)`` of rounded
-    intermediate values to continue from instead of the oracle's own
-    rounding (a quantised code decided by another implementation, checked
-    first by the caller); either part may be None.
+    fp8, its scales (``h_scale``, ``h_sh_scale``).
 
     Returns a dict with ``logits, prob, score, idx, gap, w, counts, offsets,
     sorted_pair, slot_of_pair, out64 [n,H], out [n,H]`` (rounded to the
@@ -296,7 +282,6 @@ def forward(spec: LayerSpec, x, router_w, w13, w2, w13_scale=None,
     pos_of_tok = {int(t): i for i, t in enumerate(tok)}
     acc = np.zeros((len(tok), H))
     h_rows, h_pre, h_sc = {}, {}, {}
-    h_or, hs_or = (None, None) if h_override is None else h_override
     # routed experts: walk the sorted pairs expert by expert (grouped GEMM).
     for e in range(E):
         seg = sorted_pair[offsets[e]:offsets[e + 1]]
@@ -308,8 +293,7 @@ def forward(spec: LayerSpec, x, router_w, w13, w2, w13_scale=None,
                              spec.dtype, B)
         w2e = weight_values(w2[e], None if w2_scale is None else w2_scale[e],
                             spec.dtype, B)
-        y, hv, _, hs, hp = expert_mlp(xt[rows], w13e, w2e, I, spec.dtype, B,
-                                      None if h_or is None else h_or[seg])
+        y, hv, _, hs, hp = expert_mlp(xt[rows], w13e, w2e, I, spec.dtype, B)
         if keep_h:
             for i, p in enumerate(seg):
                 h_rows[p] = hv[i]
@@ -324,8 +308,7 @@ def forward(spec: LayerSpec, x, router_w, w13, w2, w13_scale=None,
         s13 = weight_values(shared["w13"], shared.get("w13_scale"), spec.dtype, B)
         s2 = weight_values(shared["w2"], shared.get("w2_scale"), spec.dtype, B)
         ysh, hv, _, hs, hp = expert_mlp(xt[tok], s13, s2, spec.shared_inter,
-                                        spec.dtype, B,
-                                        None if hs_or is None else hs_or[tok])
+                                        spec.dtype, B)
         if keep_h:
             res.update(h_sh=hv, h_sh_pre=hp, h_sh_scale=hs)
         if shared.get("gate") is not None:

@@ -9,27 +9,19 @@ Acceptance rules:
 * ``topk_w``: |gpu - oracle| <= 1e-5.
 * permutation (counts, offsets, sorted_pair, slot_of_pair): bit-exact
   against the oracle's permutation of the GPU's ``topk_idx``.
-* ``out``: err = max |o - r| / max(|r|, rms(r)) over the checked tokens,
-  r the unrounded fp64 oracle output: at most 2e-2 (bf16), 4e-2 (fp8),
-  1e-4 (fp32); and the relative L2 error ||o - r|| / ||r|| at most 5e-3,
-  8e-3, 1e-5.  The same maximum with the floor at 0.1 * rms(r) is reported
-  (``out_err_01``) but not gated: the GPU accumulates in fp32 and the
-  oracle in fp64, so a bf16 / fp8 intermediate (h, stored y) now and then
-  lands one unit on the other side of a rounding boundary, and next to an
-  output that cancels to far below the rms that one unit reads as a 5-20 %
-  "relative" error.
-* fp8 SwiGLU codes: the fp8 MFMA of gfx950 does not sum its 128 products
-  in full fp32 (measured: errors up to ~5e-5 of the sum of the products'
-  magnitudes, about 2^-14), so the GPU decides some h codes from a slightly
-  different value than the fp64 oracle.  Where floating point decides a
-  code, both sides must take the decision in the same precision; as for a
-  near-tie top-k choice, the GPU's decision is first checked -- every h
+* ``out``: err = max |o - r| / max(|r|, 0.1 * rms(r)) over the checked
+  tokens, r the unrounded fp64 oracle output (computed from the layer's
+  inputs alone, nothing taken from the GPU besides a near-tie choice): at
+  most 2e-2 (bf16 and the MX formats, whose arithmetic is bf16), 4e-2
+  (fp8), 1e-4 (fp32); and the relative L2 error ||o - r|| / ||r|| at most
+  5e-3, 8e-3, 1e-5.  The same maximum with the floor at rms(r) is reported
+  (``out_err_rms``).
+* fp8 SwiGLU codes and scales (when the debug buffers hold them): every h
   scale within ``H_SCALE_TOL`` of the oracle's amax / 448, every code within
-  one e4m3 step of the oracle's exact quotient (plus ``H_SLACK`` of the row's
-  range), at most ``H_FLIP_FRAC`` of the codes other than the nearest one --
-  and the output maximum error is then measured against the oracle continued
-  from the GPU's codes.  The relative L2 gate always uses the oracle's own
-  codes, and the error against them is reported (``out_err_raw``).
+  one e4m3 step of the oracle's exact quotient (plus ``H_SLACK`` of the
+  row's range), and at most ``H_FLIP_FRAC`` of the codes other than the
+  nearest one.  These check the intermediate on its own; the output gate
+  above does not depend on them.
 """
 from __future__ import annotations
 
@@ -61,10 +53,9 @@ class Report:
     hard_mismatch: int = 0
     max_w_err: float = 0.0
     out_err: float = 0.0
-    out_err_01: float = 0.0
+    out_err_rms: float = 0.0
     out_abs: float = 0.0
     rel_l2: float = 0.0
-    out_err_raw: float = 0.0
     h_checked: int = 0
     h_flips: int = 0
     h_far: int = 0
@@ -107,22 +98,16 @@ def h_decisions(pre: np.ndarray, codes: np.ndarray, scales: np.ndarray, block: i
 
 
 class SortedRows:
-    """Rows of a GPU intermediate kept in sorted (by expert) order, indexed
-    by pair: ``rows[pairs]`` decodes rows ``slot_of_pair[pairs]`` (fp8 codes
-    times their scales) as fp64 values."""
+    """fp8 codes and scales of a GPU intermediate whose rows are kept in
+    sorted (by expert) order: ``rows(pairs)`` are the rows of those pairs
+    (through ``slot_of_pair``; token order when it is None)."""
 
     def __init__(self, codes, scales, slot_of_pair=None, block=128):
         self.codes, self.scales, self.slot, self.block = codes, scales, slot_of_pair, block
 
     def rows(self, idx):
         idx = np.asarray(idx, dtype=np.int64)
-        r = idx if self.slot is None else self.slot[idx]
-        return r
-
-    def __getitem__(self, idx):
-        r = self.rows(idx)
-        return e4m3_decode(self.codes[r]) * np.repeat(self.scales[r].astype(np.float64),
-                                                      self.block, axis=1)
+        return idx if self.slot is None else self.slot[idx]
 
 
 def check_layer(wl, inp, out, topk_idx, topk_w, tokens=None, debug=None,
@@ -163,17 +148,16 @@ def check_layer(wl, inp, out, topk_idx, topk_w, tokens=None, debug=None,
     r = ref_out["out64"]
     rms = float(np.sqrt(np.mean(r ** 2))) if r.size else 0.0
     rep.tokens_checked = len(tok)
-    rep.out_err_raw = rep.out_err = out_error(o, r, rms)
-    rep.out_err_01 = out_error(o, r, 0.1 * rms)
+    rep.out_err = out_error(o, r, 0.1 * rms)
+    rep.out_err_rms = out_error(o, r, rms)
     rep.rel_l2 = float(np.linalg.norm(o - r) / max(np.linalg.norm(r), 1e-300))
+    rep.out_abs = float(np.abs(o - r).max(initial=0.0))
     if want_h:
-        # fp8: check the GPU's h decisions, then measure the output against
-        # the oracle continued from them
+        # fp8: the GPU's h codes and scales against the oracle's exact values
         slot = to_np(debug["slot_of_pair"]).astype(np.int64)
         routed = SortedRows(to_np(debug["h"]), to_np(debug["h_scale"]), slot, wl.block)
         pairs = sorted(ref_out["h_pre"])
         parts = [(np.stack([ref_out["h_pre"][p] for p in pairs]), routed.rows(pairs), routed)] if pairs else []
-        shared = None
         if wl.shared_inter > 0 and "h_shared" in debug:
             shared = SortedRows(to_np(debug["h_shared"]), to_np(debug["h_shared_scale"]), None, wl.block)
             parts.append((ref_out["h_sh_pre"], tok, shared))
@@ -189,10 +173,6 @@ def check_layer(wl, inp, out, topk_idx, topk_w, tokens=None, debug=None,
             rep.failures.append(f"{rep.h_far} h codes farther than one e4m3 step from the exact value")
         if rep.h_flips > H_FLIP_FRAC * max(rep.h_checked, 1):
             rep.failures.append(f"{rep.h_flips} of {rep.h_checked} h codes not the nearest one")
-        dec = OL.forward(spec, **args, tokens=tokens, idx_override=g_idx, h_override=(routed, shared))
-        rep.out_err = out_error(o, dec["out64"], rms)
-        r = dec["out64"]
-    rep.out_abs = float(np.abs(o - r).max(initial=0.0))
     if not np.all(np.isfinite(o)):
         rep.failures.append("non-finite output")
     tol = OUT_TOL[wl.dtype]

@@ -75,3 +75,20 @@ def test_a_wrong_output_fails():
     o[4, 9] += 0.1 * float(o.abs().max())
     rep = check_layer(WL, inp, o.to(torch.bfloat16), idx, w, debug=dbg)
     assert not rep.ok()
+
+
+def test_a_small_error_at_a_cancelling_output_fails():
+    """The relative error is floored at a tenth of the output rms, not at the
+    rms: an error of 5 % of 0.1 rms at an output below 0.1 rms fails the fp8
+    bound (4e-2) although it is only 0.5 % of the rms."""
+    inp = synth.make_inputs(WL)
+    out, idx, w, dbg = _as_gpu(WL, inp)
+    spec, args = oracle_inputs(WL, inp)
+    r = OL.forward(spec, **args)["out64"]
+    rms = float(np.sqrt(np.mean(r ** 2)))
+    t, c = np.unravel_index(np.argmin(np.abs(r)), r.shape)
+    o = torch.from_numpy(r).clone()
+    o[t, c] = r[t, c] + 0.05 * 0.1 * rms
+    rep = check_layer(WL, inp, o.float(), idx, w)
+    assert rep.out_err_rms < 4e-2 < rep.out_err
+    assert any("output error" in f for f in rep.failures)
