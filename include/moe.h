@@ -163,9 +163,8 @@ typedef struct {
   void *events[MOE_NUM_STAGES + 1];
   void *h_shared;         /* [m, I_s] shared-expert SwiGLU output, as h     */
   float *h_shared_scale;  /* [m, I_s/128] its scales (FP8 weights only)     */
-  void *y;                /* [te, H] routed down output, sorted rows: bf16
-                             (fp32 for F32 weights)                          */
-  void *y_shared;         /* [m, H] shared-expert down output, as y         */
+  float *y;               /* [te, H] routed down output, sorted rows, fp32  */
+  float *y_shared;        /* [m, H] shared-expert down output, fp32         */
 } moe_debug_t;
 
 /* Validate cfg and create a plan (host memory only; no device work).

@@ -11,7 +11,8 @@
 // forward_prefill.rs (page 3, step 7 "Unpermute + weighted reduce") gathers
 // each token's sorted expert rows through the token-to-slot map and applies
 // the gate weights; forward.rs (page 2, MoeV41::forward) sums routed and
-// shared rows into one fp32 accumulator and rounds once.  Here the sum runs
+// shared rows into one fp32 accumulator and rounds once.  Here the expert
+// rows arrive in fp32 (unrounded since their down product) and the sum runs
 // in fp32 in a fixed order (j ascending, then the shared row) with no
 // atomics, so two calls give bit-identical outputs.
 #include "common.h"
@@ -59,10 +60,10 @@ __device__ __forceinline__ float shared_gate_factor(const void *x, const void *g
   return 1.0f / (1.0f + expf(-dot));
 }
 
-// One block per token row chunk; 8 columns per thread (16-byte y loads).
+// One block per token row chunk; 8 columns per thread (two 16-byte y loads).
 template <bool F32>
 __global__ __launch_bounds__(256) void combine_kernel(
-    const void *__restrict__ y, const void *__restrict__ y_sh,
+    const float *__restrict__ y, const float *__restrict__ y_sh,
     const int *__restrict__ slot_of_pair, const float *__restrict__ topk_w,
     const void *__restrict__ x, const void *__restrict__ sgate,
     int m, int H, int k, void *__restrict__ out) {
@@ -78,13 +79,13 @@ __global__ __launch_bounds__(256) void combine_kernel(
     const float wj = topk_w[static_cast<size_t>(t) * k + j];
     const size_t row = static_cast<size_t>(slot_of_pair[static_cast<size_t>(t) * k + j]);
     float v[8];
-    load8<F32>(y, row * H + n0, v);
+    load8<true>(y, row * H + n0, v);
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = fmaf(wj, v[i], acc[i]);
   }
   if (y_sh) {
     float v[8];
-    load8<F32>(y_sh, static_cast<size_t>(t) * H + n0, v);
+    load8<true>(y_sh, static_cast<size_t>(t) * H + n0, v);
     if (sgate) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc[i] = fmaf(gsh, v[i], acc[i]);
@@ -111,7 +112,7 @@ hipError_t launch_combine(const Dims &d, const Inputs &in, const Work &w, const 
                           const float *topk_w, void *out, hipStream_t s) {
   (void)topk_idx;
   const dim3 grid((d.H / 8 + 255) / 256, d.m);
-  const void *ysh = d.Is > 0 ? w.y_sh : nullptr;
+  const float *ysh = d.Is > 0 ? w.y_sh : nullptr;
   const void *sg = d.Is > 0 ? in.sgate : nullptr;
   if (d.wdt == kF32)
     hipLaunchKernelGGL(combine_kernel<true>, grid, dim3(256), 0, s, w.y, ysh,

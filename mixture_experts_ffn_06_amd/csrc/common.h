@@ -46,6 +46,17 @@ __device__ __forceinline__ int fp8_pack2(float a, float b) {
   return __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
 }
 
+// Eight e4m3fn codes (two 32-bit words, lowest byte first) as their exact
+// bf16 values: every e4m3 value, subnormals included, is a bf16 value, and a
+// scale operand of 1.0 leaves the conversion unscaled.
+__device__ __forceinline__ bf16x8_t e4m3x8_to_bf16(uint32_t lo, uint32_t hi) {
+  const bf16x2_t q0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
+  const bf16x2_t q1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
+  const bf16x2_t q2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
+  const bf16x2_t q3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
+  return bf16x8_t{q0[0], q0[1], q1[0], q1[1], q2[0], q2[1], q3[0], q3[1]};
+}
+
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
 __device__ __forceinline__ float wave_max(float v) {

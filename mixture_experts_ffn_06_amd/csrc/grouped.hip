@@ -420,8 +420,11 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void grouped_kernel(GroupedArgs a)
       }
     };
 
-    // fp8 stage st, operands read and multiplied in two halves of the weight
-    // blocks (8 blocks of operands do not fit next to 128 accumulators)
+    // fp8 stage st: e4m3 operands read from LDS, converted to their exact
+    // bf16 values in registers and multiplied on the bf16 MFMA (gfx950's fp8
+    // MFMA does not sum its products in full fp32: it drops product bits
+    // below ~2^-14 of the largest product in each group of eight, enough to
+    // move SwiGLU codes across rounding boundaries)
     auto compute_fp8 = [&](int st) {
       if constexpr (C::SCALED) {
         const uint8_t *sa = lds + (st % C::DA) * C::A_BYTES;
@@ -463,10 +466,18 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void grouped_kernel(GroupedArgs a)
           const uint32_t lb = lb0 + j0 * BLK;
           lds_read4<0, 0, BLK, BLK>(lb, lb + d1, lb, lb + d1, bq[0], bq[1], bq[2], bq[3]);
           lds_read4<2 * BLK, 2 * BLK, 3 * BLK, 3 * BLK>(lb, lb + d1, lb, lb + d1, bq[4], bq[5], bq[6], bq[7]);
+          // weight blocks as bf16 (exact), [block][step of 8 K elements]
+          bf16x8_t bv[4][4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              bv[j][2 * h] = e4m3x8_to_bf16(bq[2 * j + h].x, bq[2 * j + h].y);
+              bv[j][2 * h + 1] = e4m3x8_to_bf16(bq[2 * j + h].z, bq[2 * j + h].w);
+            }
 #pragma unroll
           for (int mb = 0; mb < MBW; ++mb) {
             if (mrow(mb) >= nmb) continue;   // no rows in this m-block
-            const i32x8_t av = as_i32x8(aq[2 * mb], aq[2 * mb + 1]);
             // row scale x weight-block scale, once per scale group: the
             // wave's blocks are 16 * NB <= 64 consecutive 16-aligned output
             // columns, so its gate blocks share one 128-row weight-scale
@@ -480,14 +491,28 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void grouped_kernel(GroupedArgs a)
 #pragma unroll
               for (int i = 0; i < 4; ++i) sc[gi][i] = __uint_as_float(sv[mb][i]) * ws;
             }
+            // the lane's 32 K elements as four bf16 steps of 8 (exact), four
+            // 16x16x32 bf16 MFMAs per weight block from zero, then the
+            // two-level accumulation
+            bf16x8_t av[4];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              av[2 * h] = e4m3x8_to_bf16(aq[2 * mb + h].x, aq[2 * mb + h].y);
+              av[2 * h + 1] = e4m3x8_to_bf16(aq[2 * mb + h].z, aq[2 * mb + h].w);
+            }
+            f32x4_t p[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) p[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+              for (int j = 0; j < 4; ++j)
+                p[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[ks], bv[j][ks], p[j], 0, 0, 0);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-              const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
-              const f32x4_t p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                  av, as_i32x8(bq[2 * j], bq[2 * j + 1]), z, 0, 0, 0, 127, 0, 127);
               const int gi = (j0 + j) / (NB / NG);
 #pragma unroll
-              for (int i = 0; i < 4; ++i) acc[mb][j0 + j][i] = fmaf(p[i], sc[gi][i], acc[mb][j0 + j][i]);
+              for (int i = 0; i < 4; ++i) acc[mb][j0 + j][i] = fmaf(p[j][i], sc[gi][i], acc[mb][j0 + j][i]);
             }
           }
         }
@@ -628,8 +653,7 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void grouped_kernel(GroupedArgs a)
         }
       }
     } else {
-      uint16_t *ybase = static_cast<uint16_t *>(shared ? a.w.y_sh : a.w.y) +
-                        static_cast<size_t>(seg0 + row0) * d.H;
+      float *ybase = (shared ? a.w.y_sh : a.w.y) + static_cast<size_t>(seg0 + row0) * d.H;
 #pragma unroll
       for (int mb = 0; mb < MBW; ++mb) {
 #pragma unroll
@@ -639,7 +663,7 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void grouped_kernel(GroupedArgs a)
 #pragma unroll
             for (int j = 0; j < NB; ++j)
               if (col0 + 16 * j < ncol_lim)
-                ybase[static_cast<size_t>(rr) * d.H + col0 + 16 * j + cl] = f32_to_bf16(acc[mb][j][i]);
+                ybase[static_cast<size_t>(rr) * d.H + col0 + 16 * j + cl] = acc[mb][j][i];
           }
         }
       }
@@ -681,8 +705,7 @@ hipError_t launch_grouped_gateup(const Dims &d, const Inputs &in,
   }
   // fp8: 128 h columns = one h scale group (4 column waves x 2 gate + 2 up
   // blocks; 4 x 4 block tiles per wave keep the scale promotion cheap)
-  if (big_tiles(d)) return launch_one<kFP8, kGateUp, 4, 4, 2, 6, 3, 128>(ga, s);   // 192 rows, 8 waves
-  return launch_one<kFP8, kGateUp, 4, 4, 2, 4, 3, 128>(ga, s);                     // 128 rows, 8 waves
+  return launch_one<kFP8, kGateUp, 4, 4, 2, 4, 3, 128>(ga, s);   // 128 rows, 8 waves
 }
 
 hipError_t launch_grouped_down(const Dims &d, const Inputs &in, const Work &w,
@@ -694,8 +717,7 @@ hipError_t launch_grouped_down(const Dims &d, const Inputs &in, const Work &w,
     ga.order = kOrderSharedFirst;
     return launch_one<kBF16, kDown, 4, 4, 1, 6, 4, 64>(ga, s);
   }
-  // 192 (128) rows x 256 columns, 8 waves
-  if (big_tiles(d)) return launch_one<kFP8, kDown, 4, 4, 2, 6, 3, 128>(ga, s);
+  // 128 rows x 256 columns, 8 waves
   return launch_one<kFP8, kDown, 4, 4, 2, 4, 3, 128>(ga, s);
 }
 

@@ -57,8 +57,8 @@ struct Work {
   float *h_scale;       // [te,I/128]
   void *h_sh;           // [m,Is]  shared SwiGLU output
   float *h_sh_scale;    // [m,Is/128]
-  void *y;              // [te,H]  routed down output (sorted rows)
-  void *y_sh;           // [m,H]   shared down output
+  float *y;             // [te,H]  routed down output (sorted rows), fp32
+  float *y_sh;          // [m,H]   shared down output, fp32
 };
 
 // permute.hip: one block below kPermMultiMin pairs, else chunks of

@@ -84,7 +84,7 @@ Layout layout(const moe_plan_s &p, int m) {
   const size_t te = static_cast<size_t>(m) * c.topk;
   const bool fp8 = c.weight_dtype == MOE_FP8_E4M3;
   const size_t hb = c.weight_dtype == MOE_F32 ? 4 : (fp8 ? 1 : 2);
-  const size_t yb = c.weight_dtype == MOE_F32 ? 4 : 2;
+  const size_t yb = 4;   // expert down outputs reach the combine in fp32
   Layout L;
   L.size[Layout::kLogits] = m * E * 4;
   L.size[Layout::kRpart] = m <= 16 ? static_cast<size_t>(moe::kRouterMaxSplits) * m * E * 4 : 0;
@@ -133,8 +133,8 @@ moe::Work carve(const Layout &L, void *ws) {
   w.h_scale = static_cast<float *>(at(Layout::kHs));
   w.h_sh = at(Layout::kHsh);
   w.h_sh_scale = static_cast<float *>(at(Layout::kHshs));
-  w.y = at(Layout::kY);
-  w.y_sh = at(Layout::kYsh);
+  w.y = static_cast<float *>(at(Layout::kY));
+  w.y_sh = static_cast<float *>(at(Layout::kYsh));
   return w;
 }
 

@@ -60,7 +60,7 @@ struct RowInfo {
   int inter;        // I'
   void *h;          // h row base
   float *hs;        // h scale row base
-  void *y;          // y row base
+  float *y;         // y row base (fp32)
 };
 
 template <int DT>
@@ -69,7 +69,6 @@ __device__ __forceinline__ RowInfo row_info(const Dims &d, const Inputs &in,
   RowInfo r;
   // bytes per weight element (MXFP4: half a byte, counted per expert below)
   constexpr int B = is_mx(DT) ? 2 : StorageBytes<DT>::value;   // h element bytes
-  const int yb = DT == kF32 ? 4 : 2;
   if (s < d.te) {
     const int e = expert_of_row(w.offsets, d.E, s);
     r.t = w.sorted_pair[s] / d.k;
@@ -87,7 +86,7 @@ __device__ __forceinline__ RowInfo row_info(const Dims &d, const Inputs &in,
     }
     r.h = static_cast<char *>(w.h) + static_cast<size_t>(s) * d.I * B;
     r.hs = DT == kFP8 ? w.h_scale + static_cast<size_t>(s) * (d.I / kQBlock) : nullptr;
-    r.y = static_cast<char *>(w.y) + static_cast<size_t>(s) * d.H * yb;
+    r.y = w.y + static_cast<size_t>(s) * d.H;
   } else {
     r.t = s - d.te;
     r.inter = d.Is;
@@ -97,7 +96,7 @@ __device__ __forceinline__ RowInfo row_info(const Dims &d, const Inputs &in,
     r.s2 = in.sw2_scale;
     r.h = static_cast<char *>(w.h_sh) + static_cast<size_t>(r.t) * d.Is * B;
     r.hs = DT == kFP8 ? w.h_sh_scale + static_cast<size_t>(r.t) * (d.Is / kQBlock) : nullptr;
-    r.y = static_cast<char *>(w.y_sh) + static_cast<size_t>(r.t) * d.H * yb;
+    r.y = w.y_sh + static_cast<size_t>(r.t) * d.H;
   }
   return r;
 }
@@ -193,10 +192,7 @@ __global__ __launch_bounds__(256) void simple_down_kernel(Dims d, Inputs in, Wor
     for (int j = 0; j < K; ++j)
       acc = fmaf(load_as_f32<DT>(r.h, j), load_as_f32<DT>(r.w2, rw + j), acc);
   }
-  if constexpr (DT == kF32)
-    static_cast<float *>(r.y)[n] = acc;
-  else
-    static_cast<uint16_t *>(r.y)[n] = f32_to_bf16(acc);
+  r.y[n] = acc;
 }
 
 template <int DT>

@@ -242,7 +242,7 @@ __global__ __launch_bounds__(kSmBlockWaves * kWave) void sm_kernel(Dims d, Input
       }
     }
   } else {
-    uint16_t *y = static_cast<uint16_t *>(shared ? w.y_sh : w.y) + static_cast<size_t>(seg0) * d.H;
+    float *y = (shared ? w.y_sh : w.y) + static_cast<size_t>(seg0) * d.H;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = (lane >> 4) * 4 + i;
@@ -250,7 +250,7 @@ __global__ __launch_bounds__(kSmBlockWaves * kWave) void sm_kernel(Dims d, Input
 #pragma unroll
         for (int j = 0; j < NBLK; ++j)
           if (c0 + 16 * j < ncol)
-            y[static_cast<size_t>(row) * d.H + c0 + 16 * j + cl] = f32_to_bf16(acc[j][i]);
+            y[static_cast<size_t>(row) * d.H + c0 + 16 * j + cl] = acc[j][i];
       }
     }
   }
@@ -574,7 +574,7 @@ __global__ __launch_bounds__(kSmBlockWaves * kWave, NB == 2 ? 4 : 2) void sm_mx_
       }
     }
   } else {
-    uint16_t *y = static_cast<uint16_t *>(shared ? w.y_sh : w.y) + static_cast<size_t>(seg0) * d.H;
+    float *y = (shared ? w.y_sh : w.y) + static_cast<size_t>(seg0) * d.H;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = (lane >> 4) * 4 + i;
@@ -582,7 +582,7 @@ __global__ __launch_bounds__(kSmBlockWaves * kWave, NB == 2 ? 4 : 2) void sm_mx_
 #pragma unroll
         for (int j = 0; j < NB; ++j)
           if (c0 + 16 * j < ncol)
-            y[static_cast<size_t>(row) * d.H + c0 + 16 * j + cl] = f32_to_bf16(acc[j][i]);
+            y[static_cast<size_t>(row) * d.H + c0 + 16 * j + cl] = acc[j][i];
       }
     }
   }

@@ -212,17 +212,26 @@ def round_intermediate(a: np.ndarray, dtype: str, block: int):
 
 
 def expert_mlp(a_rows: np.ndarray, w13: np.ndarray, w2: np.ndarray,
-               inter: int, dtype: str, block: int):
+               inter: int, dtype: str, block: int, h_ties=None):
     """SwiGLU expert on rows ``a_rows [n, H]`` with exact fp64 weights.
 
     ``w13 [2I, H]`` holds w1 (gate) in rows [0, I) and w3 (up) in [I, 2I);
     ``w2 [H, I]``.  Returns ``(y [n, H] unrounded, h values [n, I], h codes,
     h scales, h before rounding)``.
+
+    ``h_ties``: optional ``(rows, cols, values)`` -- rounded intermediate
+    values taken at near-ties: where the exact value lies next to the
+    midpoint of two neighbouring codes, either code is a correct rounding,
+    and the down product then continues from the one given (the caller
+    checks that each given value is the other neighbour of such a tie).
     """
     g = a_rows @ w13[:inter].T
     u = a_rows @ w13[inter:].T
     h = silu(g) * u
     hv, hc, hs = round_intermediate(h, dtype, block)
+    if h_ties is not None and len(h_ties[0]):
+        hv = hv.copy()
+        hv[h_ties[0], h_ties[1]] = h_ties[2]
     return hv @ w2.T, hv, hc, hs, h
 
 
@@ -230,7 +239,7 @@ def expert_mlp(a_rows: np.ndarray, w13: np.ndarray, w2: np.ndarray,
 
 def forward(spec: LayerSpec, x, router_w, w13, w2, w13_scale=None,
             w2_scale=None, shared=None, bias=None, tokens=None,
-            idx_override=None, keep_h=False) -> dict:
+            idx_override=None, keep_h=False, h_ties=None) -> dict:
     """Oracle forward of the layer.
 
     ``x [m,H]``: bf16 bit patterns (uint16) or fp32.  ``router_w [E,H]``
@@ -247,7 +256,11 @@ def forward(spec: LayerSpec, x, router_w, w13, w2, w13_scale=None,
     probabilities at those indices).  ``keep_h``: also return, per pair p
     (routed) and per token (shared), the intermediate before rounding
     (``h_pre``, ``h_sh_pre``), its rounded values (``h``, ``h_sh``) and, for
-    fp8, its scales (``h_scale``, ``h_sh_scale``).
+    fp8, its scales (``h_scale``, ``h_sh_scale``).  ``h_ties``: near-tie
+    choices of the rounded intermediate, ``(routed, shared)`` with ``routed``
+    a dict pair -> ``(cols, values)`` and ``shared`` a dict token -> ``(cols,
+    values)`` (see ``expert_mlp``); like ``idx_override`` for a top-k
+    near-tie, they select between two correct roundings.
 
     Returns a dict with ``logits, prob, score, idx, gap, w, counts, offsets,
     sorted_pair, slot_of_pair, out64 [n,H], out [n,H]`` (rounded to the
@@ -293,7 +306,17 @@ def forward(spec: LayerSpec, x, router_w, w13, w2, w13_scale=None,
                              spec.dtype, B)
         w2e = weight_values(w2[e], None if w2_scale is None else w2_scale[e],
                             spec.dtype, B)
-        y, hv, _, hs, hp = expert_mlp(xt[rows], w13e, w2e, I, spec.dtype, B)
+        ties = None
+        if h_ties is not None and h_ties[0]:
+            tr, tc, tv = [], [], []
+            for i, p in enumerate(seg):
+                if p in h_ties[0]:
+                    cols, vals = h_ties[0][p]
+                    tr += [i] * len(cols)
+                    tc += list(cols)
+                    tv += list(vals)
+            ties = (np.array(tr, dtype=np.int64), np.array(tc, dtype=np.int64), np.array(tv))
+        y, hv, _, hs, hp = expert_mlp(xt[rows], w13e, w2e, I, spec.dtype, B, ties)
         if keep_h:
             for i, p in enumerate(seg):
                 h_rows[p] = hv[i]
@@ -307,8 +330,18 @@ def forward(spec: LayerSpec, x, router_w, w13, w2, w13_scale=None,
     if shared is not None and spec.shared_inter > 0:
         s13 = weight_values(shared["w13"], shared.get("w13_scale"), spec.dtype, B)
         s2 = weight_values(shared["w2"], shared.get("w2_scale"), spec.dtype, B)
+        ties = None
+        if h_ties is not None and h_ties[1]:
+            tr, tc, tv = [], [], []
+            for i, t in enumerate(tok):
+                if int(t) in h_ties[1]:
+                    cols, vals = h_ties[1][int(t)]
+                    tr += [i] * len(cols)
+                    tc += list(cols)
+                    tv += list(vals)
+            ties = (np.array(tr, dtype=np.int64), np.array(tc, dtype=np.int64), np.array(tv))
         ysh, hv, _, hs, hp = expert_mlp(xt[tok], s13, s2, spec.shared_inter,
-                                        spec.dtype, B)
+                                        spec.dtype, B, ties)
         if keep_h:
             res.update(h_sh=hv, h_sh_pre=hp, h_sh_scale=hs)
         if shared.get("gate") is not None:

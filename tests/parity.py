@@ -16,12 +16,19 @@ Acceptance rules:
   (fp8), 1e-4 (fp32); and the relative L2 error ||o - r|| / ||r|| at most
   5e-3, 8e-3, 1e-5.  The same maximum with the floor at rms(r) is reported
   (``out_err_rms``).
-* fp8 SwiGLU codes and scales (when the debug buffers hold them): every h
-  scale within ``H_SCALE_TOL`` of the oracle's amax / 448, every code within
-  one e4m3 step of the oracle's exact quotient (plus ``H_SLACK`` of the
-  row's range), and at most ``H_FLIP_FRAC`` of the codes other than the
-  nearest one.  These check the intermediate on its own; the output gate
-  above does not depend on them.
+* fp8 SwiGLU codes (when the debug buffers hold them) are decisions taken
+  by floating point: each is the rounding of a value that the GPU forms in
+  fp32 and the oracle in fp64.  Where the exact value lies within ``H_TIE``
+  (relative) of the midpoint between two neighbouring e4m3 codes, both
+  codes are correct roundings and the two sides may differ.  Such codes are
+  treated like a near-tie top-k choice: counted (``h_ties``), and the
+  output is then compared with the oracle rerun with the GPU's choice at
+  exactly those codes (expressed in the oracle's own scale); every other
+  code and every output element is compared with the oracle computed from
+  the inputs alone.  A code that differs from the oracle's away from such a
+  tie is counted as ``h_hard`` and left to the output gate; the error
+  against the unconditioned oracle is reported as ``out_err_raw``.  Every
+  GPU h scale must lie within ``H_SCALE_TOL`` of the oracle's.
 """
 from __future__ import annotations
 
@@ -40,9 +47,8 @@ W_TOL = 1e-5
 # bounds apply
 OUT_TOL = {"f32": 1e-4, "bf16": 2e-2, "fp8": 4e-2, "mxfp4": 2e-2, "mxfp8": 2e-2}
 L2_TOL = {"f32": 1e-5, "bf16": 5e-3, "fp8": 8e-3, "mxfp4": 5e-3, "mxfp8": 5e-3}
-H_SCALE_TOL = 1e-3     # relative, GPU h scale vs the oracle's amax / 448
-H_SLACK = 1e-3         # of the code range (448), beyond one e4m3 step
-H_FLIP_FRAC = 1e-2     # codes allowed to differ from the nearest one
+H_SCALE_TOL = 1e-5     # relative, GPU h scale vs the oracle's amax / 448
+H_TIE = 1e-5           # relative distance of an exact quotient from a code midpoint
 
 
 @dataclass
@@ -56,9 +62,10 @@ class Report:
     out_err_rms: float = 0.0
     out_abs: float = 0.0
     rel_l2: float = 0.0
+    out_err_raw: float = 0.0
     h_checked: int = 0
-    h_flips: int = 0
-    h_far: int = 0
+    h_ties: int = 0
+    h_hard: int = 0
     h_scale_rel: float = 0.0
     failures: list = field(default_factory=list)
 
@@ -77,24 +84,35 @@ def gpu_out_values(out: torch.Tensor) -> np.ndarray:
     return out.detach().float().cpu().numpy().astype(np.float64)
 
 
-def h_decisions(pre: np.ndarray, codes: np.ndarray, scales: np.ndarray, block: int = 128):
-    """Check fp8 codes and scales decided by the GPU for rows whose exact
-    (fp64 oracle) values before rounding are ``pre``.
+def h_compare(pre, o_vals, o_scales, g_codes, g_scales, block: int = 128):
+    """Compare the GPU's fp8 codes of some h rows with the oracle's.
 
-    Returns ``(max relative scale error, codes farther than one e4m3 step
-    (+ slack) from the exact quotient, codes other than the nearest one)``.
+    ``pre [n, I]``: exact (fp64) values before rounding; ``o_vals``,
+    ``o_scales``: the oracle's rounded values and scales; ``g_codes``,
+    ``g_scales``: the GPU's codes and scales of the same rows.  Returns
+    ``(max relative scale difference, ties, hard)``: ``ties`` a list of
+    ``(row, col, value)`` -- codes where the two sides differ at a near-tie,
+    with the GPU's code in the oracle's scale -- and ``hard`` the number of
+    differing codes away from a tie.
     """
     n, I = pre.shape
-    s = scales.astype(np.float64)
-    amax = np.abs(pre).reshape(n, I // block, block).max(axis=2)
-    s_or = np.where(amax > 0, (amax.astype(np.float32) / np.float32(448.0)).astype(np.float64), 1.0)
-    srel = float((np.abs(s - s_or) / s_or).max(initial=0.0))
-    q = np.clip(pre / np.repeat(s, block, axis=1), -448.0, 448.0)
-    cv = e4m3_decode(codes)
-    step = np.exp2(np.floor(np.log2(np.maximum(np.abs(q), 2.0 ** -6))) - 3)
-    far = int((np.abs(cv - q) > step + H_SLACK * 448.0).sum())
-    flips = int((cv != e4m3_decode(e4m3_encode(q))).sum())
-    return srel, far, flips
+    so = np.repeat(np.asarray(o_scales, np.float64).reshape(n, -1), block, axis=1)
+    sg = np.asarray(g_scales, np.float64).reshape(n, -1)
+    srel = float((np.abs(sg - so[:, ::block]) / so[:, ::block]).max(initial=0.0))
+    oc = e4m3_decode(e4m3_encode((o_vals / so).astype(np.float32)))   # oracle code values
+    gc = e4m3_decode(g_codes)
+    diff = oc != gc
+    q = pre / so
+    mid = 0.5 * (oc + gc)
+    step = np.abs(oc - gc)
+    # a tie: q lies between the two codes, within H_TIE of their midpoint
+    # (the oracle's code being the nearest to q, the two are then neighbours)
+    lo, hi = np.minimum(oc, gc), np.maximum(oc, gc)
+    inside = (q >= lo) & (q <= hi)
+    tie = diff & inside & (np.abs(q - mid) <= H_TIE * np.abs(q) + H_TIE * 2.0 ** -9) & (step > 0)
+    r, c = np.nonzero(tie)
+    ties = [(int(i), int(j), float(gc[i, j] * so[i, j])) for i, j in zip(r, c)]
+    return srel, ties, int((diff & ~tie).sum())
 
 
 class SortedRows:
@@ -152,27 +170,46 @@ def check_layer(wl, inp, out, topk_idx, topk_w, tokens=None, debug=None,
     rep.out_err_rms = out_error(o, r, rms)
     rep.rel_l2 = float(np.linalg.norm(o - r) / max(np.linalg.norm(r), 1e-300))
     rep.out_abs = float(np.abs(o - r).max(initial=0.0))
+    rep.out_err_raw = rep.out_err
     if want_h:
-        # fp8: the GPU's h codes and scales against the oracle's exact values
+        # fp8: the GPU's h codes against the oracle's; near-ties as choices
         slot = to_np(debug["slot_of_pair"]).astype(np.int64)
         routed = SortedRows(to_np(debug["h"]), to_np(debug["h_scale"]), slot, wl.block)
         pairs = sorted(ref_out["h_pre"])
-        parts = [(np.stack([ref_out["h_pre"][p] for p in pairs]), routed.rows(pairs), routed)] if pairs else []
+        ties_r, ties_s = {}, {}
+        if pairs:
+            rows = routed.rows(pairs)
+            srel, ties, hard = h_compare(np.stack([ref_out["h_pre"][p] for p in pairs]),
+                                         np.stack([ref_out["h"][p] for p in pairs]),
+                                         np.stack([ref_out["h_scale"][p] for p in pairs]),
+                                         routed.codes[rows], routed.scales[rows], wl.block)
+            rep.h_scale_rel, rep.h_hard = srel, hard
+            rep.h_checked += len(pairs) * wl.inter
+            for i, c, v in ties:
+                cols, vals = ties_r.setdefault(pairs[i], ([], []))
+                cols.append(c)
+                vals.append(v)
         if wl.shared_inter > 0 and "h_shared" in debug:
-            shared = SortedRows(to_np(debug["h_shared"]), to_np(debug["h_shared_scale"]), None, wl.block)
-            parts.append((ref_out["h_sh_pre"], tok, shared))
-        for pre, rows, src in parts:
-            srel, far, flips = h_decisions(pre, src.codes[rows], src.scales[rows], wl.block)
-            rep.h_scale_rel = max(rep.h_scale_rel, srel)
-            rep.h_far += far
-            rep.h_flips += flips
-            rep.h_checked += pre.size
+            codes, scales = to_np(debug["h_shared"]), to_np(debug["h_shared_scale"])
+            srel, ties, hard = h_compare(ref_out["h_sh_pre"], ref_out["h_sh"], ref_out["h_sh_scale"],
+                                         codes[tok], scales[tok], wl.block)
+            rep.h_scale_rel, rep.h_hard = max(rep.h_scale_rel, srel), rep.h_hard + hard
+            rep.h_checked += len(tok) * wl.shared_inter
+            for i, c, v in ties:
+                cols, vals = ties_s.setdefault(int(tok[i]), ([], []))
+                cols.append(c)
+                vals.append(v)
+        rep.h_ties = sum(len(v[0]) for v in ties_r.values()) + sum(len(v[0]) for v in ties_s.values())
         if rep.h_scale_rel > H_SCALE_TOL:
             rep.failures.append(f"h scale error {rep.h_scale_rel:.3g} > {H_SCALE_TOL}")
-        if rep.h_far:
-            rep.failures.append(f"{rep.h_far} h codes farther than one e4m3 step from the exact value")
-        if rep.h_flips > H_FLIP_FRAC * max(rep.h_checked, 1):
-            rep.failures.append(f"{rep.h_flips} of {rep.h_checked} h codes not the nearest one")
+        if rep.h_ties:
+            cond = OL.forward(spec, **args, tokens=tokens,
+                              idx_override=g_idx if rep.near_tie_mismatch else None,
+                              h_ties=(ties_r, ties_s))
+            r = cond["out64"]
+            rep.out_err = out_error(o, r, 0.1 * rms)
+            rep.out_err_rms = out_error(o, r, rms)
+            rep.out_abs = float(np.abs(o - r).max(initial=0.0))
     if not np.all(np.isfinite(o)):
         rep.failures.append("non-finite output")
     tol = OUT_TOL[wl.dtype]

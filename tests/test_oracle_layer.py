@@ -385,6 +385,25 @@ def test_kept_h_rounds_the_pre_rounding_values():
                       np.stack([r["h_scale"][p] for p in range(te)]), 128, axis=1))
 
 
+def test_h_ties_with_own_values_are_the_identity():
+    """A near-tie choice equal to the oracle's own rounded value changes
+    nothing; the neighbouring code at one position changes the output of
+    that pair's token only."""
+    wl = synth.Workload("ties", m=9, hidden=256, experts=5, topk=2, inter=256,
+                        shared_inter=128, dtype="fp8", gating="sigmoid",
+                        routed_scale=2.5, seed=13)
+    inp = synth.make_inputs(wl)
+    spec, args = oracle_inputs(wl, inp)
+    r = OL.forward(spec, **args, keep_h=True)
+    p, c = 5, 17
+    same = OL.forward(spec, **args, h_ties=({p: ([c], [r["h"][p][c]])}, {3: ([4], [r["h_sh"][3][4]])}))
+    assert np.array_equal(same["out64"], r["out64"])
+    other = r["h"][p][c] * (1 + 2.0 ** -3)
+    moved = OL.forward(spec, **args, h_ties=({p: ([c], [other])}, {}))
+    changed = np.nonzero(np.any(moved["out64"] != r["out64"], axis=1))[0]
+    assert changed.tolist() == [p // wl.topk]
+
+
 # ---------------------------------------------------------- symmetries ---
 
 def test_token_permutation_equivariance():

@@ -7,7 +7,8 @@ import oracle.layer as OL
 import synth
 from oracle.codec import bf16_encode, e4m3_encode
 from tests.conftest import oracle_inputs
-from tests.parity import check_layer
+from oracle.codec import e4m3_decode as dec, e4m3_encode as enc
+from tests.parity import check_layer, h_compare
 
 WL = synth.Workload("rules_fp8", m=12, hidden=256, experts=6, topk=2, inter=256,
                     shared_inter=128, dtype="fp8", gating="sigmoid", routed_scale=2.5,
@@ -48,16 +49,48 @@ def test_oracle_results_pass_and_h_codes_are_checked():
     rep = check_layer(WL, inp, out, idx, w, debug=dbg)
     assert rep.ok(), rep.failures
     assert rep.h_checked == WL.m * WL.topk * WL.inter + WL.m * WL.shared_inter
-    assert rep.h_flips == 0 and rep.h_far == 0
+    assert rep.h_ties == 0 and rep.h_hard == 0
 
 
-def test_a_code_several_steps_off_fails():
+def test_a_code_off_away_from_a_tie_is_hard():
     inp = synth.make_inputs(WL)
     out, idx, w, dbg = _as_gpu(WL, inp)
     c = dbg["h"].numpy()
     c[3, 5] = (int(c[3, 5]) & 0x80) | min((int(c[3, 5]) & 0x7F) + 3, 0x7E)
     rep = check_layer(WL, inp, out, idx, w, debug=dbg)
-    assert any("farther than one e4m3 step" in f for f in rep.failures)
+    assert rep.h_hard == 1 and rep.h_ties == 0
+
+
+def test_the_other_code_at_a_planted_tie_is_a_choice():
+    """An h value placed exactly between two codes: the GPU's other code is
+    accepted as a tie and the output compared with the oracle rerun with it;
+    the same code flip away from a tie is not."""
+    inp = synth.make_inputs(WL)
+    spec, args = oracle_inputs(WL, inp)
+    r = OL.forward(spec, **args, keep_h=True)
+    p = 7
+    s = float(r["h_scale"][p][0])
+    pre = r["h_pre"][p].copy()
+    col = int(np.argmax(np.abs(pre[:128]) < 0.5 * np.abs(pre[:128]).max()))
+    q = pre[col] / s
+    # the quotient's nearest code and the neighbour on the far side of it
+    c0 = int(enc(np.float32(q)))
+    v0 = float(dec(np.uint8(c0)))
+    c1 = c0 + 1 if abs(q) > abs(v0) else c0 - 1
+    v1 = float(dec(np.uint8(c1)))
+    # move the exact value onto the midpoint: both codes are then correct
+    pre_t = pre.copy()[None, :]
+    pre_t[0, col] = 0.5 * (v0 + v1) * s
+    gcodes = enc((r["h"][p] / np.repeat(r["h_scale"][p], 128)).astype(np.float32))[None, :]
+    gcodes[0, col] = c1
+    _, ties, hard = h_compare(pre_t, r["h"][p][None, :], r["h_scale"][p][None, :], gcodes,
+                              r["h_scale"][p][None, :])
+    assert len(ties) == 1 and hard == 0 and ties[0][:2] == (0, col)
+    # the same choice with the exact value a tenth of a step from the midpoint
+    pre_t[0, col] = (0.5 * (v0 + v1) + 0.1 * (v0 - v1)) * s
+    _, ties, hard = h_compare(pre_t, r["h"][p][None, :], r["h_scale"][p][None, :], gcodes,
+                              r["h_scale"][p][None, :])
+    assert len(ties) == 0 and hard == 1
 
 
 def test_a_wrong_scale_fails():
