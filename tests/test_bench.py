@@ -46,6 +46,19 @@ def test_mxfp4_counts_take_half_a_byte_per_weight_and_a_scale_byte_per_32():
     assert bench.COMPUTE_DTYPE["mxfp4"] == "bf16"
 
 
+def test_fp8_layer_products_take_the_bf16_peak():
+    assert bench.MFMA_PEAK_TFLOPS["fp8"] == bench.MFMA_PEAK_TFLOPS["bf16"]
+    assert bench.COMPUTE_DTYPE["fp8"] == "bf16"
+
+
+def test_every_config_entry_names_a_workload_with_a_cpu_sample():
+    for name, m, launch in bench.CONFIG_RUNS:
+        assert name in synth.WORKLOADS and launch in ("eager", "graph")
+        assert m <= synth.WORKLOADS[name].m
+        assert name in bench.CPU_SAMPLE
+    assert "large_fp8" in bench.CPU_SAMPLE
+
+
 def test_recorded_traffic_follows_the_kernel_sources(tmp_path, monkeypatch):
     """The counters stand only while the kernel's sources are the ones counted."""
     files = bench.KERNEL_SOURCES["small_m"]
