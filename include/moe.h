@@ -232,6 +232,29 @@ int moe_forward_debug(moe_plan_t plan, int32_t m, const void *x,
                       size_t workspace_bytes, void *stream,
                       const moe_debug_t *dbg);
 
+/* Bytes of the static device scratch behind moe_forward_noalloc (one copy
+ * per GPU the library runs on, held until the process ends). */
+#define MOE_NOALLOC_SCRATCH_BYTES (128u << 20)
+
+/* moe_forward for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same arguments without the workspace, which comes from a static device
+ * array of MOE_NOALLOC_SCRATCH_BYTES per GPU instead (its device address is
+ * looked up once per device; no hipMalloc, hipFree or allocating library
+ * call is made).  The caller still owns every input and output.  A call
+ * whose workspace would exceed the scratch (moe_workspace_bytes(plan, m) >
+ * MOE_NOALLOC_SCRATCH_BYTES, e.g. the 4096-token fp8 layer) returns
+ * MOE_ERR_WORKSPACE before anything is enqueued, and moe_strerror names the
+ * sizes.  Every call on one GPU shares that GPU's scratch and leaves its
+ * contents behind (the layer needs none of them zeroed): calls that may
+ * overlap on one GPU -- on different streams or threads -- race on it and
+ * must be ordered by the caller.  Other errors as moe_forward. */
+int moe_forward_noalloc(moe_plan_t plan, int32_t m, const void *x, const void *router_w,
+                        const void *experts_w13, const void *experts_w2,
+                        const moe_shared_t *shared_w, int32_t topk, void *out,
+                        int32_t *topk_idx, float *topk_w, const float *router_bias,
+                        const void *w13_scale, const void *w2_scale, void *stream);
+
 /* Which expert path moe_forward takes for m tokens (a moe_path_t other than
  * AUTO), or -1 on a NULL plan. */
 int moe_path_for(moe_plan_t plan, int32_t m);
@@ -240,7 +263,8 @@ int moe_path_for(moe_plan_t plan, int32_t m);
 void moe_plan_destroy(moe_plan_t plan);
 
 /* Static text for a status code.  For MOE_ERR_HIP the text of the most
- * recent failing HIP call on this thread is appended. */
+ * recent failing HIP call on this thread is appended; for MOE_ERR_WORKSPACE
+ * the sizes of the most recent workspace error on this thread. */
 const char *moe_strerror(int status);
 
 #ifdef __cplusplus

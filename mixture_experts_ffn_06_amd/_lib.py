@@ -21,7 +21,8 @@ GATINGS = {"softmax": GATE_SOFTMAX, "sigmoid": GATE_SIGMOID,
            "sqrtsoftplus": GATE_SQRTSOFTPLUS}
 
 EXPORTS = ("moe_plan", "moe_workspace_bytes", "moe_forward", "moe_forward_debug",
-           "moe_path_for", "moe_plan_destroy", "moe_strerror")
+           "moe_forward_noalloc", "moe_path_for", "moe_plan_destroy", "moe_strerror")
+NOALLOC_SCRATCH_BYTES = 128 << 20      # MOE_NOALLOC_SCRATCH_BYTES
 
 
 class MoeConfig(ctypes.Structure):
@@ -82,6 +83,8 @@ def lib() -> ctypes.CDLL:
         L.moe_forward.restype = ctypes.c_int
         L.moe_forward_debug.argtypes = fwd + [ctypes.POINTER(MoeDebug)]
         L.moe_forward_debug.restype = ctypes.c_int
+        L.moe_forward_noalloc.argtypes = fwd[:14] + [vp]
+        L.moe_forward_noalloc.restype = ctypes.c_int
         L.moe_path_for.argtypes = [vp, i32]
         L.moe_path_for.restype = ctypes.c_int
         L.moe_plan_destroy.argtypes = [vp]
@@ -190,4 +193,30 @@ class MoePlan:
             st = lib().moe_forward_debug(*args, ctypes.byref(dbg))
         if st != 0 and check:
             raise MoeError(st, "moe_forward")
+        return st
+
+    def forward_noalloc(self, x, router_w, w13, w2, out, topk_idx, topk_w,
+                        shared=None, bias=None, w13_scale=None, w2_scale=None,
+                        stream=None, m: int | None = None, check: bool = True) -> int:
+        """Enqueue one layer forward through ``moe_forward_noalloc`` (the
+        library's static per-GPU scratch instead of a workspace)."""
+        import torch
+        if m is None:
+            m = x.shape[0]
+        if stream is None:
+            stream = torch.cuda.current_stream().cuda_stream
+        elif hasattr(stream, "cuda_stream"):
+            stream = stream.cuda_stream
+        sh = None
+        if shared is not None:
+            sh = MoeShared(_ptr(shared["w13"]), _ptr(shared["w2"]),
+                           _ptr(shared.get("w13_scale")), _ptr(shared.get("w2_scale")),
+                           _ptr(shared.get("gate")))
+        st = lib().moe_forward_noalloc(
+            self._h, m, _ptr(x), _ptr(router_w), _ptr(w13), _ptr(w2),
+            ctypes.byref(sh) if sh is not None else None, self.cfg.topk,
+            _ptr(out), _ptr(topk_idx), _ptr(topk_w), _ptr(bias),
+            _ptr(w13_scale), _ptr(w2_scale), stream)
+        if st != 0 and check:
+            raise MoeError(st, "moe_forward_noalloc")
         return st

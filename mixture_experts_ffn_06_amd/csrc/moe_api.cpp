@@ -12,6 +12,7 @@
 
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 
 #include "../../include/moe.h"
@@ -213,7 +214,10 @@ int run_forward(moe_plan_t plan, int32_t m, const void *x, const void *router_w,
   const int path = resolve_path(c, m);
   if (path == MOE_PATH_SMALL_M && m > small_m_limit(c)) return MOE_ERR_UNSUPPORTED;
   const Layout L = layout(*plan, m);
-  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  if (ws_bytes < L.total) {
+    std::snprintf(g_err, sizeof(g_err), "%d tokens need %zu bytes, %zu given", m, L.total, ws_bytes);
+    return MOE_ERR_WORKSPACE;
+  }
 
   moe::Dims d;
   d.m = m; d.H = c.hidden; d.E = c.num_experts; d.I = c.inter;
@@ -309,6 +313,37 @@ int run_forward(moe_plan_t plan, int32_t m, const void *x, const void *router_w,
   return MOE_OK;
 }
 
+// ---- scratch of moe_forward_noalloc ----
+// One copy of this array per GPU the library runs on, held until the process
+// ends.  In host code its name is only a host-side stand-in: the device
+// address comes from hipGetSymbolAddress, once per device with that device
+// current, and only that address is ever handed to a kernel.
+static_assert(MOE_NOALLOC_SCRATCH_BYTES % 256 == 0, "scratch size");
+__device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+
+// Device address of this GPU's scratch (nullptr and the error on failure).
+void *scratch_address(hipError_t *err) {
+  static std::once_flag once[kMaxDevices];
+  static void *addr[kMaxDevices];
+  static hipError_t status[kMaxDevices];
+  int dev = 0;
+  *err = hipGetDevice(&dev);
+  if (*err != hipSuccess) return nullptr;
+  if (dev < 0 || dev >= kMaxDevices) {
+    *err = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  std::call_once(once[dev], [dev] {
+    void *p = nullptr;
+    status[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    addr[dev] = status[dev] == hipSuccess ? p : nullptr;
+  });
+  *err = status[dev];
+  return addr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -356,6 +391,31 @@ int moe_forward_debug(moe_plan_t plan, int32_t m, const void *x,
                      w2_scale, workspace, workspace_bytes, stream, dbg);
 }
 
+int moe_forward_noalloc(moe_plan_t plan, int32_t m, const void *x, const void *router_w,
+                        const void *experts_w13, const void *experts_w2,
+                        const moe_shared_t *shared_w, int32_t topk, void *out,
+                        int32_t *topk_idx, float *topk_w, const float *router_bias,
+                        const void *w13_scale, const void *w2_scale, void *stream) {
+  if (!plan) return MOE_ERR_INVALID_ARG;
+  if (m < 0 || m > plan->cfg.max_tokens) return MOE_ERR_INVALID_ARG;
+  const size_t need = layout(*plan, m).total;
+  if (need > MOE_NOALLOC_SCRATCH_BYTES) {
+    std::snprintf(g_err, sizeof(g_err),
+                  "moe_forward_noalloc: %d tokens need %zu bytes of scratch, the static scratch "
+                  "holds %zu", m, need, static_cast<size_t>(MOE_NOALLOC_SCRATCH_BYTES));
+    return MOE_ERR_WORKSPACE;
+  }
+  if (m == 0) return run_forward(plan, 0, x, router_w, experts_w13, experts_w2, shared_w, topk,
+                                 out, topk_idx, topk_w, router_bias, w13_scale, w2_scale,
+                                 nullptr, 0, stream, nullptr);
+  hipError_t e;
+  void *ws = scratch_address(&e);
+  if (!ws) return hip_fail(e, "moe_forward_noalloc: scratch address");
+  return run_forward(plan, m, x, router_w, experts_w13, experts_w2, shared_w, topk, out,
+                     topk_idx, topk_w, router_bias, w13_scale, w2_scale, ws,
+                     MOE_NOALLOC_SCRATCH_BYTES, stream, nullptr);
+}
+
 int moe_path_for(moe_plan_t plan, int32_t m) {
   if (!plan) return -1;
   return resolve_path(plan->cfg, m);
@@ -369,7 +429,9 @@ const char *moe_strerror(int status) {
     case MOE_OK: return "ok";
     case MOE_ERR_INVALID_ARG: return "invalid argument";
     case MOE_ERR_UNSUPPORTED: return "unsupported configuration";
-    case MOE_ERR_WORKSPACE: return "workspace too small";
+    case MOE_ERR_WORKSPACE:
+      std::snprintf(buf, sizeof(buf), "workspace too small (%s)", g_err);
+      return buf;
     case MOE_ERR_HIP:
       std::snprintf(buf, sizeof(buf), "HIP error (%s)", g_err);
       return buf;

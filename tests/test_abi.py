@@ -134,3 +134,20 @@ def test_strerror_texts():
     assert moe.strerror(0) == "ok"
     assert "workspace" in moe.strerror(3)
     assert moe.strerror(99) == "unknown status"
+
+
+def test_noalloc_rejects_calls_beyond_its_scratch_before_any_launch():
+    """moe_forward_noalloc checks the call's workspace against the static
+    scratch first: too many tokens is MOE_ERR_WORKSPACE with the sizes named,
+    more than the plan's max_tokens MOE_ERR_INVALID_ARG; nothing is touched."""
+    from mixture_experts_ffn_06_amd._lib import NOALLOC_SCRATCH_BYTES
+    p = moe.MoePlan(**_cfg(weight_dtype="fp8", hidden=7168, num_experts=256, inter=2048,
+                           topk=8, shared_inter=2048, max_tokens=4096))
+    assert p.workspace_bytes(4096) > NOALLOC_SCRATCH_BYTES
+    L = lib()
+    args = [FAKE] * 4 + [None, 8] + [FAKE] * 3 + [None, FAKE, FAKE, None]
+    st = L.moe_forward_noalloc(p.handle, 4096, *args)
+    assert st == 3
+    assert b"scratch" in L.moe_strerror(st)
+    assert L.moe_forward_noalloc(p.handle, 4097, *args) == 1
+    assert L.moe_forward_noalloc(None, 4, *args) == 1
