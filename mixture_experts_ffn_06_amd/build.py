@@ -30,6 +30,16 @@ FLAGS = [
 ]
 
 
+# Per-file additions: the gate/up kernel keeps its accumulators in VGPRs
+# (its fp8 path rescales them with VALU multiplies, which cannot read AGPRs),
+# so its MFMAs take the VGPR form.
+FILE_FLAGS = {"gateup.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
+def file_flags(src: str) -> list:
+    return FILE_FLAGS.get(os.path.basename(src), [])
+
+
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC)
                   if f.endswith((".hip", ".cpp")))
@@ -37,7 +47,7 @@ def sources():
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-x", "hip", "-c", src, "-o", obj]
+    cmd = [HIPCC, *FLAGS, *file_flags(src), "-x", "hip", "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")

@@ -1,0 +1,508 @@
+// Grouped gate/up GEMM with the SwiGLU epilogue on the bf16 32x32x16 MFMA
+// (bf16 weights, or e4m3 codes converted to their exact bf16 values).
+//
+// forward_prefill.rs (page 3, MoeLayer::forward_prefill, doc comment
+// "Pipeline", steps 4-5) sorts token rows by expert so that each expert's
+// weights are loaded once for all of its tokens, then runs the grouped gate/up
+// GEMM and the SiLU gate; its notes on the fp8 grouped GEMM describe a
+// weight-stationary per-expert kernel with two-level fp32 block-scale
+// accumulation.
+//
+// Layout on CDNA4:
+//  * A unit is (group, N tile, M tile): 128 h columns (128 gate rows of w1
+//    and the matching 128 up rows of w3) against up to 128 token rows of one
+//    group (a routed expert's sorted rows, or the m tokens for the shared
+//    expert, group E).  Consecutive units are the M tiles of one N tile and
+//    run side by side on one XCD, so a tile's weights come from HBM once and
+//    from that XCD's L2 for the other M tiles.
+//  * A block is 4 waves, one per SIMD, each with the whole register file
+//    (512 per lane).  Wave w owns weight rows [32 w, 32 w + 32) of the gate
+//    half and of the up half of the tile, as the M side of the MFMA, and
+//    multiplies them with all token blocks (the N side): each lane then holds
+//    one token's results, so its activation scale is one value per token
+//    block and the block-scale promotion is one FMA per accumulator.
+//  * Per K stage (128 bytes of every row: 64 bf16 or 128 e4m3 elements) the
+//    256 weight rows and the token rows go to LDS by direct global->LDS
+//    loads (each wave loads its own 64 weight rows and one 32-row token
+//    block, 16-byte pieces XOR-swizzled per row); three stages in flight, one
+//    barrier per stage for the shared token rows.
+//  * Lane l multiplies row l % 32 of a block and takes 64 of the stage's
+//    bytes: pieces P(g, j) = 4 (j / 2) + 2 g + j % 2 for lane group g = l / 32,
+//    j = 0..3.  MFMA step s uses piece j = s (bf16) or half s % 2 of piece
+//    j = s / 2 (fp8); any split of K over the lanes gives the same product as
+//    long as both operands use it, and this one makes the first half of a
+//    bf16 stage (steps 0, 1) the first 32 K elements, so a half stage at the
+//    end of K runs two steps.
+//  * fp8: the accumulators hold the running sum over the 128-wide K blocks
+//    divided by the current block's scale (activation row scale x weight
+//    block scale) and are rescaled to the next block's scale before its
+//    first MFMA; after the last block they are multiplied by its scale.  The fp8
+//    MFMA itself is not used here: it drops product bits below ~2^-14 of the
+//    largest of each eight products, enough to move SwiGLU outputs across the
+//    fp8 rounding boundaries of h.
+//  * Epilogue: SwiGLU from the gate and up accumulators (the same layout);
+//    bf16 h, or fp8 h quantised per row per 128 columns (the unit's
+//    columns: row amax across the four waves through LDS).
+#include "common.h"
+#include "kernels.h"
+#include "launch.h"
+#include "lds.h"
+
+namespace moe {
+
+namespace {
+
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+constexpr int kGuWaves = 4;
+constexpr int kGuRowBytes = 128;   // bytes of a row per stage
+constexpr int kGuWRows = 256;      // weight rows per unit (4 waves x (32 gate + 32 up))
+constexpr int kGuTBlocks = 4;      // token blocks of 32 rows per unit
+constexpr int kGuTRows = 32 * kGuTBlocks;
+constexpr int kGuDepth = 3;        // stages in the LDS ring
+
+template <int DT>
+struct GuCfg {
+  static constexpr int ESZ = DT == kBF16 ? 2 : 1;
+  static constexpr int SK = kGuRowBytes / ESZ;              // K elements per stage
+  static constexpr int STEPS = SK / 16;                     // MFMA steps per stage
+  static constexpr int W_BYTES = kGuWRows * kGuRowBytes;    // 32 KB
+  static constexpr int S_BYTES = DT == kFP8 ? 2048 : 0;     // token and weight-block scales, 2 K blocks
+  static constexpr int T_BYTES = kGuTRows * kGuRowBytes;    // 16 KB
+  static constexpr int SLOT = W_BYTES + S_BYTES + T_BYTES;
+  static constexpr int LDS = kGuDepth * SLOT;
+  // vector-memory operations per wave per stage: 8 weight + 4 token loads
+  // (+ two 4-byte scale loads for fp8: this K block's and the next one's)
+  static constexpr int OPS = 8 + 4 + (DT == kFP8 ? 2 : 0);
+  static_assert(OPS < 16 && 2 * OPS < 64, "vmcnt range");
+  static_assert(LDS <= 160 * 1024, "LDS");
+};
+
+struct GuArgs {
+  Dims d;
+  Inputs in;
+  Work w;
+  int ntile_r;   // N tiles of a routed expert (128 h columns each)
+  int ntile_s;   // N tiles of the shared expert
+};
+
+// Position of logical 16-byte piece p in row r of a stage: the 16 rows read
+// by one quarter of a wave's read instruction land in 16 distinct 16-byte
+// bank groups (8 XOR values x the row's 128-byte parity).
+__device__ __forceinline__ int gu_swz(int r) { return (r >> 1) & 7; }
+
+// Logical piece of the lane's j-th 16 bytes (lane group g).
+__device__ __forceinline__ int gu_piece(int g, int j) { return 4 * (j >> 1) + 2 * g + (j & 1); }
+
+template <int DT>
+__global__ __launch_bounds__(kGuWaves * kWave, 1) void gu_kernel(GuArgs a) {
+  using C = GuCfg<DT>;
+  extern __shared__ __align__(1024) uint8_t lds[];
+  __shared__ int uoff[1026];             // unit prefix over the E + 1 groups
+  __shared__ int wsum[kGuWaves];
+  __shared__ float amax_w[kGuWaves][kGuTRows];
+  const Dims &d = a.d;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = uniform(tid >> 6);
+  const int G = d.E + (d.Is > 0 ? 1 : 0);
+  const int *offsets = a.w.offsets;
+
+  // ---- unit prefix: units(g) = ceil(rows_g / 128) * ntile_g ----
+  {
+    constexpr int PER = (1025 + kGuWaves * kWave - 1) / (kGuWaves * kWave);
+    int loc[PER];
+    int sum = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int g = tid * PER + i;
+      int u = 0;
+      if (g < G) {
+        const int rows = g < d.E ? offsets[g + 1] - offsets[g] : d.m;
+        u = (rows + kGuTRows - 1) / kGuTRows * (g < d.E ? a.ntile_r : a.ntile_s);
+      }
+      loc[i] = u;
+      sum += u;
+    }
+    int incl = sum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int t = __shfl_up(incl, o);
+      if (lane >= o) incl += t;
+    }
+    if (lane == 63) wsum[wave] = incl;
+    __syncthreads();
+    int base = 0;
+#pragma unroll
+    for (int i = 0; i < kGuWaves; ++i) base += i < wave ? wsum[i] : 0;
+    int run = base + incl - sum;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int g = tid * PER + i;
+      if (g <= G) uoff[g] = run;
+      run += loc[i];
+    }
+    __syncthreads();
+  }
+  const int total = uoff[G];
+  const int P = gridDim.x;
+  const int per_xcd = P / 8;
+  const int xcd = blockIdx.x & 7, slot_id = blockIdx.x >> 3;
+
+  const int lg = lane >> 5, lr = lane & 31;   // lane group, row inside a block
+  // the lane's read offsets inside a 32-row block, pieces j = 0..3
+  uint32_t loff[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) loff[j] = lr * kGuRowBytes + ((gu_piece(lg, j) ^ gu_swz(lr)) * 16);
+  // a load instruction covers 8 rows: lane l writes piece l % 8 of row l / 8
+  const int drow = lane >> 3, dpiece = lane & 7;
+
+#pragma unroll 1
+  for (int r = 0; r * P < total; ++r) {
+    const int uu = r * P + xcd * per_xcd + slot_id;
+    if (uu >= total) continue;
+    // ---- decode the unit (block-uniform) ----
+    int lo = 0, hi = G - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (uoff[mid] <= uu) lo = mid; else hi = mid - 1;
+    }
+    const int g = uniform(lo);
+    const bool shared = g == d.E;
+    const int grows = uniform(shared ? d.m : offsets[g + 1] - offsets[g]);
+    const int nmt = (grows + kGuTRows - 1) / kGuTRows;
+    const int local = uu - uniform(uoff[g]);
+    const int ntile = local / nmt;
+    // the group's rows split evenly over its nmt M tiles (a 150-row expert
+    // runs two tiles of 75 rows, not 128 + 22)
+    const int trows = (grows + nmt - 1) / nmt;
+    const int row0 = (local - ntile * nmt) * trows;
+    const int rows = min(trows, grows - row0);
+    const int ntb = (rows + 31) >> 5;                       // token blocks with rows
+    const bool tload = wave < ntb;                          // this wave loads token block `wave`
+    const int seg0 = shared ? 0 : uniform(offsets[g]);
+    const int inter = shared ? d.Is : d.I;
+    const int kbytes = d.H * C::ESZ;
+    const int nstage = (kbytes + kGuRowBytes - 1) / kGuRowBytes;
+    const int c0 = ntile * 128 + 32 * wave;                 // this wave's first h column
+    const bool wave_on = c0 < inter;
+
+    const uint8_t *Wb = static_cast<const uint8_t *>(shared ? a.in.sw13 : a.in.w13) +
+                        (shared ? 0 : static_cast<size_t>(g) * 2 * d.I * d.H * C::ESZ);
+    const uint8_t *Ab = DT == kFP8 ? static_cast<const uint8_t *>(a.w.xq)
+                                   : static_cast<const uint8_t *>(a.in.x);
+
+    // ---- this wave's load sources (32-bit byte offsets; operands < 2 GiB) ----
+    // Weight instruction q (0..7) moves rows 8 (q % 4) + drow of the gate
+    // (q < 4) or up block to LDS rows 64 wave + 8 q + drow; token instruction
+    // q (0..3) token rows 32 wave + 8 q + drow (past the tile's rows: its last
+    // row again).  The lane fetches logical piece dpiece ^ swz(LDS row); for
+    // these rows that is p0 ^ 4 (q % 2), p0 = dpiece ^ (drow / 2), so the
+    // offsets are two lane values plus a wave-uniform part.  *hi: the piece
+    // lies in the second half of the stage's 128 bytes.
+    const int p0 = dpiece ^ (drow >> 1);
+    const int wrow0 = wave_on ? c0 + drow : 0;             // out of range: read valid memory, store nothing
+    const uint32_t wlane[2] = {static_cast<uint32_t>(wrow0) * kbytes + p0 * 16,
+                               static_cast<uint32_t>(wrow0) * kbytes + (p0 ^ 4) * 16};
+    const bool whi[2] = {p0 >= 4, (p0 ^ 4) >= 4};
+    auto wuni = [&](int q) -> uint32_t {   // wave-uniform part of weight instruction q
+      return wave_on ? static_cast<uint32_t>(8 * (q & 3) + (q >= 4 ? inter : 0)) * kbytes : 0u;
+    };
+    uint32_t toff[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int rr = min(32 * wave + 8 * q + drow, rows - 1);
+      const int tok = shared ? row0 + rr : a.w.sorted_pair[seg0 + row0 + rr] / d.k;
+      toff[q] = static_cast<uint32_t>(tok) * kbytes + (p0 ^ (4 * (q & 1))) * 16;
+    }
+    // fp8 scales of the stage's K block and of the next one (a scale area
+    // of 2 x 1 KB per slot): waves 0, 1 load the token rows' scales (64
+    // each), wave 2 the gate (even lanes) and up (odd lanes) weight-block
+    // scales, wave 3 the same again into a spare area (every wave issues two
+    // scale loads per stage)
+    const float *sbase = nullptr;
+    uint32_t soff = 0;
+    if constexpr (DT == kFP8) {
+      const int nkb = d.H / kQBlock;
+      if (wave < 2) {
+        const int rr = min(64 * wave + lane, rows - 1);
+        const int tok = shared ? row0 + rr : a.w.sorted_pair[seg0 + row0 + rr] / d.k;
+        sbase = a.w.sx;
+        soff = static_cast<uint32_t>(tok) * nkb;
+      } else {
+        sbase = shared ? a.in.sw13_scale
+                       : a.in.w13_scale + static_cast<size_t>(g) * (2 * d.I / kQBlock) * nkb;
+        const int srow = (lane & 1) ? inter / kQBlock + ntile : ntile;
+        soff = static_cast<uint32_t>(srow) * nkb;
+      }
+    }
+
+    // Stage st goes to ring slot st % 3: weights, scales, tokens, issued in
+    // four parts (the gate block's weight rows, the up block's, the token
+    // block, the fp8 scales).  Each load instruction holds the CU's address
+    // path for ~16 cycles and a wave cannot issue past a load that waits for
+    // it, so the parts of a later stage are spread between a stage's MFMAs
+    // and the four waves issue different parts at a time.  In a bf16 half
+    // stage (the last one when K % 64 == 32) the pieces past the row's end
+    // load the piece 64 bytes before (valid memory; the steps that would use
+    // them are skipped).
+    auto issue_part = [&](int st, int part) {
+      uint8_t *sl = lds + (st % kGuDepth) * C::SLOT;
+      const uint32_t kb = static_cast<uint32_t>(st) * kGuRowBytes;
+      const bool half = DT == kBF16 && kb + kGuRowBytes > static_cast<uint32_t>(kbytes);
+      const uint32_t kb2 = half ? kb - 64 : kb;
+      if (part < 2) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int q = 4 * part + i;
+          dma16_to_lds(Wb + (wlane[q & 1] + wuni(q) + (whi[q & 1] ? kb2 : kb)), sl + (8 * wave + q) * 1024);
+        }
+      } else if (part == 2) {
+        if (tload) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            dma16_to_lds(Ab + (toff[q] + (whi[q & 1] ? kb2 : kb)),
+                         sl + C::W_BYTES + C::S_BYTES + (4 * wave + q) * 1024);
+        }
+      } else {
+        if constexpr (DT == kFP8) {
+          // the next K block's scales too (past the last block: the last
+          // block's again, unused)
+          dma4_to_lds(sbase + (soff + st), sl + C::W_BYTES + 256 * wave);
+          dma4_to_lds(sbase + (soff + min(st + 1, nstage - 1)), sl + C::W_BYTES + 1024 + 256 * wave);
+        }
+      }
+    };
+    auto issue = [&](int st) {
+      for (int part = 0; part < 4; ++part) issue_part(st, part);
+    };
+
+    // ---- accumulators: [weight block: 0 gate, 1 up][token block] ----
+    f32x16_t acc[2][kGuTBlocks];
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int t = 0; t < kGuTBlocks; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[b][t][i] = 0.f;
+
+    // fp8: acc holds the running sum divided by the current K block's scale
+    // s_k (activation row scale x weight block scale): after block k's last
+    // MFMA, acc *= s_k / s_(k+1) (each stage's scale area holds both); the
+    // MFMAs of block k + 1 then accumulate its products directly, and after
+    // the last block acc *= s_last.  That is sum_k s_k P_k with one VALU
+    // operation per accumulator and K block (as a separate partial sum would
+    // take) but no registers for partials, and each accumulator block's
+    // rescale sits between the last MFMAs of the others.
+    // One stage: the lane's LDS reads of operand pieces (fp8: after its
+    // token and weight-block scales), issued one piece ahead and waited for
+    // piece by piece, the MFMAs of each piece's steps in between; NT = token
+    // blocks with rows (a template parameter keeps the MFMA sequence free of
+    // branches).
+    auto stage = [&](int st, auto ntc, int dma_st) {
+      constexpr int NT = decltype(ntc)::value;
+      const uint8_t *sl = lds + (st % kGuDepth) * C::SLOT;
+      const uint32_t lw = lds_off(sl + 64 * wave * kGuRowBytes);
+      const uint32_t lt = lds_off(sl + C::W_BYTES + C::S_BYTES);
+      const bool half = DT == kBF16 && static_cast<uint32_t>(st + 1) * kGuRowBytes > static_cast<uint32_t>(kbytes);
+      u32x4_t wr[4][2], tr[4][NT];
+      uint32_t sxr[2][NT];     // [this K block, next][token block]
+      u32x2_t swr[2];
+      if constexpr (DT == kFP8) {
+        const uint32_t ls = lds_off(sl + C::W_BYTES);
+        static_for<0, NT>([&](auto tc) {
+          constexpr int t = decltype(tc)::value;
+          lds_issue_b32<128 * t>(ls + 4 * lr, sxr[0][t]);
+          lds_issue_b32<1024 + 128 * t>(ls + 4 * lr, sxr[1][t]);
+        });
+        lds_issue_b64<512>(ls, swr[0]);
+        lds_issue_b64<1024 + 512>(ls, swr[1]);
+      }
+      auto issue_piece = [&](auto jc) {
+        constexpr int j = decltype(jc)::value;
+        lds_issue<0>(lw + loff[j], wr[j][0]);
+        lds_issue<32 * kGuRowBytes>(lw + loff[j], wr[j][1]);
+        static_for<0, NT>([&](auto tc) {
+          constexpr int t = decltype(tc)::value;
+          lds_issue<32 * kGuRowBytes * t>(lt + loff[j], tr[j][t]);
+        });
+      };
+      issue_piece(std::integral_constant<int, 0>{});
+      static_for<0, 4>([&](auto jc) {
+        constexpr int j = decltype(jc)::value;
+        if constexpr (j + 1 < 4) issue_piece(std::integral_constant<int, j + 1>{});
+        // after piece j + 1 was issued: wait for piece j
+        if constexpr (j < 3) asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(2 + NT) : "memory");
+        else asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        lds_tie(wr[j][0]);
+        lds_tie(wr[j][1]);
+        static_for<0, NT>([&](auto tc) { lds_tie(tr[j][decltype(tc)::value]); });
+        if constexpr (DT == kFP8 && j == 0) {
+          static_for<0, NT>([&](auto tc) {
+            lds_tie_b32(sxr[0][decltype(tc)::value]);
+            lds_tie_b32(sxr[1][decltype(tc)::value]);
+          });
+          lds_tie_b64(swr[0]);
+          lds_tie_b64(swr[1]);
+        }
+        // a quarter of a later stage's loads: part (j + wave) % 4, so the
+        // four waves issue different parts at any one time
+        if (dma_st >= 0) issue_part(dma_st, (j + wave) & 3);
+        if constexpr (DT == kBF16) {
+          // step j: the piece as 8 bf16 values; a half stage runs steps 0, 1
+          if (!(half && j >= 2)) {
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+#pragma unroll
+              for (int b = 0; b < 2; ++b)
+                acc[b][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    __builtin_bit_cast(bf16x8_t, wr[j][b]), __builtin_bit_cast(bf16x8_t, tr[j][t]),
+                    acc[b][t], 0, 0, 0);
+          }
+        } else {
+          // steps 2 j and 2 j + 1: the two 8-byte halves of the piece; the
+          // rescale to this K block's scale before its first step
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            bf16x8_t wv[2], tv[NT];
+#pragma unroll
+            for (int b = 0; b < 2; ++b) wv[b] = e4m3x8_to_bf16(wr[j][b][2 * h], wr[j][b][2 * h + 1]);
+#pragma unroll
+            for (int t = 0; t < NT; ++t) tv[t] = e4m3x8_to_bf16(tr[j][t][2 * h], tr[j][t][2 * h + 1]);
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+#pragma unroll
+              for (int b = 0; b < 2; ++b)
+                acc[b][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wv[b], tv[t], acc[b][t], 0, 0, 0);
+          }
+          if constexpr (j == 3) {
+            // the K block is done: to the next block's scale (after the last
+            // block, to its own scale: acc becomes the sum itself)
+            const bool last = st + 1 == nstage;
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+#pragma unroll
+              for (int b = 0; b < 2; ++b) {
+                const float s0 = __uint_as_float(sxr[0][t]) * __uint_as_float(swr[0][b]);
+                const float s1 = __uint_as_float(sxr[1][t]) * __uint_as_float(swr[1][b]);
+                const float r = last ? s0 : s0 * __builtin_amdgcn_rcpf(s1);
+                acc[b][t] *= r;
+              }
+          }
+        }
+      });
+    };
+
+    __syncthreads();   // the previous unit is done with every slot and amax_w
+    // ---- the ring: stage st waits for its own loads (only stage st + 1 was
+    // issued after them), passes the barrier -- every wave's loads of stage
+    // st have landed and every wave is done with stage st - 1 -- and
+    // multiplies stage st while refilling stage st - 1's slot with stage
+    // st + 2 ----
+    auto run = [&](auto ntc) {
+      constexpr int NT = decltype(ntc)::value;
+      issue(0);
+      if (nstage > 1) issue(1);
+#pragma unroll 1
+      for (int st = 0; st < nstage; ++st) {
+        if (st + 1 < nstage) {
+          if (tload) wait_vm<C::OPS>();
+          else wait_vm<C::OPS - 4>();
+        } else {
+          wait_vm<0>();
+        }
+        ring_barrier();
+        const int dma_st = st + 2 < nstage ? st + 2 : -1;
+        if (wave_on) stage(st, ntc, dma_st);
+        else if (dma_st >= 0) issue(dma_st);
+      }
+    };
+    switch (ntb) {
+      case 1: run(std::integral_constant<int, 1>{}); break;
+      case 2: run(std::integral_constant<int, 2>{}); break;
+      case 3: run(std::integral_constant<int, 3>{}); break;
+      default: run(std::integral_constant<int, 4>{}); break;
+    }
+
+    // ---- epilogue: lane holds token row 32 t + lr, h columns
+    // c0 + 8 (i / 4) + 4 lg + i % 4 for i = 0..15 ----
+    if constexpr (DT == kBF16) {
+      uint16_t *h = static_cast<uint16_t *>(shared ? a.w.h_sh : a.w.h);
+#pragma unroll
+      for (int t = 0; t < kGuTBlocks; ++t) {
+        const int rr = 32 * t + lr;
+        if (!wave_on || rr >= rows) continue;
+        uint16_t *hr = h + static_cast<size_t>(seg0 + row0 + rr) * inter + c0 + 4 * lg;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          uint32_t w0 = f32_to_bf16(silu(acc[0][t][4 * q]) * acc[1][t][4 * q]) |
+                        (static_cast<uint32_t>(f32_to_bf16(silu(acc[0][t][4 * q + 1]) * acc[1][t][4 * q + 1])) << 16);
+          uint32_t w1 = f32_to_bf16(silu(acc[0][t][4 * q + 2]) * acc[1][t][4 * q + 2]) |
+                        (static_cast<uint32_t>(f32_to_bf16(silu(acc[0][t][4 * q + 3]) * acc[1][t][4 * q + 3])) << 16);
+          *reinterpret_cast<u32x2_t *>(hr + 8 * q) = u32x2_t{w0, w1};
+        }
+      }
+    } else {
+      // h per row per 128 columns (this unit's): amax across the 4 waves
+#pragma unroll
+      for (int t = 0; t < kGuTBlocks; ++t) {
+        float am = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float hv = wave_on ? silu(acc[0][t][i]) * acc[1][t][i] : 0.f;
+          acc[0][t][i] = hv;
+          am = fmaxf(am, fabsf(hv));
+        }
+        am = fmaxf(am, __shfl_xor(am, 32));
+        if (lg == 0) amax_w[wave][32 * t + lr] = am;
+      }
+      __syncthreads();
+      uint8_t *h = static_cast<uint8_t *>(shared ? a.w.h_sh : a.w.h);
+      float *hs = shared ? a.w.h_sh_scale : a.w.h_scale;
+#pragma unroll
+      for (int t = 0; t < kGuTBlocks; ++t) {
+        const int rr = 32 * t + lr;
+        if (rr >= rows) continue;
+        float amax = 0.f;
+#pragma unroll
+        for (int w = 0; w < kGuWaves; ++w) amax = fmaxf(amax, amax_w[w][rr]);
+        const float sc = amax > 0.f ? amax / kE4M3Max : 1.0f;
+        const size_t row = static_cast<size_t>(seg0 + row0 + rr);
+        if (wave == 0 && lg == 0) hs[row * (inter / kQBlock) + ntile] = sc;
+        if (!wave_on) continue;
+        uint8_t *hr = h + row * inter + c0 + 4 * lg;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t lo = static_cast<uint32_t>(fp8_pack2(acc[0][t][4 * q] / sc, acc[0][t][4 * q + 1] / sc)) & 0xffffu;
+          const uint32_t hi2 = static_cast<uint32_t>(fp8_pack2(acc[0][t][4 * q + 2] / sc, acc[0][t][4 * q + 3] / sc)) & 0xffffu;
+          *reinterpret_cast<uint32_t *>(hr + 8 * q) = lo | (hi2 << 16);
+        }
+      }
+    }
+  }
+}
+
+template <int DT>
+hipError_t gu_launch(const Dims &d, const Inputs &in, const Work &w, hipStream_t s) {
+  using C = GuCfg<DT>;
+  auto kern = gu_kernel<DT>;
+  static const KernelSetup su = kernel_setup(reinterpret_cast<const void *>(kern), kGuWaves * kWave, C::LDS);
+  if (su.err != hipSuccess) return su.err;
+  GuArgs ga{d, in, w, (d.I + 127) / 128, (d.Is + 127) / 128};
+  const int grid = (device_cus() * su.blocks_per_cu + 7) / 8 * 8;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kGuWaves * kWave), C::LDS, s, ga);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool gu_supported(const Dims &d) {
+  if (d.wdt == kFP8) return d.H % kQBlock == 0 && d.I % kQBlock == 0 && d.Is % kQBlock == 0;
+  if (d.wdt == kBF16) return d.H % 32 == 0 && d.I % 32 == 0 && d.Is % 32 == 0;
+  return false;
+}
+
+hipError_t launch_gu(const Dims &d, const Inputs &in, const Work &w, hipStream_t s) {
+  return d.wdt == kFP8 ? gu_launch<kFP8>(d, in, w, s) : gu_launch<kBF16>(d, in, w, s);
+}
+
+}  // namespace moe

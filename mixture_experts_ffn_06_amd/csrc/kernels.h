@@ -97,6 +97,10 @@ hipError_t launch_simple_down(const Dims &d, const Inputs &in, const Work &w, hi
 // grouped.hip (MFMA grouped GEMM, bf16 / fp8 weights)
 hipError_t launch_grouped_gateup(const Dims &d, const Inputs &in, const Work &w, hipStream_t s);
 hipError_t launch_grouped_down(const Dims &d, const Inputs &in, const Work &w, hipStream_t s);
+// gateup.hip (gate/up + SwiGLU on the bf16 32x32x16 MFMA; bf16 weights with
+// H % 32 == 0, fp8 weights)
+bool gu_supported(const Dims &d);
+hipError_t launch_gu(const Dims &d, const Inputs &in, const Work &w, hipStream_t s);
 // small_m.hip (weight streaming for m <= 16; bf16, MXFP4 and MXFP8 weights)
 hipError_t launch_small_m_gateup(const Dims &d, const Inputs &in, const Work &w, hipStream_t s);
 hipError_t launch_small_m_down(const Dims &d, const Inputs &in, const Work &w, hipStream_t s);

@@ -59,6 +59,18 @@ __device__ __forceinline__ void lds_issue(uint32_t p, u32x4_t &v) {
 }
 __device__ __forceinline__ void lds_tie(u32x4_t &v) { asm volatile("" : "+v"(v)); }
 
+// The same for 4- and 8-byte reads.
+template <int O>
+__device__ __forceinline__ void lds_issue_b32(uint32_t p, uint32_t &v) {
+  asm volatile("ds_read_b32 %0, %1 offset:%2" : "=v"(v) : "v"(p), "i"(O));
+}
+template <int O>
+__device__ __forceinline__ void lds_issue_b64(uint32_t p, u32x2_t &v) {
+  asm volatile("ds_read_b64 %0, %1 offset:%2" : "=v"(v) : "v"(p), "i"(O));
+}
+__device__ __forceinline__ void lds_tie_b32(uint32_t &v) { asm volatile("" : "+v"(v)); }
+__device__ __forceinline__ void lds_tie_b64(u32x2_t &v) { asm volatile("" : "+v"(v)); }
+
 // Compile-time loop: f(integral_constant<int, I>) for I in [B, E).
 template <int B, int E, typename F>
 __device__ __forceinline__ void static_for(F &&f) {

@@ -1,7 +1,7 @@
 """The LDS-ring kernels never touch a register an un-waited asm LDS read
 will still write.
 
-Compiles the kernels that issue inline-asm LDS reads (grouped GEMM, small-m
+Compiles the kernels that issue inline-asm LDS reads (grouped GEMMs, small-m
 weight streaming) to gfx950 assembly with the library's own flags and scans
 it; the scanner itself is checked on hand-written snippets first.
 """
@@ -34,8 +34,11 @@ _Zkern:
 HAZARD_COPY = SAFE.replace("v_add_u32_e32 v2, v3, v12", "v_accvgpr_write_b32 a9, v6")
 # an in-flight destination reused as the next read's address
 HAZARD_ADDR = SAFE.replace("ds_read_b128 v[8:11], v1 offset:16", "ds_read_b128 v[8:11], v5 offset:16")
-# a wait for only some of the reads does not clear them
+# a wait for only some of the reads does not clear the most recent ones
 HAZARD_PARTIAL = SAFE.replace("s_waitcnt lgkmcnt(0)", "s_waitcnt lgkmcnt(1)")
+# ... but it does clear the older ones (reads complete in order)
+SAFE_PARTIAL = SAFE.replace("v_mfma_f32_16x16x32_bf16 a[0:3], v[4:7], v[8:11], a[0:3]",
+                            "v_mov_b32 v20, v4").replace("s_waitcnt lgkmcnt(0)", "s_waitcnt lgkmcnt(1)")
 
 
 def test_scanner_on_snippets():
@@ -46,12 +49,14 @@ def test_scanner_on_snippets():
     h, _, _ = scan(HAZARD_ADDR)
     assert [x[3] for x in h] == [("v", 5)]
     h, _, _ = scan(HAZARD_PARTIAL)
-    assert {x[3] for x in h} == {("v", r) for r in range(4, 12)}
+    assert {x[3] for x in h} == {("v", r) for r in range(8, 12)}
+    h, _, _ = scan(SAFE_PARTIAL)
+    assert h == []
 
 
 def _asm(src: str) -> str:
     flags = [f for f in B.FLAGS if f != "-fPIC"]
-    r = subprocess.run([B.HIPCC, *flags, "-x", "hip", "--cuda-device-only", "-S",
+    r = subprocess.run([B.HIPCC, *flags, *B.file_flags(src), "-x", "hip", "--cuda-device-only", "-S",
                         os.path.join(B.CSRC, src), "-o", "-"],
                        capture_output=True, text=True)
     if r.returncode != 0:
@@ -62,7 +67,7 @@ def _asm(src: str) -> str:
 @pytest.mark.skipif(not os.path.exists(B.HIPCC) and shutil.which("hipcc") is None,
                     reason="hipcc not installed")
 def test_ring_kernels_have_no_lds_read_hazards():
-    srcs = ["grouped.hip", "small_m.hip"]
+    srcs = ["grouped.hip", "small_m.hip", "gateup.hip"]
     with ThreadPoolExecutor(len(srcs)) as ex:
         texts = list(ex.map(_asm, srcs))
     for src, text in zip(srcs, texts):
