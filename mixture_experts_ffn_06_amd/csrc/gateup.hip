@@ -75,7 +75,7 @@ struct GuCfg {
   // (+ two 4-byte scale loads for fp8: this K block's and the next one's)
   static constexpr int OPS = 8 + 4 + (DT == kFP8 ? 2 : 0);
   static_assert(OPS < 16 && 2 * OPS < 64, "vmcnt range");
-  static_assert(LDS <= 160 * 1024, "LDS");
+  static_assert(LDS <= 152 * 1024, "LDS");
 };
 
 struct GuArgs {
@@ -178,7 +178,6 @@ __global__ __launch_bounds__(kGuWaves * kWave, 1) void gu_kernel(GuArgs a) {
     const int row0 = (local - ntile * nmt) * trows;
     const int rows = min(trows, grows - row0);
     const int ntb = (rows + 31) >> 5;                       // token blocks with rows
-    const bool tload = wave < ntb;                          // this wave loads token block `wave`
     const int seg0 = shared ? 0 : uniform(offsets[g]);
     const int inter = shared ? d.Is : d.I;
     const int kbytes = d.H * C::ESZ;
@@ -245,24 +244,24 @@ __global__ __launch_bounds__(kGuWaves * kWave, 1) void gu_kernel(GuArgs a) {
     // stage (the last one when K % 64 == 32) the pieces past the row's end
     // load the piece 64 bytes before (valid memory; the steps that would use
     // them are skipped).
-    auto issue_part = [&](int st, int part) {
+    auto issue_part = [&](int st, auto pc) {
+      constexpr int part = decltype(pc)::value;
       uint8_t *sl = lds + (st % kGuDepth) * C::SLOT;
       const uint32_t kb = static_cast<uint32_t>(st) * kGuRowBytes;
       const bool half = DT == kBF16 && kb + kGuRowBytes > static_cast<uint32_t>(kbytes);
       const uint32_t kb2 = half ? kb - 64 : kb;
-      if (part < 2) {
+      if constexpr (part < 2) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int q = 4 * part + i;
           dma16_to_lds(Wb + (wlane[q & 1] + wuni(q) + (whi[q & 1] ? kb2 : kb)), sl + (8 * wave + q) * 1024);
         }
-      } else if (part == 2) {
-        if (tload) {
+
+      } else if constexpr (part == 2) {
 #pragma unroll
-          for (int q = 0; q < 4; ++q)
-            dma16_to_lds(Ab + (toff[q] + (whi[q & 1] ? kb2 : kb)),
-                         sl + C::W_BYTES + C::S_BYTES + (4 * wave + q) * 1024);
-        }
+        for (int q = 0; q < 4; ++q)
+          dma16_to_lds(Ab + (toff[q] + (whi[q & 1] ? kb2 : kb)),
+                       sl + C::W_BYTES + C::S_BYTES + (4 * wave + q) * 1024);
       } else {
         if constexpr (DT == kFP8) {
           // the next K block's scales too (past the last block: the last
@@ -273,7 +272,7 @@ __global__ __launch_bounds__(kGuWaves * kWave, 1) void gu_kernel(GuArgs a) {
       }
     };
     auto issue = [&](int st) {
-      for (int part = 0; part < 4; ++part) issue_part(st, part);
+      static_for<0, 4>([&](auto pc) { issue_part(st, pc); });
     };
 
     // ---- accumulators: [weight block: 0 gate, 1 up][token block] ----
@@ -344,9 +343,8 @@ __global__ __launch_bounds__(kGuWaves * kWave, 1) void gu_kernel(GuArgs a) {
           lds_tie_b64(swr[0]);
           lds_tie_b64(swr[1]);
         }
-        // a quarter of a later stage's loads: part (j + wave) % 4, so the
-        // four waves issue different parts at any one time
-        if (dma_st >= 0) issue_part(dma_st, (j + wave) & 3);
+        // a quarter of a later stage's loads: part j
+        issue_part(dma_st, jc);
         if constexpr (DT == kBF16) {
           // step j: the piece as 8 bf16 values; a half stage runs steps 0, 1
           if (!(half && j >= 2)) {
@@ -393,27 +391,26 @@ __global__ __launch_bounds__(kGuWaves * kWave, 1) void gu_kernel(GuArgs a) {
     };
 
     __syncthreads();   // the previous unit is done with every slot and amax_w
-    // ---- the ring: stage st waits for its own loads (only stage st + 1 was
-    // issued after them), passes the barrier -- every wave's loads of stage
-    // st have landed and every wave is done with stage st - 1 -- and
-    // multiplies stage st while refilling stage st - 1's slot with stage
-    // st + 2 ----
+    // ---- the ring: stage st multiplies slot st % 3 while stages st + 1 and
+    // st + 2 load.  Every step issues one stage -- past the end the last
+    // stage again, cache hits into a free slot, never read -- and every wave
+    // loads its token block (past the tile's rows: its last row again), so
+    // each wave always has exactly OPS operations per stage outstanding and
+    // one count serves every step: waiting until OPS remain completes this
+    // stage's loads (in-order completion).  The barrier then makes every
+    // wave's loads of stage st visible and frees slot (st + 2) % 3, which all
+    // waves finished reading in stage st - 1 ----
     auto run = [&](auto ntc) {
-      constexpr int NT = decltype(ntc)::value;
       issue(0);
-      if (nstage > 1) issue(1);
+      issue(min(1, nstage - 1));
 #pragma unroll 1
       for (int st = 0; st < nstage; ++st) {
-        if (st + 1 < nstage) {
-          if (tload) wait_vm<C::OPS>();
-          else wait_vm<C::OPS - 4>();
-        } else {
-          wait_vm<0>();
-        }
+        __builtin_amdgcn_sched_barrier(0);   // nothing moves across a stage boundary
+        wait_vm<C::OPS>();
         ring_barrier();
-        const int dma_st = st + 2 < nstage ? st + 2 : -1;
+        const int dma_st = min(st + 2, nstage - 1);
         if (wave_on) stage(st, ntc, dma_st);
-        else if (dma_st >= 0) issue(dma_st);
+        else issue(dma_st);
       }
     };
     switch (ntb) {
