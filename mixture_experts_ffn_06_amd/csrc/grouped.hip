@@ -320,16 +320,19 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void grouped_kernel(GroupedArgs a)
         if (kb + pc >= static_cast<uint32_t>(kbytes)) return co - pc;
       return co + kb;
     };
-    auto issue_a = [&](int st) {
-      uint8_t *sl = lds + (st % C::DA) * C::A_BYTES;
+    // (slot_st: the stage whose ring slot the loads fill -- by default the
+    // stage itself; past the end of K the last stage is loaded again into
+    // the slot of the stage after it, which no one reads)
+    auto issue_a = [&](int st, int slot_st) {
+      uint8_t *sl = lds + (slot_st % C::DA) * C::A_BYTES;
       const uint32_t kb = static_cast<uint32_t>(st) * C::RB;
 #pragma unroll
       for (int q = 0; q < C::CPA; ++q)   // m-blocks past the rows are not loaded
         if ((wave * C::CPA + q) / C::BV < nmb)
           dma16_to_lds(Ab + src_off(coffA[q], cpcA[q], kb), sl + (wave * C::CPA + q) * 1024);
     };
-    auto issue_b = [&](int st) {
-      uint8_t *sl = lds + C::DA * C::A_BYTES + (st % DEPTH) * C::B_STAGE;
+    auto issue_b = [&](int st, int slot_st) {
+      uint8_t *sl = lds + C::DA * C::A_BYTES + (slot_st % DEPTH) * C::B_STAGE;
       const uint32_t kb = static_cast<uint32_t>(st) * C::RB;
 #pragma unroll
       for (int q = 0; q < C::CPB; ++q)
@@ -554,8 +557,8 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void grouped_kernel(GroupedArgs a)
         if (st + DEPTH - 1 < nstage) wait_vm<C::LB>();
         else wait_vm<0>();
         ring_barrier();
-        if (st + 2 < nstage) issue_a(st + 2);
-        if (st + DEPTH < nstage) issue_b(st + DEPTH);
+        if (st + 2 < nstage) issue_a(st + 2, st + 2);
+        if (st + DEPTH < nstage) issue_b(st + DEPTH, st + DEPTH);
         if (rows_on) {
           if (st + 1 < nstage) read_stage(st + 1, next);
           __builtin_amdgcn_sched_barrier(0);
@@ -564,10 +567,10 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void grouped_kernel(GroupedArgs a)
           if (st + 1 < nstage) lds_wait(next);
         }
       };
-      issue_b(0);
-      issue_a(0);
+      issue_b(0, 0);
+      issue_a(0, 0);
       static_for<1, DEPTH - 1>([&](auto ic) {
-        if (decltype(ic)::value < nstage) issue_b(decltype(ic)::value);
+        if (decltype(ic)::value < nstage) issue_b(decltype(ic)::value, decltype(ic)::value);
       });
       // issued after A(0): B(1 .. D-2), where they exist (a wave's A loads
       // per stage vary with the tile's rows, so waits only ever count B loads)
@@ -578,8 +581,8 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void grouped_kernel(GroupedArgs a)
         read_stage(0, RA);
         lds_wait(RA);
       }
-      if (nstage > 1) issue_a(1);
-      if (DEPTH - 1 < nstage) issue_b(DEPTH - 1);
+      if (nstage > 1) issue_a(1, 1);
+      if (DEPTH - 1 < nstage) issue_b(DEPTH - 1, DEPTH - 1);
       for (int st = 0; st < nstage; st += 2) {
         step(st, RA, RB);
         if (st + 1 >= nstage) break;
@@ -591,16 +594,21 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void grouped_kernel(GroupedArgs a)
       // own loads up to A(st) (only B(st+1) was issued after it; B(st)
       // precedes it), passes the barrier -- every wave's stage st has landed
       // and every wave is done with stage st - 1 -- then refills the slots of
-      // stage st - 1 with A(st+1) and B(st+2) and multiplies stage st. ----
-      issue_b(0);
-      issue_a(0);
-      if (nstage > 1) issue_b(1);
+      // stage st - 1 with A(st+1) and B(st+2) and multiplies stage st.  Every
+      // step issues both (past the end of K, the last stage again into the
+      // free slots), so the count is the same along every path and the loop
+      // has no branch around its loads. ----
+      const int last = nstage - 1;
+      issue_b(0, 0);
+      issue_a(0, 0);
+      issue_b(min(1, last), 1);
+#pragma unroll 1
       for (int st = 0; st < nstage; ++st) {
-        if (st + 1 < nstage) wait_vm<C::LB>();
-        else wait_vm<0>();
+        __builtin_amdgcn_sched_barrier(0);   // nothing moves across a stage boundary
+        wait_vm<C::LB>();
         ring_barrier();
-        if (st + 1 < nstage) issue_a(st + 1);
-        if (st + 2 < nstage) issue_b(st + 2);
+        issue_a(min(st + 1, last), st + 1);
+        issue_b(min(st + 2, last), st + 2);
         if (rows_on) compute_fp8(st);
       }
     }
