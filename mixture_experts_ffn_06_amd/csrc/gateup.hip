@@ -15,17 +15,20 @@
 //    expert, group E).  Consecutive units are the M tiles of one N tile and
 //    run side by side on one XCD, so a tile's weights come from HBM once and
 //    from that XCD's L2 for the other M tiles.
-//  * A block is 4 waves, one per SIMD, each with the whole register file
-//    (512 per lane).  Wave w owns weight rows [32 w, 32 w + 32) of the gate
-//    half and of the up half of the tile, as the M side of the MFMA, and
-//    multiplies them with all token blocks (the N side): each lane then holds
-//    one token's results, so its activation scale is one value per token
-//    block and the block-scale promotion is one FMA per accumulator.
+//  * A block is 8 waves, two per SIMD.  Waves 0-3 multiply: wave w owns
+//    weight rows [32 w, 32 w + 32) of the gate half and of the up half of the
+//    tile, as the M side of the MFMA, and multiplies them with all token
+//    blocks (the N side): each lane then holds one token's results, so its
+//    activation scale is one value per token block and the block-scale
+//    promotion is one FMA per accumulator.  Waves 4-7 only move data: load
+//    wave 4 + w brings wave w's 64 weight rows, token block w and a share of
+//    the fp8 scales.  A load instruction holds the CU's address path for many
+//    cycles once HBM pushes back, and a wave cannot issue past it; kept out
+//    of the multiplying waves, those stalls no longer idle the MFMA.
 //  * Per K stage (128 bytes of every row: 64 bf16 or 128 e4m3 elements) the
 //    256 weight rows and the token rows go to LDS by direct global->LDS
-//    loads (each wave loads its own 64 weight rows and one 32-row token
-//    block, 16-byte pieces XOR-swizzled per row); three stages in flight, one
-//    barrier per stage for the shared token rows.
+//    loads (16-byte pieces XOR-swizzled per row); three slots, two stages in
+//    flight while one is multiplied, one barrier per stage.
 //  * Lane l multiplies row l % 32 of a block and takes 64 of the stage's
 //    bytes: pieces P(g, j) = 4 (j / 2) + 2 g + j % 2 for lane group g = l / 32,
 //    j = 0..3.  MFMA step s uses piece j = s (bf16) or half s % 2 of piece
@@ -54,7 +57,8 @@ namespace {
 
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-constexpr int kGuWaves = 4;
+constexpr int kGuWaves = 4;        // multiplying waves (and as many load waves)
+constexpr int kGuThreads = 2 * kGuWaves * kWave;
 constexpr int kGuRowBytes = 128;   // bytes of a row per stage
 constexpr int kGuWRows = 256;      // weight rows per unit (4 waves x (32 gate + 32 up))
 constexpr int kGuTBlocks = 4;      // token blocks of 32 rows per unit
@@ -71,8 +75,8 @@ struct GuCfg {
   static constexpr int T_BYTES = kGuTRows * kGuRowBytes;    // 16 KB
   static constexpr int SLOT = W_BYTES + S_BYTES + T_BYTES;
   static constexpr int LDS = kGuDepth * SLOT;
-  // vector-memory operations per wave per stage: 8 weight + 4 token loads
-  // (+ two 4-byte scale loads for fp8: this K block's and the next one's)
+  // vector-memory operations per load wave per stage: 8 weight + 4 token
+  // loads (+ two 4-byte scale loads for fp8: this K block's and the next one's)
   static constexpr int OPS = 8 + 4 + (DT == kFP8 ? 2 : 0);
   static_assert(OPS < 16 && 2 * OPS < 64, "vmcnt range");
   static_assert(LDS <= 152 * 1024, "LDS");
@@ -95,21 +99,23 @@ __device__ __forceinline__ int gu_swz(int r) { return (r >> 1) & 7; }
 __device__ __forceinline__ int gu_piece(int g, int j) { return 4 * (j >> 1) + 2 * g + (j & 1); }
 
 template <int DT>
-__global__ __launch_bounds__(kGuWaves * kWave, 1) void gu_kernel(GuArgs a) {
+__global__ __launch_bounds__(kGuThreads, 1) void gu_kernel(GuArgs a) {
   using C = GuCfg<DT>;
   extern __shared__ __align__(1024) uint8_t lds[];
   __shared__ int uoff[1026];             // unit prefix over the E + 1 groups
-  __shared__ int wsum[kGuWaves];
+  __shared__ int wsum[2 * kGuWaves];
   __shared__ float amax_w[kGuWaves][kGuTRows];
   const Dims &d = a.d;
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = uniform(tid >> 6);
+  const int wave_id = uniform(tid >> 6);
+  const bool loader = wave_id >= kGuWaves;                  // waves 4-7 load, 0-3 multiply
+  const int wave = loader ? wave_id - kGuWaves : wave_id;   // the multiplying wave served / itself
   const int G = d.E + (d.Is > 0 ? 1 : 0);
   const int *offsets = a.w.offsets;
 
   // ---- unit prefix: units(g) = ceil(rows_g / 128) * ntile_g ----
   {
-    constexpr int PER = (1025 + kGuWaves * kWave - 1) / (kGuWaves * kWave);
+    constexpr int PER = (1025 + kGuThreads - 1) / kGuThreads;
     int loc[PER];
     int sum = 0;
 #pragma unroll
@@ -129,11 +135,11 @@ __global__ __launch_bounds__(kGuWaves * kWave, 1) void gu_kernel(GuArgs a) {
       const int t = __shfl_up(incl, o);
       if (lane >= o) incl += t;
     }
-    if (lane == 63) wsum[wave] = incl;
+    if (lane == 63) wsum[wave_id] = incl;
     __syncthreads();
     int base = 0;
 #pragma unroll
-    for (int i = 0; i < kGuWaves; ++i) base += i < wave ? wsum[i] : 0;
+    for (int i = 0; i < 2 * kGuWaves; ++i) base += i < wave_id ? wsum[i] : 0;
     int run = base + incl - sum;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
@@ -206,23 +212,27 @@ __global__ __launch_bounds__(kGuWaves * kWave, 1) void gu_kernel(GuArgs a) {
     auto wuni = [&](int q) -> uint32_t {   // wave-uniform part of weight instruction q
       return wave_on ? static_cast<uint32_t>(8 * (q & 3) + (q >= 4 ? inter : 0)) * kbytes : 0u;
     };
-    uint32_t toff[4];
+    uint32_t toff[4] = {0u, 0u, 0u, 0u};
+    if (loader) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int rr = min(32 * wave + 8 * q + drow, rows - 1);
-      const int tok = shared ? row0 + rr : a.w.sorted_pair[seg0 + row0 + rr] / d.k;
-      toff[q] = static_cast<uint32_t>(tok) * kbytes + (p0 ^ (4 * (q & 1))) * 16;
+      for (int q = 0; q < 4; ++q) {
+        const int rr = min(32 * wave + 8 * q + drow, rows - 1);
+        const int tok = shared ? row0 + rr : a.w.sorted_pair[seg0 + row0 + rr] / d.k;
+        toff[q] = static_cast<uint32_t>(tok) * kbytes + (p0 ^ (4 * (q & 1))) * 16;
+      }
     }
     // fp8 scales of the stage's K block and of the next one (a scale area
-    // of 2 x 1 KB per slot): waves 0, 1 load the token rows' scales (64
-    // each), wave 2 the gate (even lanes) and up (odd lanes) weight-block
-    // scales, wave 3 the same again into a spare area (every wave issues two
-    // scale loads per stage)
+    // of 2 x 1 KB per slot): load waves 4, 5 load the token rows' scales (64
+    // each), wave 6 the gate (even lanes) and up (odd lanes) weight-block
+    // scales, wave 7 the same again into a spare area (every load wave issues
+    // two scale loads per stage)
     const float *sbase = nullptr;
     uint32_t soff = 0;
     if constexpr (DT == kFP8) {
       const int nkb = d.H / kQBlock;
-      if (wave < 2) {
+      if (!loader) {
+        // multiplying waves read the scales from LDS
+      } else if (wave < 2) {
         const int rr = min(64 * wave + lane, rows - 1);
         const int tok = shared ? row0 + rr : a.w.sorted_pair[seg0 + row0 + rr] / d.k;
         sbase = a.w.sx;
@@ -235,15 +245,12 @@ __global__ __launch_bounds__(kGuWaves * kWave, 1) void gu_kernel(GuArgs a) {
       }
     }
 
-    // Stage st goes to ring slot st % 3: weights, scales, tokens, issued in
-    // four parts (the gate block's weight rows, the up block's, the token
-    // block, the fp8 scales).  Each load instruction holds the CU's address
-    // path for ~16 cycles and a wave cannot issue past a load that waits for
-    // it, so the parts of a later stage are spread between a stage's MFMAs
-    // and the four waves issue different parts at a time.  In a bf16 half
-    // stage (the last one when K % 64 == 32) the pieces past the row's end
-    // load the piece 64 bytes before (valid memory; the steps that would use
-    // them are skipped).
+    // Stage st goes to ring slot st % 3: weights, scales, tokens, issued by
+    // the load wave in four parts (the gate block's weight rows, the up
+    // block's, the token block, the fp8 scales).  In a bf16 half stage (the
+    // last one when K % 64 == 32) the pieces past the row's end load the piece
+    // 64 bytes before (valid memory; the steps that would use them are
+    // skipped).
     auto issue_part = [&](int st, auto pc) {
       constexpr int part = decltype(pc)::value;
       uint8_t *sl = lds + (st % kGuDepth) * C::SLOT;
@@ -297,7 +304,7 @@ __global__ __launch_bounds__(kGuWaves * kWave, 1) void gu_kernel(GuArgs a) {
     // piece by piece, the MFMAs of each piece's steps in between; NT = token
     // blocks with rows (a template parameter keeps the MFMA sequence free of
     // branches).
-    auto stage = [&](int st, auto ntc, int dma_st) {
+    auto stage = [&](int st, auto ntc) {
       constexpr int NT = decltype(ntc)::value;
       const uint8_t *sl = lds + (st % kGuDepth) * C::SLOT;
       const uint32_t lw = lds_off(sl + 64 * wave * kGuRowBytes);
@@ -343,8 +350,6 @@ __global__ __launch_bounds__(kGuWaves * kWave, 1) void gu_kernel(GuArgs a) {
           lds_tie_b64(swr[0]);
           lds_tie_b64(swr[1]);
         }
-        // a quarter of a later stage's loads: part j
-        issue_part(dma_st, jc);
         if constexpr (DT == kBF16) {
           // step j: the piece as 8 bf16 values; a half stage runs steps 0, 1
           if (!(half && j >= 2)) {
@@ -391,35 +396,45 @@ __global__ __launch_bounds__(kGuWaves * kWave, 1) void gu_kernel(GuArgs a) {
     };
 
     __syncthreads();   // the previous unit is done with every slot and amax_w
-    // ---- the ring: stage st multiplies slot st % 3 while stages st + 1 and
-    // st + 2 load.  Every step issues one stage -- past the end the last
-    // stage again, cache hits into a free slot, never read -- and every wave
-    // loads its token block (past the tile's rows: its last row again), so
-    // each wave always has exactly OPS operations per stage outstanding and
-    // one count serves every step: waiting until OPS remain completes this
-    // stage's loads (in-order completion).  The barrier then makes every
-    // wave's loads of stage st visible and frees slot (st + 2) % 3, which all
-    // waves finished reading in stage st - 1 ----
-    auto run = [&](auto ntc) {
+    // ---- the ring: stage st is multiplied from slot st % 3 while stages
+    // st + 1 and st + 2 load.  A load wave issues stages 0 and 1, waits for
+    // stage 0, and at each stage's barrier (every multiplying wave is done
+    // with stage st - 1, whose slot stage st + 2 takes) issues stage st + 2
+    // -- past the end the last stage again, into a free slot no one reads, so
+    // each step leaves exactly OPS operations behind the one awaited -- and
+    // waits until only those are outstanding: stage st + 1 has landed by the
+    // next barrier (in-order completion).  The multiplying waves pass the
+    // same barriers.  Both sides take exactly nstage barriers per unit. ----
+    const int last = nstage - 1;
+    if (loader) {
       issue(0);
-      issue(min(1, nstage - 1));
+      issue(min(1, last));
+      wait_vm<C::OPS>();
 #pragma unroll 1
       for (int st = 0; st < nstage; ++st) {
-        __builtin_amdgcn_sched_barrier(0);   // nothing moves across a stage boundary
-        wait_vm<C::OPS>();
+        __builtin_amdgcn_sched_barrier(0);
         ring_barrier();
-        const int dma_st = min(st + 2, nstage - 1);
-        if (wave_on) stage(st, ntc, dma_st);
-        else issue(dma_st);
+        issue(min(st + 2, last));
+        wait_vm<C::OPS>();
       }
-    };
-    switch (ntb) {
-      case 1: run(std::integral_constant<int, 1>{}); break;
-      case 2: run(std::integral_constant<int, 2>{}); break;
-      case 3: run(std::integral_constant<int, 3>{}); break;
-      default: run(std::integral_constant<int, 4>{}); break;
+    } else {
+      auto run = [&](auto ntc) {
+#pragma unroll 1
+        for (int st = 0; st < nstage; ++st) {
+          __builtin_amdgcn_sched_barrier(0);   // nothing moves across a stage boundary
+          ring_barrier();
+          if (wave_on) stage(st, ntc);
+        }
+      };
+      switch (ntb) {
+        case 1: run(std::integral_constant<int, 1>{}); break;
+        case 2: run(std::integral_constant<int, 2>{}); break;
+        case 3: run(std::integral_constant<int, 3>{}); break;
+        default: run(std::integral_constant<int, 4>{}); break;
+      }
     }
-
+    // the trailing loads (the last stage again) land before the slots are
+    // refilled: the next unit's first barrier waits for every load
     // ---- epilogue: lane holds token row 32 t + lr, h columns
     // c0 + 8 (i / 4) + 4 lg + i % 4 for i = 0..15 ----
     if constexpr (DT == kBF16) {
@@ -427,7 +442,7 @@ __global__ __launch_bounds__(kGuWaves * kWave, 1) void gu_kernel(GuArgs a) {
 #pragma unroll
       for (int t = 0; t < kGuTBlocks; ++t) {
         const int rr = 32 * t + lr;
-        if (!wave_on || rr >= rows) continue;
+        if (loader || !wave_on || rr >= rows) continue;
         uint16_t *hr = h + static_cast<size_t>(seg0 + row0 + rr) * inter + c0 + 4 * lg;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -450,7 +465,7 @@ __global__ __launch_bounds__(kGuWaves * kWave, 1) void gu_kernel(GuArgs a) {
           am = fmaxf(am, fabsf(hv));
         }
         am = fmaxf(am, __shfl_xor(am, 32));
-        if (lg == 0) amax_w[wave][32 * t + lr] = am;
+        if (!loader && lg == 0) amax_w[wave][32 * t + lr] = am;
       }
       __syncthreads();
       uint8_t *h = static_cast<uint8_t *>(shared ? a.w.h_sh : a.w.h);
@@ -458,7 +473,7 @@ __global__ __launch_bounds__(kGuWaves * kWave, 1) void gu_kernel(GuArgs a) {
 #pragma unroll
       for (int t = 0; t < kGuTBlocks; ++t) {
         const int rr = 32 * t + lr;
-        if (rr >= rows) continue;
+        if (loader || rr >= rows) continue;
         float amax = 0.f;
 #pragma unroll
         for (int w = 0; w < kGuWaves; ++w) amax = fmaxf(amax, amax_w[w][rr]);
@@ -482,11 +497,11 @@ template <int DT>
 hipError_t gu_launch(const Dims &d, const Inputs &in, const Work &w, hipStream_t s) {
   using C = GuCfg<DT>;
   auto kern = gu_kernel<DT>;
-  static const KernelSetup su = kernel_setup(reinterpret_cast<const void *>(kern), kGuWaves * kWave, C::LDS);
+  static const KernelSetup su = kernel_setup(reinterpret_cast<const void *>(kern), kGuThreads, C::LDS);
   if (su.err != hipSuccess) return su.err;
   GuArgs ga{d, in, w, (d.I + 127) / 128, (d.Is + 127) / 128};
   const int grid = (device_cus() * su.blocks_per_cu + 7) / 8 * 8;
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(kGuWaves * kWave), C::LDS, s, ga);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kGuThreads), C::LDS, s, ga);
   return hipGetLastError();
 }
 
