@@ -77,7 +77,7 @@ typedef enum {
   MOE_GATE_SQRTSOFTPLUS = 2
 } moe_gating_t;
 
-/* Expert-path choice.  AUTO: fp32 weights -> SIMPLE; bf16 weights: m <= 128
+/* Expert-path choice.  AUTO: fp32 weights -> SIMPLE; bf16 weights: m <= 256
  * -> SMALL_M, else GROUPED; MXFP4 / MXFP8 weights: m <= 1024 -> SMALL_M, else
  * SIMPLE; fp8 weights: GROUPED.  The others force a path (for testing; every path
  * computes the same layer). */
@@ -85,7 +85,7 @@ typedef enum {
   MOE_PATH_AUTO = 0,
   MOE_PATH_SIMPLE = 1,   /* fp32 VALU kernels, any dtype */
   MOE_PATH_GROUPED = 2,  /* MFMA grouped GEMM, bf16 / fp8 */
-  MOE_PATH_SMALL_M = 3   /* weight-streaming path: bf16 m <= 128, MXFP4 / MXFP8 m <= 1024 */
+  MOE_PATH_SMALL_M = 3   /* weight-streaming path: bf16 m <= 256, MXFP4 / MXFP8 m <= 1024 */
 } moe_path_t;
 
 typedef enum {

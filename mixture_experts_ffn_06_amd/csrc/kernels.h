@@ -50,6 +50,7 @@ struct Work {
   int *lrank;           // [te] rank of a pair among same-expert pairs of its run
   int *active;          // [E] experts with >= 1 pair, ascending
   int *nactive;         // [1]
+  int *rboff;           // [E+1] per active slot: its first 16-row block (prefix of ceil(rows/16)); [nactive] = total
   int *perm_blk;        // [chunks][E] per-chunk counts, then starts (many pairs)
   uint8_t *xq;          // [m,H] fp8 codes of x
   float *sx;            // [m,H/128]

@@ -42,17 +42,17 @@ bool aligned(const void *p, size_t a) {
 // 16, each streaming its expert's weights once; the blocks of one expert run
 // side by side, so the repeats are mostly served from cache): bf16 weights
 // kBf16StreamMaxTokens, where the grouped MFMA path takes over (bf16 layer of
-// 128 experts, 2048 x 768: 32 tokens 154 K against 118 K tokens/s, 64 tokens
-// 267 K against 212 K, 128 tokens 440 K against 407 K; 192 tokens: 562 K
-// against 620 K, the repeated down streams cost more than they save); MX weights
-// kMxStreamMaxTokens.  With no grouped MX
-// GEMM the alternative is the VALU path (MXFP4, 64 tokens: 59.5 ms against
-// 0.14 ms); at 1024 tokens MXFP4 runs at 2.0 M tokens/s.
+// 128 experts, 2048 x 768, steps of 20: 64 tokens 269 K against 219 K
+// tokens/s, 128 tokens 510 K against 423 K, 256 tokens 915 K against 828 K;
+// 384 tokens 1.11 M against 1.21 M, the repeated streams cost more than they
+// save); MX weights kMxStreamMaxTokens.  With no grouped MX GEMM the
+// alternative is the VALU path (MXFP4, 64 tokens: 59.5 ms against 0.14 ms);
+// at 1024 tokens MXFP4 runs at 2.76 M tokens/s.
 constexpr int kMxStreamMaxTokens = 1024;
 
 bool is_mx(int weight_dtype) { return weight_dtype == MOE_MXFP4 || weight_dtype == MOE_MXFP8; }
 
-constexpr int kBf16StreamMaxTokens = 128;
+constexpr int kBf16StreamMaxTokens = 256;
 
 int small_m_limit(const moe_config_t &c) {
   return is_mx(c.weight_dtype) ? kMxStreamMaxTokens : kBf16StreamMaxTokens;
@@ -71,7 +71,7 @@ int resolve_path(const moe_config_t &c, int m) {
 // Byte sizes of every workspace region for m tokens.
 struct Layout {
   enum {
-    kLogits, kRpart, kCounts, kOffsets, kSorted, kSlot, kLrank, kActive, kNactive, kPermBlk, kXq,
+    kLogits, kRpart, kCounts, kOffsets, kSorted, kSlot, kLrank, kActive, kNactive, kRbOff, kPermBlk, kXq,
     kSx, kH, kHs, kHsh, kHshs, kY, kYsh, kN
   };
   size_t size[kN];
@@ -96,6 +96,7 @@ Layout layout(const moe_plan_s &p, int m) {
   L.size[Layout::kLrank] = te * 4;
   L.size[Layout::kActive] = E * 4;
   L.size[Layout::kNactive] = 4;
+  L.size[Layout::kRbOff] = (E + 1) * 4;
   L.size[Layout::kPermBlk] = static_cast<size_t>(moe::permute_chunks(static_cast<long>(te))) * E * 4;
   L.size[Layout::kXq] = fp8 ? m * H : 0;
   L.size[Layout::kSx] = fp8 ? m * (H / 128) * 4 : 0;
@@ -127,6 +128,7 @@ moe::Work carve(const Layout &L, void *ws) {
   w.lrank = static_cast<int *>(at(Layout::kLrank));
   w.active = static_cast<int *>(at(Layout::kActive));
   w.nactive = static_cast<int *>(at(Layout::kNactive));
+  w.rboff = static_cast<int *>(at(Layout::kRbOff));
   w.perm_blk = static_cast<int *>(at(Layout::kPermBlk));
   w.xq = static_cast<uint8_t *>(at(Layout::kXq));
   w.sx = static_cast<float *>(at(Layout::kSx));
@@ -161,8 +163,8 @@ int check_cfg(const moe_config_t &c) {
   const bool mx = c.weight_dtype == MOE_MXFP4 || c.weight_dtype == MOE_MXFP8;
   if (c.path == MOE_PATH_SMALL_M && c.weight_dtype != MOE_BF16 && !mx) return MOE_ERR_UNSUPPORTED;
   // the MX formats run on the weight-streaming path (one stage is 256 (FP4)
-  // or 128 (FP8) K elements) up to 16 tokens and on the VALU path above;
-  // there is no grouped MX GEMM
+  // or 128 (FP8) K elements) up to kMxStreamMaxTokens tokens and on the VALU
+  // path above; there is no grouped MX GEMM
   const int mx_k = c.weight_dtype == MOE_MXFP4 ? 256 : 128;
   if (mx && (c.hidden % mx_k || c.inter % mx_k || c.shared_inter % mx_k || c.path == MOE_PATH_GROUPED))
     return MOE_ERR_UNSUPPORTED;

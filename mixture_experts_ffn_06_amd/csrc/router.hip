@@ -243,7 +243,7 @@ __global__ __launch_bounds__(kFusedThreads) void topk_permute_kernel(Dims d, Inp
   __syncthreads();
   // ---- stable sort by expert ----
   permute_block(idx_s, d.te, E, wcnt, scan_tmp, w.counts, w.offsets, w.sorted_pair, w.slot_of_pair,
-                lrank, w.active, w.nactive);
+                lrank, w.active, w.nactive, w.rboff);
 }
 
 hipError_t launch_topk_permute(const Dims &d, const Inputs &in, const Work &w, int *topk_idx,

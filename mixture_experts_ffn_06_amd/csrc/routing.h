@@ -265,23 +265,31 @@ __device__ __forceinline__ void chunk_scatter(const int *topk_idx, int c0, int c
   }
 }
 
-// Expert totals -> counts, offsets, the active list; returns offsets[x] for
-// thread x (E <= kPermThreads).
+// Expert totals -> counts, offsets, the active list and, per active slot,
+// the prefix of its 16-row blocks (rboff[s] = sum over the active slots
+// before s of ceil(rows / 16), rboff[nactive] = their total: the
+// small-batch kernels' items); returns offsets[x] for thread x
+// (E <= kPermThreads).
 __device__ __forceinline__ int expert_offsets(int tot, int E, int *scan_tmp, int *__restrict__ counts,
                                               int *__restrict__ offsets, int *__restrict__ active,
-                                              int *__restrict__ nactive) {
+                                              int *__restrict__ nactive, int *__restrict__ rboff) {
   const int x = threadIdx.x;
-  int all_pairs, all_active;
+  int all_pairs, all_active, all_rb;
   const int off = block_exclusive_scan(x < E ? tot : 0, scan_tmp, &all_pairs);
   const int aoff = block_exclusive_scan(x < E && tot > 0 ? 1 : 0, scan_tmp, &all_active);
+  const int rb = block_exclusive_scan(x < E ? (tot + 15) >> 4 : 0, scan_tmp, &all_rb);
   if (x < E) {
     counts[x] = tot;
     offsets[x] = off;
-    if (tot > 0) active[aoff] = x;
+    if (tot > 0) {
+      active[aoff] = x;
+      rboff[aoff] = rb;
+    }
   }
   if (x == 0) {
     offsets[E] = all_pairs;
     *nactive = all_active;
+    rboff[all_active] = all_rb;
   }
   return off;
 }
@@ -291,13 +299,13 @@ __device__ __forceinline__ void permute_block(
     const int *topk_idx, int te, int E, int *wcnt, int *scan_tmp,
     int *__restrict__ counts, int *__restrict__ offsets,
     int *__restrict__ sorted_pair, int *__restrict__ slot_of_pair,
-    int *__restrict__ lrank, int *__restrict__ active, int *__restrict__ nactive) {
+    int *__restrict__ lrank, int *__restrict__ active, int *__restrict__ nactive, int *__restrict__ rboff) {
   chunk_ranks(topk_idx, 0, te, E, wcnt, lrank);
   const int x = threadIdx.x;
   int tot = 0;
   if (x < E)
     for (int w = 0; w < kPermWaves; ++w) tot += wcnt[w * E + x];
-  const int off = expert_offsets(tot, E, scan_tmp, counts, offsets, active, nactive);
+  const int off = expert_offsets(tot, E, scan_tmp, counts, offsets, active, nactive, rboff);
   chunk_bases(E, wcnt, off);
   chunk_scatter(topk_idx, 0, te, E, wcnt, lrank, sorted_pair, slot_of_pair);
 }

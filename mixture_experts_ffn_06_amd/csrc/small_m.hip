@@ -9,11 +9,13 @@
 // selected experts; forward_layer.rs, page 4: one dispatch covers all
 // selected experts of a decode step).
 //
-// Work item = (slot, column group): a slot is a routed expert with >= 1 row
-// (or the shared expert, whose rows are the m tokens); a column group is
-// NBLK weight blocks of 16 rows (gate/up: NBLK/2 blocks of w1 and the
-// matching NBLK/2 of w3; down: NBLK blocks of w2).  One wave (or KS waves
-// splitting K, their partial sums met in LDS) owns an item.
+// Work item = (16-row block of a slot, column group): a slot is a routed
+// expert with >= 1 row (or the shared expert, whose rows are the m tokens),
+// cut into ceil(rows / 16) row blocks (the permute scan leaves each active
+// slot's first block in rboff); a column group is NBLK weight blocks of 16
+// rows (gate/up: NBLK/2 blocks of w1 and the matching NBLK/2 of w3; down:
+// NBLK blocks of w2).  One wave (or KS waves splitting K, their partial sums
+// met in LDS) owns an item.
 //
 // HBM efficiency decides this kernel, and the MFMA operand layout (a load
 // instruction touching 16 weight rows, 64 bytes each) streams markedly slower
@@ -21,10 +23,12 @@
 // row: each direct global->LDS load covers 1024/RUN whole rows of RUN
 // contiguous bytes, into a per-wave ring of DEPTH stages, and the MFMA B
 // fragments are read back from LDS (16-byte pieces XOR-swizzled per row so
-// those reads are bank-conflict free).  The slot's <= 16 token rows (A, read
+// those reads are bank-conflict free).  The item's <= 16 token rows (A, read
 // from L2) go straight to registers, one stage ahead like the weights.  The
 // grid covers the largest item count the routing allows (the live count is
 // only known on the device; waves past it exit at once).
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 #include "launch.h"
@@ -59,6 +63,50 @@ __device__ __forceinline__ int sm_swz(int p, int r) {
   return p ^ ((r / (256 / RUN)) % (RUN / 16));
 }
 
+// An item: a 16-row block of a slot and a column group.  Routed items come
+// first: row block sr of all the active slots' blocks (the permute scan
+// leaves each active slot's first block in rboff), column groups fastest,
+// the slot found as the last one whose first block is <= sr; then the
+// shared expert's ceil(m / 16) row blocks of the tokens.  Items past those
+// have no rows (rows = 0).
+struct SmItem {
+  int e, seg0, rows, inter, cg;
+  bool shared;
+};
+__device__ __forceinline__ SmItem sm_item(const Dims &d, const Work &w, int item, int ipr, int ips) {
+  SmItem it{0, 0, 0, 0, 0, false};
+  const int na = uniform(*w.nactive);
+  const int nrb_r = uniform(w.rboff[na]);
+  const int nrb_s = (d.m + 15) >> 4;
+  if (item < nrb_r * ipr) {
+    const int sr = item / ipr;
+    it.cg = item - sr * ipr;
+    int lo = 0, hi = na - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (uniform(w.rboff[mid]) <= sr) lo = mid;
+      else hi = mid - 1;
+    }
+    const int rb = sr - uniform(w.rboff[lo]);
+    it.e = uniform(w.active[lo]);
+    const int s0 = uniform(w.offsets[it.e]);
+    const int r = uniform(w.offsets[it.e + 1]) - s0;
+    it.seg0 = s0 + 16 * rb;
+    it.rows = min(16, r - 16 * rb);
+    it.inter = d.I;
+  } else if (item < nrb_r * ipr + ips * nrb_s) {
+    const int t = item - nrb_r * ipr;
+    const int rb = t / ips;
+    it.cg = t - rb * ips;
+    it.shared = true;
+    it.e = d.E;
+    it.seg0 = 16 * rb;
+    it.rows = min(16, d.m - 16 * rb);   // the shared expert's rows are the tokens
+    it.inter = d.Is;
+  }
+  return it;
+}
+
 template <int MODE, int NBLK, int RUN, int DEPTH>
 __global__ __launch_bounds__(kSmBlockWaves * kWave) void sm_kernel(Dims d, Inputs in, Work w, int ks) {
   using C = SmCfg<NBLK, RUN, DEPTH>;
@@ -70,43 +118,17 @@ __global__ __launch_bounds__(kSmBlockWaves * kWave) void sm_kernel(Dims d, Input
   const int kp = uniform(wave % ks);
 
   // ---- the item: slot, block of 16 rows and column group ----
-  // Items (slot, row block rb, column group) run column groups fastest; a
-  // slot has nrb = ceil(m / 16) row blocks (an expert holds at most m rows),
-  // and row blocks past a slot's rows exit at once.
-  const int na = uniform(*w.nactive);
   const int ncol_r = MODE == kSmGateUp ? d.I : d.H;
   const int ipr = (ncol_r + CW - 1) / CW;                  // items per routed slot
   const int ips = d.Is > 0 ? ((MODE == kSmGateUp ? d.Is : d.H) + CW - 1) / CW : 0;
-  const int nrb = (d.m + 15) >> 4;
 
   f32x4_t acc[NBLK];
 #pragma unroll
   for (int j = 0; j < NBLK; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  int seg0 = 0, rows = 0, inter = 0, c0 = 0, ncol = 0, e = 0, cg = 0;
-  bool shared = false;
-  if (item < (na * ipr + ips) * nrb) {
-    int rb;
-    if (item < na * nrb * ipr) {
-      const int sr = item / ipr;
-      cg = item - sr * ipr;
-      const int slot = sr / nrb;
-      rb = sr - slot * nrb;
-      e = uniform(w.active[slot]);
-      seg0 = uniform(w.offsets[e]);
-      rows = uniform(w.offsets[e + 1]) - seg0;
-      inter = d.I;
-    } else {
-      shared = true;
-      e = d.E;
-      const int t = item - na * nrb * ipr;
-      rb = t / ips;
-      cg = t - rb * ips;
-      rows = d.m;
-      inter = d.Is;
-    }
-    seg0 = uniform(seg0 + 16 * rb);
-    rows = uniform(min(16, rows - 16 * rb));
-  }
+  const SmItem it = sm_item(d, w, item, ipr, ips);
+  const bool shared = it.shared;
+  const int e = it.e, seg0 = uniform(it.seg0), rows = uniform(it.rows), inter = it.inter, cg = it.cg;
+  int c0 = 0, ncol = 0;
   const bool live = rows > 0;
   if (live) {
     c0 = cg * CW;
@@ -348,43 +370,17 @@ __global__ __launch_bounds__(kSmBlockWaves * kWave, NB == 2 ? 4 : 2) void sm_mx_
   const int kp = uniform(wave % ks);
 
   // ---- the item: slot, block of 16 rows and column group ----
-  // Items (slot, row block rb, column group) run column groups fastest; a
-  // slot has nrb = ceil(m / 16) row blocks (an expert holds at most m rows),
-  // and row blocks past a slot's rows exit at once.
-  const int na = uniform(*w.nactive);
   const int ncol_r = MODE == kSmGateUp ? d.I : d.H;
   const int ipr = (ncol_r + CW - 1) / CW;
   const int ips = d.Is > 0 ? ((MODE == kSmGateUp ? d.Is : d.H) + CW - 1) / CW : 0;
-  const int nrb = (d.m + 15) >> 4;
 
   f32x4_t acc[NB];
 #pragma unroll
   for (int j = 0; j < NB; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  int seg0 = 0, rows = 0, inter = 0, c0 = 0, ncol = 0, e = 0, cg = 0;
-  bool shared = false;
-  if (item < (na * ipr + ips) * nrb) {
-    int rb;
-    if (item < na * nrb * ipr) {
-      const int sr = item / ipr;   // slot * nrb + rb
-      cg = item - sr * ipr;
-      const int slot = sr / nrb;
-      rb = sr - slot * nrb;
-      e = uniform(w.active[slot]);
-      seg0 = uniform(w.offsets[e]);
-      rows = uniform(w.offsets[e + 1]) - seg0;   // <= m
-      inter = d.I;
-    } else {
-      shared = true;
-      e = d.E;
-      const int t = item - na * nrb * ipr;
-      rb = t / ips;
-      cg = t - rb * ips;
-      rows = d.m;   // the shared expert's rows are the tokens
-      inter = d.Is;
-    }
-    seg0 = uniform(seg0 + 16 * rb);
-    rows = uniform(min(16, rows - 16 * rb));   // <= 0: no rows in this block
-  }
+  const SmItem it = sm_item(d, w, item, ipr, ips);
+  const bool shared = it.shared;
+  const int e = it.e, seg0 = uniform(it.seg0), rows = uniform(it.rows), inter = it.inter, cg = it.cg;
+  int c0 = 0, ncol = 0;
   const bool live = rows > 0;
   if (live) {
     c0 = cg * CW;
@@ -588,8 +584,18 @@ __global__ __launch_bounds__(kSmBlockWaves * kWave, NB == 2 ? 4 : 2) void sm_mx_
   }
 }
 
-// Grid for the largest possible item count (the number of slots is only
-// known on the device: items past it exit at once).  KS, the waves per item
+// The largest item count the routing allows (the row blocks are only known
+// on the device): the routed slots hold at most sum ceil(r_e / 16) <=
+// (te + 15 slots) / 16 blocks (and at most ceil(m / 16) each), the shared
+// expert ceil(m / 16).
+static long sm_items_max(const Dims &d, int slots, int ipr, int ips) {
+  const long nrb = (d.m + 15) / 16;
+  const long rb_routed = std::min(static_cast<long>(slots) * nrb, (static_cast<long>(d.te) + 15L * slots) / 16);
+  return rb_routed * ipr + static_cast<long>(ips) * nrb;
+}
+
+// Grid for the largest possible item count (items past the actual count exit
+// at once).  KS, the waves per item
 // (each streams 1/KS of K, partial sums meet in LDS), is at least 2 whenever
 // every wave keeps three stages, then the largest of 2, 4 that keeps the wave
 // tasks within three rounds of what fits at once and leaves every wave at
@@ -614,7 +620,7 @@ static hipError_t sm_launch(const Dims &d, const Inputs &in, const Work &w, hipS
   const int ncol_r = MODE == kSmGateUp ? d.I : d.H;
   const int ipr = (ncol_r + CW - 1) / CW;
   const int ips = d.Is > 0 ? ((MODE == kSmGateUp ? d.Is : d.H) + CW - 1) / CW : 0;
-  const long items = (static_cast<long>(slots) * ipr + ips) * ((d.m + 15) / 16);
+  const long items = sm_items_max(d, slots, ipr, ips);
   const long cap = static_cast<long>(device_cus()) * blocks_per_cu * kSmBlockWaves;
   // K stages of the shortest item (the shared expert's down K is I_s)
   const int kmin = MODE == kSmGateUp ? d.H : (d.Is > 0 && d.Is < d.I ? d.Is : d.I);
@@ -649,7 +655,7 @@ static hipError_t sm_mx_launch(const Dims &d, const Inputs &in, const Work &w, h
   const int ncol_r = MODE == kSmGateUp ? d.I : d.H;
   const int ipr = (ncol_r + CW - 1) / CW;
   const int ips = d.Is > 0 ? ((MODE == kSmGateUp ? d.Is : d.H) + CW - 1) / CW : 0;
-  const long items = (static_cast<long>(slots) * ipr + ips) * ((d.m + 15) / 16);
+  const long items = sm_items_max(d, slots, ipr, ips);
   const long cap = static_cast<long>(device_cus()) * blocks_per_cu * kSmBlockWaves;
   const int kmin = MODE == kSmGateUp ? d.H : (d.Is > 0 && d.Is < d.I ? d.Is : d.I);
   const int nst = kmin / C::KPS;

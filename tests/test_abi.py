@@ -59,8 +59,8 @@ def test_plan_rejects_bad_configs(kw, status):
 
 def test_plan_accepts_and_reports_paths_and_workspace():
     p = moe.MoePlan(**_cfg())
-    assert p.path_for(1) == "small_m" and p.path_for(128) == "small_m"
-    assert p.path_for(129) == "grouped"
+    assert p.path_for(1) == "small_m" and p.path_for(256) == "small_m"
+    assert p.path_for(257) == "grouped"
     assert p.workspace_bytes(0) >= 0
     assert p.workspace_bytes(64) > p.workspace_bytes(8) > 0
     assert moe.MoePlan(**_cfg(weight_dtype="f32", hidden=64, inter=32)).path_for(4) == "simple"

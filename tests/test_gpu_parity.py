@@ -214,7 +214,8 @@ def test_small_m_with_shared_expert(m):
 
 @pytest.mark.parametrize("wl", [RAGGED_BF16.replace(name="ragged_bf16_40", m=40),
                                 RAGGED_BF16.replace(name="ragged_bf16_128", m=128),
-                                SIGMOID_BF16], ids=["ragged40", "ragged128", "sigmoid77"])
+                                RAGGED_BF16.replace(name="ragged_bf16_256", m=256),
+                                SIGMOID_BF16], ids=["ragged40", "ragged128", "ragged256", "sigmoid77"])
 def test_small_m_above_16_tokens(wl):
     """bf16 weights above 16 tokens stream each expert's rows in blocks of
     16 (the shared expert's 40 or 77 rows: a partial last block)."""
@@ -224,6 +225,14 @@ def test_small_m_above_16_tokens(wl):
 @pytest.mark.timeout(300)
 def test_decode_bf16_64_tokens_small_m_all():
     wl = synth.WORKLOADS["decode_bf16"].replace(name="decode_bf16_64", m=64)
+    run_case(wl, path="small_m", lazy=True)
+
+
+@pytest.mark.timeout(300)
+def test_decode_bf16_256_tokens_small_m_all():
+    """The streaming path at its bf16 limit, every token: experts of up to
+    ~30 rows, two or three 16-row blocks each."""
+    wl = synth.WORKLOADS["decode_bf16"].replace(name="decode_bf16_256", m=256)
     run_case(wl, path="small_m", lazy=True)
 
 
