@@ -79,6 +79,9 @@ hipError_t launch_permute(const Dims &d, const int *topk_idx, const Work &w,
 // and the sort by expert
 constexpr int kRouterMaxSplits = 8;
 bool route_fused_ok(const Dims &d);
+// fp8 layers with m > 16 and H a multiple of 512: the router kernel also
+// writes xq and sx (no quantisation launch)
+bool router_quant_fused(const Dims &d);
 int router_splits(const Dims &d);
 hipError_t launch_topk_permute(const Dims &d, const Inputs &in, const Work &w, int *topk_idx,
                                float *topk_w, hipStream_t s);

@@ -268,7 +268,10 @@ int run_forward(moe_plan_t plan, int32_t m, const void *x, const void *router_w,
       stage(MOE_STAGE_PERMUTE, "permute", [&] {
         return fused ? hipSuccess : moe::launch_permute(d, topk_idx, w, s);
       }) &&
-      stage(MOE_STAGE_QUANT, "quant_x", [&] { return fp8 ? moe::launch_quant_x(d, in, w, s) : hipSuccess; }) &&
+      // fp8: the router kernel quantised x already where it could
+      stage(MOE_STAGE_QUANT, "quant_x", [&] {
+        return fp8 && !moe::router_quant_fused(d) ? moe::launch_quant_x(d, in, w, s) : hipSuccess;
+      }) &&
       stage(MOE_STAGE_GATEUP, "gate/up", [&] {
         switch (path) {
           case MOE_PATH_SIMPLE: return moe::launch_simple_gateup(d, in, w, s);

@@ -58,10 +58,20 @@ __global__ __launch_bounds__(256) void router_valu_kernel(
 //
 // With SPLIT (m <= 16 * MBW): blockIdx.y picks one of gridDim.y K ranges and
 // the block writes its partial tile to logits + blockIdx.y * m * E.
-template <int MBW, int NBW, bool SPLIT>
+//
+// With QUANT (fp8 layers, H a multiple of 512): the pass over x also
+// quantises it for the expert GEMMs (the quant_x_kernel rule: per token per
+// 128 columns, scale = amax / 448, code = round-to-nearest-even of x /
+// scale, an all-zero group gets scale 1).  Each wave's K range is then whole
+// 128-column groups and one batch of four 32-wide steps is one group: the
+// four lanes of a token row hold its 128 values.  Group g is written by the
+// block with blockIdx.x == g % gridDim.x (every expert tile reads the same
+// x rows), so the quantisation work is spread over all blocks.
+template <int MBW, int NBW, bool SPLIT, bool QUANT = false>
 __global__ __launch_bounds__(256) void router_mfma_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ wr,
-    float *__restrict__ logits, int m, int E, int H) {
+    float *__restrict__ logits, int m, int E, int H,
+    uint8_t *__restrict__ xq = nullptr, float *__restrict__ sx = nullptr) {
   __shared__ f32x4_t part[3][MBW * NBW][kWave];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int t0 = SPLIT ? 0 : blockIdx.y * 16 * MBW, e0 = blockIdx.x * 16 * NBW;
@@ -106,6 +116,42 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
               __builtin_bit_cast(bf16x8_t, av[q][i]), __builtin_bit_cast(bf16x8_t, bv[q][j]),
               acc[i][j], 0, 0, 0);
+    if constexpr (QUANT) {
+      const int g = s >> 2;   // this batch's 128-column group
+      if (g % static_cast<int>(gridDim.x) == static_cast<int>(blockIdx.x)) {
+#pragma unroll
+        for (int i = 0; i < MBW; ++i) {
+          float v[BATCH][8];
+          float am = 0.f;
+#pragma unroll
+          for (int q = 0; q < BATCH; ++q) {
+            const uint32_t u[4] = {av[q][i].x, av[q][i].y, av[q][i].z, av[q][i].w};
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              v[q][2 * c] = bf16_to_f32(static_cast<uint16_t>(u[c] & 0xffffu));
+              v[q][2 * c + 1] = bf16_to_f32(static_cast<uint16_t>(u[c] >> 16));
+              am = fmaxf(am, fmaxf(fabsf(v[q][2 * c]), fabsf(v[q][2 * c + 1])));
+            }
+          }
+          am = fmaxf(am, __shfl_xor(am, 16));   // the four lanes of this token row
+          am = fmaxf(am, __shfl_xor(am, 32));
+          const float sc = am > 0.f ? am / kE4M3Max : 1.0f;
+          const int t = t0 + 16 * i + (lane & 15);
+          if (t < m) {
+#pragma unroll
+            for (int q = 0; q < BATCH; ++q) {
+              uint32_t c[4];
+#pragma unroll
+              for (int h = 0; h < 4; ++h)
+                c[h] = static_cast<uint32_t>(fp8_pack2(v[q][2 * h] / sc, v[q][2 * h + 1] / sc)) & 0xffffu;
+              *reinterpret_cast<uint2 *>(xq + static_cast<size_t>(t) * H + (s + q) * 32 + kofs) =
+                  make_uint2(c[0] | (c[1] << 16), c[2] | (c[3] << 16));
+            }
+            if ((lane >> 4) == 0) sx[static_cast<size_t>(t) * (H / kQBlock) + g] = sc;
+          }
+        }
+      }
+    }
   }
   if (wave > 0) {
 #pragma unroll
@@ -135,9 +181,15 @@ template <int MBW, int NBW>
 static hipError_t launch_router_mfma(const Dims &d, const Inputs &in, const Work &w,
                                      hipStream_t s) {
   const dim3 grid((d.E + 16 * NBW - 1) / (16 * NBW), (d.m + 16 * MBW - 1) / (16 * MBW));
-  hipLaunchKernelGGL((router_mfma_kernel<MBW, NBW, false>), grid, dim3(256), 0, s,
-                     static_cast<const uint16_t *>(in.x),
-                     static_cast<const uint16_t *>(in.router_w), w.logits, d.m, d.E, d.H);
+  if (router_quant_fused(d))
+    hipLaunchKernelGGL((router_mfma_kernel<MBW, NBW, false, true>), grid, dim3(256), 0, s,
+                       static_cast<const uint16_t *>(in.x),
+                       static_cast<const uint16_t *>(in.router_w), w.logits, d.m, d.E, d.H, w.xq, w.sx);
+  else
+    hipLaunchKernelGGL((router_mfma_kernel<MBW, NBW, false>), grid, dim3(256), 0, s,
+                       static_cast<const uint16_t *>(in.x),
+                       static_cast<const uint16_t *>(in.router_w), w.logits, d.m, d.E, d.H,
+                       static_cast<uint8_t *>(nullptr), static_cast<float *>(nullptr));
   return hipGetLastError();
 }
 
@@ -179,6 +231,10 @@ constexpr int kFusedThreads = 1024;
 constexpr int kRouterBlocksTarget = 32;
 
 bool route_fused_ok(const Dims &d) { return d.wdt != kF32 && d.m <= 16; }
+
+bool router_quant_fused(const Dims &d) {
+  return d.wdt == kFP8 && !route_fused_ok(d) && d.H % (4 * kQBlock) == 0;
+}
 
 int router_splits(const Dims &d) {
   const int eb = (d.E + 15) / 16;
