@@ -73,10 +73,11 @@ def esz(dtype):
     return {"f32": 4, "bf16": 2, "fp8": 1, "mxfp4": 0.5, "mxfp8": 1}[dtype]
 
 
-# Source files of each expert-kernel family: HBM byte counters recorded in
-# profiles/hbm_traffic.json stand only while these files are unchanged.
+# Source files of the dominant (gate/up) kernel of each expert path: HBM byte
+# counters recorded in profiles/hbm_traffic.json stand only while these files
+# are unchanged.
 KERNEL_SOURCES = {"small_m": ("small_m.hip", "lds.h", "common.h", "kernels.h"),
-                  "grouped": ("grouped.hip", "lds.h", "common.h", "kernels.h")}
+                  "grouped": ("gateup.hip", "lds.h", "common.h", "kernels.h")}
 
 
 def recorded_traffic(workload, m, stage, path):
@@ -346,7 +347,7 @@ def measure(wl, m, args, launch, cpu):
     kernel_names = {"small_m": ("sm_mx_kernel<gateup, MXFP4>" if wl.dtype == "mxfp4" else
                                 "sm_mx_kernel<gateup, MXFP8>" if wl.dtype == "mxfp8" else
                                 "sm_kernel<gateup>"),
-                    "grouped": "grouped_kernel<gateup>", "simple": "simple_gateup_kernel"}
+                    "grouped": "gu_kernel<gateup>", "simple": "simple_gateup_kernel"}
     path = layers[0].plan.path_for(m)
     res = {
         "value": m / (ms_per_step * 1e-3), "unit": "tokens/s", "ms_per_step": ms_per_step,
