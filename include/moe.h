@@ -22,8 +22,11 @@
  *   - All work is enqueued on the caller's stream (a hipStream_t passed as
  *     void*; NULL = the default stream).  Outputs are valid once that stream
  *     has completed.
- *   - Arguments are validated before anything is enqueued; on an error the
- *     return value is non-zero, nothing is enqueued and outputs are untouched.
+ *   - Arguments are validated before anything is enqueued; on a validation
+ *     error the return value is non-zero, nothing is enqueued and outputs are
+ *     untouched.  A HIP error met while enqueueing (MOE_ERR_HIP) stops the
+ *     call at that stage: the stages before it stay enqueued on the stream,
+ *     and the outputs and the workspace are then undefined.
  *   - A zero-size launch is never made (page 3: a kernel with grid.x = 0 is
  *     an invalid launch, so the shared expert is skipped when absent);
  *     m == 0 returns MOE_OK with nothing enqueued.
@@ -93,7 +96,8 @@ typedef enum {
   MOE_ERR_INVALID_ARG = 1,  /* null pointer, bad size, misalignment       */
   MOE_ERR_UNSUPPORTED = 2,  /* valid but not supported by this build      */
   MOE_ERR_WORKSPACE = 3,    /* workspace too small                        */
-  MOE_ERR_HIP = 4           /* a HIP runtime call failed (see strerror)   */
+  MOE_ERR_HIP = 4,          /* a HIP runtime call failed (see strerror)   */
+  MOE_ERR_NO_MEMORY = 5     /* moe_plan could not allocate its host record */
 } moe_status_t;
 
 typedef struct {
@@ -167,8 +171,12 @@ typedef struct {
   float *y_shared;        /* [m, H] shared-expert down output, fp32         */
 } moe_debug_t;
 
-/* Validate cfg and create a plan (host memory only; no device work).
- * Errors: MOE_ERR_INVALID_ARG for non-positive sizes, topk outside
+/* Validate cfg and create a plan (host memory only; no device work): the
+ * layer's configuration, read once before the layer runs as forward.rs
+ * (page 1, forward_rows) reads the model configuration's hidden size, top-k
+ * experts, MoE intermediate size and number of experts.
+ * Errors: MOE_ERR_NO_MEMORY if the plan's host record cannot be allocated;
+ * MOE_ERR_INVALID_ARG for non-positive sizes, topk outside
  * [1, min(E,32)], E > 1024, unknown enums; MOE_ERR_UNSUPPORTED for fp8 with
  * H, I or I_s not multiples of 128, bf16/fp8 with H, I or I_s not multiples
  * of 32, MXFP4 (MXFP8) with H, I or I_s not multiples of 256 (128) or the
@@ -181,9 +189,13 @@ typedef struct {
 int moe_plan(const moe_config_t *cfg, moe_plan_t *plan_out);
 
 /* Bytes of device workspace that moe_forward needs for any call of up to m
- * tokens (0 on a NULL plan).  The workspace holds logits, the permutation,
- * the list of experts with rows, quantised activations, the sorted
- * intermediates and, for calls of <= 16 tokens, the router's partial sums. */
+ * tokens (0 on a NULL plan): the caller-preallocated scratch of the pages'
+ * layer (forward.rs, page 1, forward_rows: the decode arm's MoeDecodeScratch
+ * of logits, expert ids, weights and quantised h buffers; forward_prefill.rs,
+ * page 3, step 2: the top-k indices and weights in the shared scratch).  The
+ * workspace holds logits, the permutation, the list of experts with rows and
+ * their row-block prefix, quantised activations, the sorted intermediates
+ * and, for calls of <= 16 tokens, the router's partial sums. */
 size_t moe_workspace_bytes(moe_plan_t plan, int32_t m);
 
 /* Forward of the layer for m tokens (page 2, MoeV41::forward: x, m and a
@@ -262,7 +274,9 @@ int moe_path_for(moe_plan_t plan, int32_t m);
 /* Release a plan (NULL is ignored). */
 void moe_plan_destroy(moe_plan_t plan);
 
-/* Static text for a status code.  For MOE_ERR_HIP the text of the most
+/* Static text for a status code (library plumbing; the pages' layer code
+ * returns each launch's error to its caller with the failing call's text,
+ * forward.rs, page 1, forward_rows).  For MOE_ERR_HIP the text of the most
  * recent failing HIP call on this thread is appended; for MOE_ERR_WORKSPACE
  * the sizes of the most recent workspace error on this thread. */
 const char *moe_strerror(int status);

@@ -359,7 +359,7 @@ int moe_plan(const moe_config_t *cfg, moe_plan_t *plan_out) {
   const int st = check_cfg(*cfg);
   if (st != MOE_OK) return st;
   moe_plan_s *p = new (std::nothrow) moe_plan_s;
-  if (!p) return MOE_ERR_INVALID_ARG;
+  if (!p) return MOE_ERR_NO_MEMORY;
   p->cfg = *cfg;
   *plan_out = p;
   return MOE_OK;
@@ -438,6 +438,7 @@ const char *moe_strerror(int status) {
     case MOE_ERR_WORKSPACE:
       std::snprintf(buf, sizeof(buf), "workspace too small (%s)", g_err);
       return buf;
+    case MOE_ERR_NO_MEMORY: return "out of host memory";
     case MOE_ERR_HIP:
       std::snprintf(buf, sizeof(buf), "HIP error (%s)", g_err);
       return buf;

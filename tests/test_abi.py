@@ -133,6 +133,7 @@ def test_topk_argument_must_match_plan():
 def test_strerror_texts():
     assert moe.strerror(0) == "ok"
     assert "workspace" in moe.strerror(3)
+    assert "host memory" in moe.strerror(5)
     assert moe.strerror(99) == "unknown status"
 
 
