@@ -403,6 +403,50 @@ def test_mx_above_16_tokens_on_the_valu_path(fmt):
     run_case(wl, path="simple")
 
 
+@pytest.mark.parametrize("fmt", ["mxfp4", "mxfp8"])
+def test_mx_scale_bytes_at_the_format_edges(fmt):
+    """E8M0 scale bytes at the ends of the format (OCP MX: byte b means
+    2^(b - 127), byte 255 is NaN), on three of the experts the batch uses
+    (the busiest two and the least busy): the busiest with scale bytes 0 and
+    1 on every block (weights near 2^-127), the next with byte 254 (2^127) on
+    blocks whose elements are all zero codes, the least busy with byte 255 on
+    one gate/up block.  Tokens routed to that one must come out NaN on every
+    column, as in the oracle; every other token is checked against the oracle
+    as usual."""
+    import oracle.layer as OL
+    from tests.conftest import oracle_inputs
+    wl = MX_SMALL.replace(name=f"{fmt}_edges", dtype=fmt, shared_inter=0, shared_gate=False)
+    inp = synth.make_inputs(wl, device=DEV)
+    spec, kw = oracle_inputs(wl, inp)
+    counts = OL.forward(spec, **kw)["counts"]
+    used = [e for e in np.argsort(-counts, kind="stable").tolist() if counts[e] > 0]
+    e_tiny, e_big, e_nan = used[0], used[1], used[-1]
+    s13, s2, w13, w2 = inp["w13_scale"], inp["w2_scale"], inp["w13"], inp["w2"]
+    pk = 2 if fmt == "mxfp4" else 1
+    s13[e_tiny].copy_(torch.arange(s13[e_tiny].numel(), device=DEV).reshape(s13[e_tiny].shape) % 2)
+    s2[e_tiny].copy_(torch.arange(s2[e_tiny].numel(), device=DEV).reshape(s2[e_tiny].shape) % 2)
+    w13[e_big, :, : 32 // pk] = 0       # first K block of every gate/up row: zero codes ...
+    s13[e_big, :, 0] = 254              # ... at scale 2^127
+    w2[e_big, :, : 32 // pk] = 0
+    s2[e_big, :, 0] = 254
+    s13[e_nan, 5, 3] = 255              # one gate/up block: NaN
+    layer = make_layer(wl, inp, "small_m")
+    _say(f"case {wl.name} edge scale bytes (experts {e_tiny}, {e_big}, {e_nan})")
+    out, idx, w = layer(inp["x"])
+    torch.cuda.synchronize()
+    nan_tok = [t for t in range(wl.m) if e_nan in to_np(idx[t]).tolist()]
+    fin_tok = [t for t in range(wl.m) if t not in nan_tok]
+    assert nan_tok and fin_tok
+    o = to_np(out.float())
+    assert np.isnan(o[nan_tok]).all(), "tokens routed to the NaN-scaled expert must be NaN"
+    spec, kw = oracle_inputs(wl, inp)
+    ref = OL.forward(spec, **kw, tokens=np.array(nan_tok))
+    assert np.isnan(ref["out64"]).all()
+    rep = check_layer(wl, inp, out, idx, w, tokens=np.array(fin_tok))
+    _say(f"  -> {rep}")
+    assert rep.ok(), rep.failures
+
+
 def test_mxfp4_k_equals_E():
     wl = synth.Workload("mx_keqE", m=9, hidden=256, experts=4, topk=4, inter=512,
                         shared_inter=0, dtype="mxfp4", gating="softmax",
