@@ -81,14 +81,14 @@ typedef enum {
 } moe_gating_t;
 
 /* Expert-path choice.  AUTO: fp32 weights -> SIMPLE; bf16 weights: m <= 256
- * -> SMALL_M, else GROUPED; MXFP4 / MXFP8 weights: m <= 1024 -> SMALL_M, else
- * SIMPLE; fp8 weights: GROUPED.  The others force a path (for testing; every path
+ * -> SMALL_M, else GROUPED; MXFP4 / MXFP8 weights: SMALL_M at every m; fp8
+ * weights: GROUPED.  The others force a path (for testing; every path
  * computes the same layer). */
 typedef enum {
   MOE_PATH_AUTO = 0,
   MOE_PATH_SIMPLE = 1,   /* fp32 VALU kernels, any dtype */
   MOE_PATH_GROUPED = 2,  /* MFMA grouped GEMM, bf16 / fp8 */
-  MOE_PATH_SMALL_M = 3   /* weight-streaming path: bf16 m <= 256, MXFP4 / MXFP8 m <= 1024 */
+  MOE_PATH_SMALL_M = 3   /* weight-streaming path: bf16 m <= 256, MXFP4 / MXFP8 any m */
 } moe_path_t;
 
 typedef enum {
@@ -180,8 +180,8 @@ typedef struct {
  * [1, min(E,32)], E > 1024, unknown enums; MOE_ERR_UNSUPPORTED for fp8 with
  * H, I or I_s not multiples of 128, bf16/fp8 with H, I or I_s not multiples
  * of 32, MXFP4 (MXFP8) with H, I or I_s not multiples of 256 (128) or the
- * GROUPED path forced (the MX formats run on the weight-streaming path up to
- * 1024 tokens and on the VALU path above), SMALL_M forced with fp8/fp32 weights, or
+ * GROUPED path forced (the MX formats run on the weight-streaming path, or
+ * the VALU path when forced), SMALL_M forced with fp8/fp32 weights, or
  * sizes whose operands
  * reach 2 GiB (max_tokens * topk * max(H, I, I_s) elements, or one expert's
  * 2 * max(I, I_s) * H weight elements, at 2 bytes per bf16/fp8 element and 4

@@ -8,6 +8,7 @@
 //   -> unpermute + weighted reduce + shared blend.
 // No host synchronisation, no allocation, no host<->device copies.
 #include <algorithm>
+#include <limits>
 #include <hip/hip_runtime.h>
 
 #include <cstdio>
@@ -38,24 +39,24 @@ bool aligned(const void *p, size_t a) {
   return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0;
 }
 
-// Most tokens the weight-streaming path takes (an expert's rows in blocks of
-// 16, each streaming its expert's weights once; the blocks of one expert run
-// side by side, so the repeats are mostly served from cache): bf16 weights
-// kBf16StreamMaxTokens, where the grouped MFMA path takes over (bf16 layer of
-// 128 experts, 2048 x 768, steps of 20: 64 tokens 269 K against 219 K
-// tokens/s, 128 tokens 510 K against 423 K, 256 tokens 915 K against 828 K;
-// 384 tokens 1.11 M against 1.21 M, the repeated streams cost more than they
-// save); MX weights kMxStreamMaxTokens.  With no grouped MX GEMM the
-// alternative is the VALU path (MXFP4, 64 tokens: 59.5 ms against 0.14 ms);
-// at 1024 tokens MXFP4 runs at 2.76 M tokens/s.
-constexpr int kMxStreamMaxTokens = 1024;
-
+// Most tokens the weight-streaming path takes with bf16 weights (an expert's
+// rows in blocks of 16, each streaming its expert's weights once; the blocks
+// of one expert run side by side, so the repeats are mostly served from
+// cache): kBf16StreamMaxTokens, where the grouped MFMA path takes over (bf16
+// layer of 128 experts, 2048 x 768, steps of 20: 64 tokens 269 K against
+// 219 K tokens/s, 128 tokens 510 K against 423 K, 256 tokens 915 K against
+// 828 K; 384 tokens 1.11 M against 1.21 M, the repeated streams cost more than
+// they save).  MX weights take it at every batch size: an expert's weights
+// (1.5 MB of MXFP4 w13 at that shape) stay in its XCD's L2 while its blocks
+// run, and the alternative is the VALU path (MXFP4, 64 tokens: 59.5 ms against
+// 0.14 ms); MXFP4 runs at 2.71 M tokens/s at 1024 tokens, 3.12 M at 2048,
+// 3.53 M at 4096 and 3.72 M at 8192 (MXFP8 1.91 M, 2.10 M, 2.31 M, 2.38 M).
 bool is_mx(int weight_dtype) { return weight_dtype == MOE_MXFP4 || weight_dtype == MOE_MXFP8; }
 
 constexpr int kBf16StreamMaxTokens = 256;
 
 int small_m_limit(const moe_config_t &c) {
-  return is_mx(c.weight_dtype) ? kMxStreamMaxTokens : kBf16StreamMaxTokens;
+  return is_mx(c.weight_dtype) ? std::numeric_limits<int>::max() : kBf16StreamMaxTokens;
 }
 
 int resolve_path(const moe_config_t &c, int m) {
@@ -63,8 +64,6 @@ int resolve_path(const moe_config_t &c, int m) {
   if (c.weight_dtype == MOE_F32) return MOE_PATH_SIMPLE;
   if ((c.weight_dtype == MOE_BF16 || is_mx(c.weight_dtype)) && m <= small_m_limit(c))
     return MOE_PATH_SMALL_M;
-  // MX weights above that: the VALU path (no grouped MX GEMM)
-  if (is_mx(c.weight_dtype)) return MOE_PATH_SIMPLE;
   return MOE_PATH_GROUPED;
 }
 
@@ -163,8 +162,8 @@ int check_cfg(const moe_config_t &c) {
   const bool mx = c.weight_dtype == MOE_MXFP4 || c.weight_dtype == MOE_MXFP8;
   if (c.path == MOE_PATH_SMALL_M && c.weight_dtype != MOE_BF16 && !mx) return MOE_ERR_UNSUPPORTED;
   // the MX formats run on the weight-streaming path (one stage is 256 (FP4)
-  // or 128 (FP8) K elements) up to kMxStreamMaxTokens tokens and on the VALU
-  // path above; there is no grouped MX GEMM
+  // or 128 (FP8) K elements; the VALU path when forced); there is no grouped
+  // MX GEMM
   const int mx_k = c.weight_dtype == MOE_MXFP4 ? 256 : 128;
   if (mx && (c.hidden % mx_k || c.inter % mx_k || c.shared_inter % mx_k || c.path == MOE_PATH_GROUPED))
     return MOE_ERR_UNSUPPORTED;

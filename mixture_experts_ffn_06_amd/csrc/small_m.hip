@@ -1,6 +1,6 @@
-// Small-batch expert path: stream each selected expert's weights once per
-// block of 16 of its rows (bf16 weights up to 128 tokens, MX weights up to
-// 1024; an expert of r rows takes ceil(r / 16) blocks).
+// Weight-streaming expert path: stream each selected expert's weights once
+// per block of 16 of its rows (bf16 weights up to 256 tokens, MX weights at
+// every batch size; an expert of r rows takes ceil(r / 16) blocks).
 //
 // With at most 16 tokens every expert holds at most 16 rows, so the work is
 // a bandwidth-bound GEMV over the selected experts' weights (forward.rs,

@@ -69,7 +69,7 @@ def test_plan_accepts_and_reports_paths_and_workspace():
     assert moe.MoePlan(**_cfg(weight_dtype="mxfp8", inter=128, max_tokens=16)).path_for(3) == "small_m"
     mx = moe.MoePlan(**_cfg(weight_dtype="mxfp4", inter=256, max_tokens=2048))
     assert mx.path_for(17) == "small_m" and mx.path_for(1024) == "small_m"
-    assert mx.path_for(1025) == "simple"
+    assert mx.path_for(2048) == "small_m"
     assert lib().moe_workspace_bytes(None, 4) == 0
 
 

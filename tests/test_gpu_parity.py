@@ -395,6 +395,29 @@ def test_mx_streaming_many_tokens_sampled(fmt, m):
     run_case(wl, path="small_m", tokens=_sample(m), lazy=True)
 
 
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("fmt,m", [("mxfp4", 2048), ("mxfp8", 2048), ("mxfp4", 4096)])
+def test_mx_large_batches_every_expert(fmt, m):
+    """MX weights above 1024 tokens stay on the streaming path (experts of
+    ~128-256 rows: 8-16 row blocks each); the checked tokens' top-k reaches
+    every active expert."""
+    wl = synth.WORKLOADS[f"decode_{fmt}"].replace(name=f"decode_{fmt}_{m}", m=m)
+    inp = synth.make_inputs(wl, device=DEV)
+    layer = make_layer(wl, inp, "auto")
+    assert layer.plan.path_for(m) == "small_m"
+    dbg = debug_buffers(wl, m, DEV)
+    out, idx, w = layer(inp["x"], debug=dbg)
+    torch.cuda.synchronize()
+    g_idx, counts = to_np(idx), to_np(dbg["counts"])
+    active = [e for e in range(wl.experts) if counts[e] > 0]
+    tokens = sorted(set(cover_experts(g_idx, active)) | {0, m - 1})
+    _say(f"case {wl.name}: {len(active)} experts, {len(tokens)} tokens")
+    rep = check_layer(wl, inp, out, idx, w, tokens=tokens, debug=dbg, lazy=True)
+    _say(f"  -> {rep}")
+    assert rep.ok(), rep.failures
+    assert set(active) <= set(g_idx[tokens].reshape(-1).tolist())
+
+
 @pytest.mark.parametrize("fmt", ["mxfp4", "mxfp8"])
 def test_mx_above_16_tokens_on_the_valu_path(fmt):
     """Above 16 tokens MX weights run on the fp32 VALU path (AUTO), which
