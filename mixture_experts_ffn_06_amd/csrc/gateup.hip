@@ -505,15 +505,16 @@ hipError_t gu_launch(const Dims &d, const Inputs &in, const Work &w, hipStream_t
   return hipGetLastError();
 }
 
-}  // namespace
-
 bool gu_supported(const Dims &d) {
   if (d.wdt == kFP8) return d.H % kQBlock == 0 && d.I % kQBlock == 0 && d.Is % kQBlock == 0;
   if (d.wdt == kBF16) return d.H % 32 == 0 && d.I % 32 == 0 && d.Is % 32 == 0;
   return false;
 }
 
+}  // namespace
+
 hipError_t launch_gu(const Dims &d, const Inputs &in, const Work &w, hipStream_t s) {
+  if (!gu_supported(d)) return hipErrorInvalidValue;
   return d.wdt == kFP8 ? gu_launch<kFP8>(d, in, w, s) : gu_launch<kBF16>(d, in, w, s);
 }
 

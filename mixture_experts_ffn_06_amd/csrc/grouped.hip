@@ -1,45 +1,42 @@
-// Grouped expert GEMMs on MFMA (bf16 and fp8-e4m3 with 128x128 block scales).
+// Grouped down GEMM on MFMA (bf16 and fp8-e4m3 with 128x128 block scales):
+// y[rows, H] = h[rows, I] . w2[e]^T for each group's sorted rows.
 //
 // forward_prefill.rs (page 3, MoeLayer::forward_prefill doc comment) sorts
 // token rows by expert so that each expert's weight matrix is loaded once
 // for all of its tokens instead of once per token, then runs a grouped gate/up
 // GEMM, SiLU gating and a grouped down GEMM (steps 4-6).  Its notes on the
 // ported fp8 grouped GEMM describe a weight-stationary per-expert kernel with
-// double-buffered prefetch and two-level fp32 block-scale accumulation.
+// double-buffered prefetch and two-level fp32 block-scale accumulation.  (The
+// gate/up GEMM is gateup.hip.)
 //
 // Layout on CDNA4:
 //  * Work units are (group, M tile of BM rows, N tile); group e < E is a
 //    routed expert with its rows in sorted order, group E is the shared
-//    expert with one row per token.  BM (128 or 256) covers all rows of a
+//    expert with one row per token.  BM (96 to 192) covers all rows of a
 //    typical expert, so each weight byte is streamed from HBM once per call;
 //    a persistent grid walks the units, consecutive units on one XCD.
 //  * A block is WM x WN waves.  Per K stage every operand byte the block needs
-//    -- the token rows (A, gathered through the sort permutation) and the
-//    weight rows (B) -- is brought into LDS exactly once by direct
-//    global->LDS loads (no register staging), in 1 KB chunks spread evenly
-//    over the waves; the WM waves of a column group share its weight chunks,
-//    the WN waves of a row group share the token chunks.  The LDS ring is
-//    split in two: the token rows (served from L2) in 2 slots, the weights
-//    (from HBM) in DEPTH slots, so that several weight stages are in flight
-//    while a stage is multiplied.
+//    -- the h rows (A, one contiguous segment per group) and the w2 rows (B)
+//    -- is brought into LDS exactly once by direct global->LDS loads (no
+//    register staging), in 1 KB chunks spread evenly over the waves; the WM
+//    waves of a column group share its weight chunks, the WN waves of a row
+//    group share the h chunks.  The LDS ring is split in two: the h rows
+//    (served from L2) in 2 slots, the weights (from HBM) in DEPTH slots, so
+//    that several weight stages are in flight while a stage is multiplied.
 //  * Chunks are loaded in row order (consecutive lanes take consecutive 16
 //    bytes of a row: coalesced), with the 16-byte pieces of each row
 //    XOR-swizzled so that the MFMA-order LDS reads are bank-conflict free.
-//  * gate/up: a wave holds the same h columns of w1 and w3, so SiLU(g) * u is
-//    formed in registers (SwiGLU epilogue fused).  For fp8 a tile covers 128 h
-//    columns, one h scale group, and quantises h in the epilogue (row amax
-//    across the WN column waves through LDS).
 //  * fp8 two-level accumulation: every 128-wide K block is one MFMA
-//    (16x16x128, fp32 out) started from zero; its result times (activation
-//    row scale * weight block scale) is added to the fp32 accumulator.
+//    (16x16x128, fp32 out) started from zero; its result times (h row scale
+//    * weight block scale) is added to the fp32 accumulator.  The output y
+//    stays fp32 (it is not rounded to fp8 again, so the fp8 MFMA's summation
+//    error stays ~1e-4 of the output).
 #include "common.h"
 #include "kernels.h"
 #include "launch.h"
 #include "lds.h"
 
 namespace moe {
-
-enum : int { kGateUp = 0, kDown = 1 };
 
 __device__ __forceinline__ i32x8_t as_i32x8(u32x4_t a, u32x4_t b) {
   return i32x8_t{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
@@ -51,7 +48,7 @@ __device__ __forceinline__ i32x8_t as_i32x8(u32x4_t a, u32x4_t b) {
 // scale block).  A "stage block" is 16 rows x 128 bytes, moved by two 1 KB
 // load instructions of 8 whole 128-byte row runs each (row-contiguous runs
 // stream from HBM faster than the 64-byte pieces of the MFMA layout).
-template <int DT, int MODE, int NB, int WN, int WM, int MBW, int DEPTH, int STAGE_K>
+template <int DT, int NB, int WN, int WM, int MBW, int DEPTH, int STAGE_K>
 struct GCfg {
   static constexpr int NW = WN * WM;
   static constexpr int THREADS = NW * kWave;
@@ -83,8 +80,8 @@ struct GCfg {
   static constexpr int CPB = B_CH / NW;
   static constexpr int LA = CPA, LB = CPB + (SCALED ? 1 : 0);
   static constexpr int LDS_BYTES = DA * A_BYTES + DEPTH * B_STAGE;
-  // output columns: gate/up pairs NB/2 gate with NB/2 up blocks
-  static constexpr int WCOLS = MODE == kGateUp ? 16 * NB / 2 : 16 * NB;
+  // output columns per wave and per block
+  static constexpr int WCOLS = 16 * NB;
   static constexpr int NCOLS = WN * WCOLS;
   static_assert(STAGE_K % KSTEP == 0, "stage = whole MFMA steps");
   static_assert(RB == 128, "stage rows of 128 bytes (swizzle, chunk and read layout)");
@@ -92,8 +89,6 @@ struct GCfg {
   static_assert(!SCALED || (ROW_WAVES < NW && WN * NB <= 64), "fp8 scale areas");
   static_assert(SCALED ? DEPTH == 3 : (DEPTH >= 3 && (DEPTH - 2) * LB < 64),
                 "ring depth (fp8 loop: 3 weight slots; bf16: >= 3) and vmcnt range");
-  static_assert(MODE == kDown || NB % 2 == 0, "gate/up pairs");
-  static_assert(!(SCALED && MODE == kGateUp) || NCOLS == 128, "fp8 gate/up tile = one h scale group");
   static_assert(!SCALED || 128 % WCOLS == 0, "fp8: a wave's columns lie in one 128-wide scale block");
 };
 
@@ -103,23 +98,21 @@ struct GroupedArgs {
   Work w;
   int ntile_routed;   // N tiles of a routed expert
   int ntile_shared;   // N tiles of the shared expert
-  int order;          // kOrderGroups, kOrderInterleaveShared or kOrderSharedFirst (bf16)
+  int order;          // kOrderGroups or kOrderSharedFirst (bf16)
 };
 
 // Order in which the persistent blocks take the units.
 enum : int {
-  kOrderGroups = 0,            // routed experts in order, then the shared expert
-  kOrderInterleaveShared = 1,  // shared-expert units spread evenly among the routed ones
-  kOrderSharedFirst = 2        // shared-expert units first (longest first when I_s > I)
+  kOrderGroups = 0,       // routed experts in order, then the shared expert
+  kOrderSharedFirst = 1   // shared-expert units first (longest first when I_s > I)
 };
 
-template <int DT, int MODE, int NB, int WN, int WM, int MBW, int DEPTH, int STAGE_K>
+template <int DT, int NB, int WN, int WM, int MBW, int DEPTH, int STAGE_K>
 __global__ __launch_bounds__(WN * WM * 64, 1) void grouped_kernel(GroupedArgs a) {
-  using C = GCfg<DT, MODE, NB, WN, WM, MBW, DEPTH, STAGE_K>;
+  using C = GCfg<DT, NB, WN, WM, MBW, DEPTH, STAGE_K>;
   extern __shared__ __align__(1024) uint8_t lds[];
   __shared__ int uoff[1026];          // unit prefix over groups (E + 1 groups)
   __shared__ int wsum[C::NW];
-  __shared__ float wmax[WN][C::BM];   // fp8 gate/up epilogue: row amax per column group
   const Dims &d = a.d;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = uniform(tid >> 6);
@@ -181,25 +174,12 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void grouped_kernel(GroupedArgs a)
     const int u = r * P + xcd * per_xcd + slot;
     if (u >= total) continue;
     // Position u runs unit uu.  The S shared-expert units are last in group
-    // order.  kOrderInterleaveShared spreads them evenly over the positions,
-    // so their cache-served weight reads share each round with the HBM-bound
-    // routed units instead of forming a last round of their own: positions p
-    // where floor((p+1) S / total) steps up take shared unit
-    // floor(p S / total), the others routed unit p - floor(p S / total).
-    // kOrderSharedFirst runs them first, so that longer units (K = I_s > I in
-    // the down product) do not form the tail.  (fp8 kernels: compiled out.)
+    // order; kOrderSharedFirst runs them first, so that longer units (K = I_s
+    // > I) do not form the tail.  (fp8 kernels: compiled out.)
     int uu = u;
-    if (DT == kBF16 && a.order != kOrderGroups) {
+    if (DT == kBF16 && a.order == kOrderSharedFirst) {
       const int S = d.Is > 0 ? total - uoff[d.E] : 0;
-      if (S > 0 && S < total) {
-        if (a.order == kOrderSharedFirst) {
-          uu = u < S ? (total - S) + u : u - S;
-        } else {
-          const int before = static_cast<int>(static_cast<long>(u) * S / total);
-          const int next = static_cast<int>(static_cast<long>(u + 1) * S / total);
-          uu = next > before ? (total - S) + before : u - before;
-        }
-      }
+      if (S > 0 && S < total) uu = u < S ? (total - S) + u : u - S;
     }
     // ---- decode the unit (all values block-uniform) ----
     int lo = 0, hi = G - 1;
@@ -218,51 +198,31 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void grouped_kernel(GroupedArgs a)
     const int nmb = (rows + 15) >> 4;
     const int seg0 = shared ? 0 : uniform(offsets[g]);   // first sorted row of the group
     const int inter = shared ? d.Is : d.I;
-    const int K = MODE == kGateUp ? d.H : inter;
+    const int K = inter;
     const int kbytes = K * C::ESZ;
     const int nstage = (K + C::SK - 1) / C::SK;
-    const int ncol_lim = MODE == kGateUp ? inter : d.H;
 
     // ---- weights of the group ----
-    const uint8_t *Wb;
+    const uint8_t *Wb = static_cast<const uint8_t *>(shared ? a.in.sw2 : a.in.w2) +
+                        (shared ? 0 : static_cast<size_t>(g) * d.H * d.I * C::ESZ);
     const float *Ws = nullptr;
-    if (MODE == kGateUp) {
-      Wb = static_cast<const uint8_t *>(shared ? a.in.sw13 : a.in.w13) +
-           (shared ? 0 : static_cast<size_t>(g) * 2 * d.I * d.H * C::ESZ);
-      if (DT == kFP8)
-        Ws = shared ? a.in.sw13_scale
-                    : a.in.w13_scale + static_cast<size_t>(g) * (2 * d.I / kQBlock) * (d.H / kQBlock);
-    } else {
-      Wb = static_cast<const uint8_t *>(shared ? a.in.sw2 : a.in.w2) +
-           (shared ? 0 : static_cast<size_t>(g) * d.H * d.I * C::ESZ);
-      if (DT == kFP8)
-        Ws = shared ? a.in.sw2_scale
-                    : a.in.w2_scale + static_cast<size_t>(g) * (d.H / kQBlock) * (d.I / kQBlock);
-    }
-    // Output column of block j of column group cg (gate and up block of a
-    // pair share it), and its first weight row.  Blocks past the last column
-    // of a partial N tile read row 0 (valid memory) and store nothing.
-    auto col_of = [&](int cg, int j) -> int {
-      return ntile * C::NCOLS + cg * C::WCOLS + 16 * (MODE == kGateUp ? j % (NB / 2) : j);
-    };
+    if (DT == kFP8)
+      Ws = shared ? a.in.sw2_scale
+                  : a.in.w2_scale + static_cast<size_t>(g) * (d.H / kQBlock) * (d.I / kQBlock);
+    // Output column of block j of column group cg, and its first weight row.
+    // Blocks past the last column of a partial N tile read row 0 (valid
+    // memory) and store nothing.
+    auto col_of = [&](int cg, int j) -> int { return ntile * C::NCOLS + cg * C::WCOLS + 16 * j; };
     auto wrow_of = [&](int cg, int j) -> int {
       const int c = col_of(cg, j);
-      if (c >= ncol_lim) return 0;
-      return (MODE == kGateUp && j >= NB / 2) ? inter + c : c;
+      return c >= d.H ? 0 : c;
     };
     // Operand bases (block-uniform) and 32-bit byte offsets from them; the
-    // plan limits every operand to < 2 GiB so offsets fit.
-    const uint8_t *Ab;
-    if (MODE == kGateUp)
-      Ab = DT == kFP8 ? reinterpret_cast<const uint8_t *>(a.w.xq) : static_cast<const uint8_t *>(a.in.x);
-    else
-      Ab = static_cast<const uint8_t *>(shared ? a.w.h_sh : a.w.h);
+    // plan limits every operand to < 2 GiB so offsets fit.  The group's h
+    // rows are one contiguous segment of the sorted rows.
+    const uint8_t *Ab = static_cast<const uint8_t *>(shared ? a.w.h_sh : a.w.h);
     auto a_off = [&](int rr) -> uint32_t {
       rr = min(rr, rows - 1);   // rows past the tile's end repeat its last row
-      if (MODE == kGateUp) {
-        const int tok = shared ? row0 + rr : a.w.sorted_pair[seg0 + row0 + rr] / d.k;
-        return static_cast<uint32_t>(tok) * kbytes;
-      }
       return static_cast<uint32_t>(seg0 + row0 + rr) * kbytes;
     };
 
@@ -289,21 +249,15 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void grouped_kernel(GroupedArgs a)
       cpcB[q] = (lpiece ^ swz(rl)) * 16;
       coffB[q] = static_cast<uint32_t>(wrow_of(blk / NB, blk % NB) + rl) * kbytes + cpcB[q];
     }
-    // fp8 scales: waves < ROW_WAVES fetch row scales (lane l: row 64w + l),
+    // fp8 scales: waves < ROW_WAVES fetch h row scales (lane l: row 64w + l),
     // the other waves the weight-block scales (lane b: block b = cg*NB + j)
     const float *sbase = nullptr;
     uint32_t soff = 0;
     if constexpr (C::SCALED) {
       if (wave < C::ROW_WAVES) {
         const int rr = min(64 * wave + lane, rows - 1);
-        if (MODE == kGateUp) {
-          const int tok = shared ? row0 + rr : a.w.sorted_pair[seg0 + row0 + rr] / d.k;
-          sbase = a.w.sx;
-          soff = static_cast<uint32_t>(tok) * (d.H / kQBlock);
-        } else {
-          sbase = shared ? a.w.h_sh_scale : a.w.h_scale;
-          soff = static_cast<uint32_t>(seg0 + row0 + rr) * (inter / kQBlock);
-        }
+        sbase = shared ? a.w.h_sh_scale : a.w.h_scale;
+        soff = static_cast<uint32_t>(seg0 + row0 + rr) * (inter / kQBlock);
       } else {
         const int b = min(lane, WN * NB - 1);
         sbase = Ws;
@@ -340,7 +294,6 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void grouped_kernel(GroupedArgs a)
       if constexpr (C::SCALED) dma4_to_lds(sbase + (soff + st), sl + C::B_BYTES + wave * 256);
     };
 
-    constexpr int HALF = NB / 2;
     f32x4_t acc[MBW][NB];
 #pragma unroll
     for (int mb = 0; mb < MBW; ++mb)
@@ -423,12 +376,10 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void grouped_kernel(GroupedArgs a)
       }
     };
 
-    // fp8 stage st.  gate/up: e4m3 operands read from LDS, converted to
-    // their exact bf16 values in registers and multiplied on the bf16 MFMA:
-    // gfx950's fp8 MFMA does not sum its products in full fp32 (it drops
-    // product bits below ~2^-14 of the largest product in each group of
-    // eight), enough to move SwiGLU outputs across fp8 rounding boundaries.
-    // down: the fp8 MFMA itself, since its fp32 output is not rounded again.
+    // fp8 stage st on the fp8 MFMA: its fp32 output is not rounded to fp8
+    // again, so the MFMA's short summation (it drops product bits below
+    // ~2^-14 of the largest product in each group of eight) stays ~1e-4 of
+    // the output.
     auto compute_fp8 = [&](int st) {
       if constexpr (C::SCALED) {
         const uint8_t *sa = lds + (st % C::DA) * C::A_BYTES;
@@ -470,70 +421,24 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void grouped_kernel(GroupedArgs a)
           const uint32_t lb = lb0 + j0 * BLK;
           lds_read4<0, 0, BLK, BLK>(lb, lb + d1, lb, lb + d1, bq[0], bq[1], bq[2], bq[3]);
           lds_read4<2 * BLK, 2 * BLK, 3 * BLK, 3 * BLK>(lb, lb + d1, lb, lb + d1, bq[4], bq[5], bq[6], bq[7]);
-          // gate/up: weight blocks as bf16 (exact), [block][step of 8 K elements]
-          bf16x8_t bv[4][4];
-          if constexpr (MODE == kGateUp) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-#pragma unroll
-              for (int h = 0; h < 2; ++h) {
-                bv[j][2 * h] = e4m3x8_to_bf16(bq[2 * j + h].x, bq[2 * j + h].y);
-                bv[j][2 * h + 1] = e4m3x8_to_bf16(bq[2 * j + h].z, bq[2 * j + h].w);
-              }
-          }
 #pragma unroll
           for (int mb = 0; mb < MBW; ++mb) {
             if (mrow(mb) >= nmb) continue;   // no rows in this m-block
-            // row scale x weight-block scale, once per scale group: the
-            // wave's blocks are 16 * NB <= 64 consecutive 16-aligned output
-            // columns, so its gate blocks share one 128-row weight-scale
-            // block and its up blocks another (down: all share one)
-            constexpr int NG = MODE == kGateUp ? 2 : 1;
-            float sc[NG][4];
+            // h row scale x weight-block scale: the wave's blocks are 16 * NB
+            // <= 64 consecutive 16-aligned output columns, inside one
+            // 128-row weight-scale block
+            const float ws = __uint_as_float(sw[0][0]);
+            float sc[4];
 #pragma unroll
-            for (int gi = 0; gi < NG; ++gi) {
-              const int jr = gi * (NB / NG);
-              const float ws = __uint_as_float(sw[jr / 4][jr % 4]);
+            for (int i = 0; i < 4; ++i) sc[i] = __uint_as_float(sv[mb][i]) * ws;
+            const i32x8_t av = as_i32x8(aq[2 * mb], aq[2 * mb + 1]);
 #pragma unroll
-              for (int i = 0; i < 4; ++i) sc[gi][i] = __uint_as_float(sv[mb][i]) * ws;
-            }
-            if constexpr (MODE == kDown) {
-              // down: the fp8 MFMA (its result is not rounded to fp8 again;
-              // its accumulation error stays ~1e-4 of the output)
-              const i32x8_t av = as_i32x8(aq[2 * mb], aq[2 * mb + 1]);
+            for (int j = 0; j < 4; ++j) {
+              const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+              const f32x4_t p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                  av, as_i32x8(bq[2 * j], bq[2 * j + 1]), z, 0, 0, 0, 127, 0, 127);
 #pragma unroll
-              for (int j = 0; j < 4; ++j) {
-                const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
-                const f32x4_t p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                    av, as_i32x8(bq[2 * j], bq[2 * j + 1]), z, 0, 0, 0, 127, 0, 127);
-                const int gi = (j0 + j) / (NB / NG);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) acc[mb][j0 + j][i] = fmaf(p[i], sc[gi][i], acc[mb][j0 + j][i]);
-              }
-            } else {
-              // gate/up: the lane's 32 K elements as four bf16 steps of 8
-              // (exact), four 16x16x32 bf16 MFMAs per weight block from zero,
-              // then the two-level accumulation
-              bf16x8_t av[4];
-#pragma unroll
-              for (int h = 0; h < 2; ++h) {
-                av[2 * h] = e4m3x8_to_bf16(aq[2 * mb + h].x, aq[2 * mb + h].y);
-                av[2 * h + 1] = e4m3x8_to_bf16(aq[2 * mb + h].z, aq[2 * mb + h].w);
-              }
-              f32x4_t p[4];
-#pragma unroll
-              for (int j = 0; j < 4; ++j) p[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-              for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                  p[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[ks], bv[j][ks], p[j], 0, 0, 0);
-#pragma unroll
-              for (int j = 0; j < 4; ++j) {
-                const int gi = (j0 + j) / (NB / NG);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) acc[mb][j0 + j][i] = fmaf(p[j][i], sc[gi][i], acc[mb][j0 + j][i]);
-              }
+              for (int i = 0; i < 4; ++i) acc[mb][j0 + j][i] = fmaf(p[i], sc[i], acc[mb][j0 + j][i]);
             }
           }
         }
@@ -618,96 +523,32 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void grouped_kernel(GroupedArgs a)
     const int cl = lane & 15;
     const int rsub = (lane >> 4) * 4;
     const int col0 = ntile * C::NCOLS + wn * C::WCOLS;
-    if constexpr (MODE == kGateUp) {
-      uint8_t *hbase = static_cast<uint8_t *>(shared ? a.w.h_sh : a.w.h) +
-                       static_cast<size_t>(seg0 + row0) * inter * C::ESZ;
-      if constexpr (DT == kBF16) {
+    float *ybase = (shared ? a.w.y_sh : a.w.y) + static_cast<size_t>(seg0 + row0) * d.H;
 #pragma unroll
-        for (int mb = 0; mb < MBW; ++mb) {
+    for (int mb = 0; mb < MBW; ++mb) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int rr = mrow(mb) * 16 + rsub + i;
-            if (rr < rows) {
+      for (int i = 0; i < 4; ++i) {
+        const int rr = mrow(mb) * 16 + rsub + i;
+        if (rr < rows) {
 #pragma unroll
-              for (int j = 0; j < HALF; ++j)
-                if (col0 + 16 * j < ncol_lim)
-                  reinterpret_cast<uint16_t *>(hbase)[static_cast<size_t>(rr) * inter + col0 + 16 * j + cl] =
-                      f32_to_bf16(silu(acc[mb][j][i]) * acc[mb][j + HALF][i]);
-            }
-          }
-        }
-      } else {
-        // fp8: h is quantised per row per 128 columns = this tile's columns
-#pragma unroll
-        for (int mb = 0; mb < MBW; ++mb) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float am = 0.f;
-#pragma unroll
-            for (int j = 0; j < HALF; ++j) {
-              const float hv = silu(acc[mb][j][i]) * acc[mb][j + HALF][i];
-              acc[mb][j][i] = hv;
-              am = fmaxf(am, fabsf(hv));
-            }
-            am = fmaxf(am, __shfl_xor(am, 1));
-            am = fmaxf(am, __shfl_xor(am, 2));
-            am = fmaxf(am, __shfl_xor(am, 4));
-            am = fmaxf(am, __shfl_xor(am, 8));
-            if (cl == 0) wmax[wn][mrow(mb) * 16 + rsub + i] = am;
-          }
-        }
-        __syncthreads();
-        float *hs = (shared ? a.w.h_sh_scale : a.w.h_scale) +
-                    static_cast<size_t>(seg0 + row0) * (inter / kQBlock) + ntile;
-#pragma unroll
-        for (int mb = 0; mb < MBW; ++mb) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int rr = mrow(mb) * 16 + rsub + i;
-            if (rr < rows) {
-              float amax = 0.f;
-#pragma unroll
-              for (int w = 0; w < WN; ++w) amax = fmaxf(amax, wmax[w][rr]);
-              const float sc = amax > 0.f ? amax / kE4M3Max : 1.0f;
-#pragma unroll
-              for (int j = 0; j < HALF; ++j)
-                hbase[static_cast<size_t>(rr) * inter + col0 + 16 * j + cl] =
-                    static_cast<uint8_t>(fp8_pack2(acc[mb][j][i] / sc, 0.f) & 0xff);
-              if (wn == 0 && cl == 0) hs[static_cast<size_t>(rr) * (inter / kQBlock)] = sc;
-            }
-          }
-        }
-      }
-    } else {
-      float *ybase = (shared ? a.w.y_sh : a.w.y) + static_cast<size_t>(seg0 + row0) * d.H;
-#pragma unroll
-      for (int mb = 0; mb < MBW; ++mb) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int rr = mrow(mb) * 16 + rsub + i;
-          if (rr < rows) {
-#pragma unroll
-            for (int j = 0; j < NB; ++j)
-              if (col0 + 16 * j < ncol_lim)
-                ybase[static_cast<size_t>(rr) * d.H + col0 + 16 * j + cl] = acc[mb][j][i];
-          }
+          for (int j = 0; j < NB; ++j)
+            if (col0 + 16 * j < d.H)
+              ybase[static_cast<size_t>(rr) * d.H + col0 + 16 * j + cl] = acc[mb][j][i];
         }
       }
     }
   }
 }
 
-template <int DT, int MODE, int NB, int WN, int WM, int MBW, int DEPTH, int STAGE_K>
+template <int DT, int NB, int WN, int WM, int MBW, int DEPTH, int STAGE_K>
 static hipError_t launch_one(GroupedArgs ga, hipStream_t s) {
-  using C = GCfg<DT, MODE, NB, WN, WM, MBW, DEPTH, STAGE_K>;
-  auto kern = grouped_kernel<DT, MODE, NB, WN, WM, MBW, DEPTH, STAGE_K>;
+  using C = GCfg<DT, NB, WN, WM, MBW, DEPTH, STAGE_K>;
+  auto kern = grouped_kernel<DT, NB, WN, WM, MBW, DEPTH, STAGE_K>;
   static const KernelSetup su = kernel_setup(reinterpret_cast<const void *>(kern), C::THREADS, C::LDS_BYTES);
   if (su.err != hipSuccess) return su.err;
   const int blocks_per_cu = su.blocks_per_cu;
-  const int ncols_r = MODE == kGateUp ? ga.d.I : ga.d.H;
-  const int ncols_s = MODE == kGateUp ? ga.d.Is : ga.d.H;
-  ga.ntile_routed = (ncols_r + C::NCOLS - 1) / C::NCOLS;
-  ga.ntile_shared = (ncols_s + C::NCOLS - 1) / C::NCOLS;
+  ga.ntile_routed = (ga.d.H + C::NCOLS - 1) / C::NCOLS;
+  ga.ntile_shared = ga.ntile_routed;
   const int grid = (device_cus() * blocks_per_cu + 7) / 8 * 8;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(C::THREADS), C::LDS_BYTES, s, ga);
   return hipGetLastError();
@@ -717,35 +558,18 @@ static hipError_t launch_one(GroupedArgs ga, hipStream_t s) {
 // (fewer idle rows per tile).
 static bool big_tiles(const Dims &d) { return d.te > 96 * d.E; }
 
-hipError_t launch_grouped_gateup(const Dims &d, const Inputs &in,
-                                 const Work &w, hipStream_t s) {
-  GroupedArgs ga{d, in, w, 0, 0, kOrderGroups};
-  if (d.wdt == kBF16) {
-    // 256-row tiles (64 h columns, 2 x 4 waves) when experts average more
-    // than 96 rows, else 96-row tiles (128 h columns, 4 column waves), with
-    // the shared-expert units interleaved (prefill gate/up 243 -> 212 us;
-    // the same order made the down and the fp8 gate/up slower)
-    if (big_tiles(d)) return launch_one<kBF16, kGateUp, 4, 2, 4, 4, 4, 64>(ga, s);
-    ga.order = kOrderInterleaveShared;
-    return launch_one<kBF16, kGateUp, 4, 4, 1, 6, 4, 64>(ga, s);
-  }
-  // fp8: 128 h columns = one h scale group (4 column waves x 2 gate + 2 up
-  // blocks; 4 x 4 block tiles per wave keep the scale promotion cheap)
-  return launch_one<kFP8, kGateUp, 4, 4, 2, 4, 3, 128>(ga, s);   // 128 rows, 8 waves
-}
-
 hipError_t launch_grouped_down(const Dims &d, const Inputs &in, const Work &w,
                                hipStream_t s) {
   GroupedArgs ga{d, in, w, 0, 0, kOrderGroups};
   if (d.wdt == kBF16) {
-    if (big_tiles(d)) return launch_one<kBF16, kDown, 4, 4, 2, 4, 3, 64>(ga, s);   // 128 rows x 256 columns, 8 waves
+    if (big_tiles(d)) return launch_one<kBF16, 4, 4, 2, 4, 3, 64>(ga, s);   // 128 rows x 256 columns, 8 waves
     // 96-row tiles, shared-expert units first (prefill down 143 -> 136 us)
     ga.order = kOrderSharedFirst;
-    return launch_one<kBF16, kDown, 4, 4, 1, 6, 4, 64>(ga, s);
+    return launch_one<kBF16, 4, 4, 1, 6, 4, 64>(ga, s);
   }
   // 192 (128) rows x 256 columns, 8 waves
-  if (big_tiles(d)) return launch_one<kFP8, kDown, 4, 4, 2, 6, 3, 128>(ga, s);
-  return launch_one<kFP8, kDown, 4, 4, 2, 4, 3, 128>(ga, s);
+  if (big_tiles(d)) return launch_one<kFP8, 4, 4, 2, 6, 3, 128>(ga, s);
+  return launch_one<kFP8, 4, 4, 2, 4, 3, 128>(ga, s);
 }
 
 }  // namespace moe

@@ -98,14 +98,13 @@ hipError_t launch_quant_x(const Dims &d, const Inputs &in, const Work &w,
 // simple.hip (fp32 VALU, any storage format)
 hipError_t launch_simple_gateup(const Dims &d, const Inputs &in, const Work &w, hipStream_t s);
 hipError_t launch_simple_down(const Dims &d, const Inputs &in, const Work &w, hipStream_t s);
-// grouped.hip (MFMA grouped GEMM, bf16 / fp8 weights)
-hipError_t launch_grouped_gateup(const Dims &d, const Inputs &in, const Work &w, hipStream_t s);
+// grouped.hip (MFMA grouped down GEMM, bf16 / fp8 weights)
 hipError_t launch_grouped_down(const Dims &d, const Inputs &in, const Work &w, hipStream_t s);
-// gateup.hip (gate/up + SwiGLU on the bf16 32x32x16 MFMA; bf16 weights with
-// H % 32 == 0, fp8 weights)
-bool gu_supported(const Dims &d);
+// gateup.hip (grouped gate/up + SwiGLU on the bf16 32x32x16 MFMA; bf16 weights
+// with H, I and I_s multiples of 32, fp8 weights with multiples of 128: the
+// plan's own conditions; anything else returns hipErrorInvalidValue)
 hipError_t launch_gu(const Dims &d, const Inputs &in, const Work &w, hipStream_t s);
-// small_m.hip (weight streaming for m <= 16; bf16, MXFP4 and MXFP8 weights)
+// small_m.hip (weight streaming in 16-row blocks; bf16, MXFP4 and MXFP8 weights)
 hipError_t launch_small_m_gateup(const Dims &d, const Inputs &in, const Work &w, hipStream_t s);
 hipError_t launch_small_m_down(const Dims &d, const Inputs &in, const Work &w, hipStream_t s);
 

@@ -275,8 +275,7 @@ int run_forward(moe_plan_t plan, int32_t m, const void *x, const void *router_w,
         switch (path) {
           case MOE_PATH_SIMPLE: return moe::launch_simple_gateup(d, in, w, s);
           case MOE_PATH_SMALL_M: return moe::launch_small_m_gateup(d, in, w, s);
-          default: return moe::gu_supported(d) ? moe::launch_gu(d, in, w, s)
-                                                : moe::launch_grouped_gateup(d, in, w, s);
+          default: return moe::launch_gu(d, in, w, s);
         }
       }) &&
       stage(MOE_STAGE_DOWN, "down", [&] {
