@@ -26,9 +26,10 @@
 //    cycles once HBM pushes back, and a wave cannot issue past it; kept out
 //    of the multiplying waves, those stalls no longer idle the MFMA.
 //  * Per K stage (128 bytes of every row: 64 bf16 or 128 e4m3 elements) the
-//    256 weight rows and the token rows go to LDS by direct global->LDS
+//    256 weight rows and the token rows go to LDS by direct buffer->LDS
 //    loads (16-byte pieces XOR-swizzled per row); three slots, two stages in
-//    flight while one is multiplied, one barrier per stage.
+//    flight while one is multiplied, one barrier per stage.  The multiplying
+//    waves read LDS with ordinary loads, whose waits the compiler places.
 //  * Lane l multiplies row l % 32 of a block and takes 64 of the stage's
 //    bytes: pieces P(g, j) = 4 (j / 2) + 2 g + j % 2 for lane group g = l / 32,
 //    j = 0..3.  MFMA step s uses piece j = s (bf16) or half s % 2 of piece
@@ -97,6 +98,81 @@ __device__ __forceinline__ int gu_swz(int r) { return (r >> 1) & 7; }
 
 // Logical piece of the lane's j-th 16 bytes (lane group g).
 __device__ __forceinline__ int gu_piece(int g, int j) { return 4 * (j >> 1) + 2 * g + (j & 1); }
+
+// The load waves' part of one unit: stage st goes to ring slot st % 3 --
+// the gate block's weight rows, the up block's, the token block and the fp8
+// scales -- by direct loads to LDS.  A load wave issues stages 0 and 1,
+// waits for stage 0, and at each stage's barrier (every multiplying wave is
+// done with stage st - 1, whose slot stage st + 2 takes) issues stage st + 2
+// -- past the end the last stage again, into a free slot no one reads, so
+// each step leaves exactly OPS operations behind the one awaited -- and waits
+// until only those are outstanding: stage st + 1 has landed by the next
+// barrier (in-order completion).  It passes exactly nstage barriers, as the
+// multiplying waves do.
+//
+// The loads go through buffer resources (buffer_load ... lds): the compiler
+// counts LDS reads exactly in a function that holds them (with the
+// flat-encoded global_load_lds it falls back to waiting for all LDS reads),
+// and an offset past a resource's extent reads zeros instead of faulting.
+//
+// Weight instruction q (0..7) moves rows 8 (q % 4) + drow of the gate (q < 4)
+// or up block (wave-uniform offset (8 (q % 4) + (q >= 4 ? inter : 0)) *
+// wstep; wstep = 0 for a wave past the columns: valid memory, never read)
+// from lane offsets wl0 / wl1 (q even / odd); token instruction q from
+// t0..t3.  hi_bits bit b: the lane's piece of lane offset b lies in the
+// second half of the stage's 128 bytes (in a bf16 half stage -- the last one
+// when K % 64 == 32 -- such pieces load the piece 64 bytes before instead:
+// valid memory, and the steps that would use them are skipped).
+template <int DT>
+__device__ __forceinline__ void gu_load_unit(
+    __amdgpu_buffer_rsrc_t rW, __amdgpu_buffer_rsrc_t rA, __amdgpu_buffer_rsrc_t rS, uint32_t wl0,
+    uint32_t wl1, uint32_t hi_bits, uint32_t wstep, uint32_t inter, uint32_t kbytes, uint32_t t0, uint32_t t1,
+    uint32_t t2, uint32_t t3, uint32_t soff, int nstage, int wave, uint32_t lds0) {
+  using C = GuCfg<DT>;
+  const uint32_t wl[2] = {wl0, wl1};
+  const bool whi[2] = {(hi_bits & 1u) != 0, (hi_bits & 2u) != 0};
+  const uint32_t toff[4] = {t0, t1, t2, t3};
+  // part 0, 1: the gate / up block's weight rows; 2: the token rows; 3: the
+  // fp8 scales of this K block and of the next one (past the last block: the
+  // last block's again, unused)
+  auto issue_part = [&](int st, auto pc) {
+    constexpr int part = decltype(pc)::value;
+    const uint32_t sl = lds0 + (st % kGuDepth) * C::SLOT;
+    const uint32_t kb = static_cast<uint32_t>(st) * kGuRowBytes;
+    const bool half = DT == kBF16 && kb + kGuRowBytes > kbytes;
+    const uint32_t kb2 = half ? kb - 64 : kb;
+    if constexpr (part < 2) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int q = 4 * part + i;
+        const uint32_t wu = static_cast<uint32_t>(8 * (q & 3) + (q >= 4 ? inter : 0)) * wstep;
+        buf16_to_lds(rW, wl[q & 1] + wu + (whi[q & 1] ? kb2 : kb), lds_ptr(sl + (8 * wave + q) * 1024));
+      }
+    } else if constexpr (part == 2) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        buf16_to_lds(rA, toff[q] + (whi[q & 1] ? kb2 : kb),
+                     lds_ptr(sl + C::W_BYTES + C::S_BYTES + (4 * wave + q) * 1024));
+    } else {
+      if constexpr (DT == kFP8) {
+        buf4_to_lds(rS, 4 * (soff + st), lds_ptr(sl + C::W_BYTES + 256 * wave));
+        buf4_to_lds(rS, 4 * (soff + min(st + 1, nstage - 1)), lds_ptr(sl + C::W_BYTES + 1024 + 256 * wave));
+      }
+    }
+  };
+  auto issue = [&](int st) { static_for<0, 4>([&](auto pc) { issue_part(st, pc); }); };
+  const int last = nstage - 1;
+  issue(0);
+  issue(min(1, last));
+  wait_vm<C::OPS>();
+#pragma unroll 1
+  for (int st = 0; st < nstage; ++st) {
+    __builtin_amdgcn_sched_barrier(0);
+    ring_barrier();
+    issue(min(st + 2, last));
+    wait_vm<C::OPS>();
+  }
+}
 
 template <int DT>
 __global__ __launch_bounds__(kGuThreads, 1) void gu_kernel(GuArgs a) {
@@ -209,9 +285,6 @@ __global__ __launch_bounds__(kGuThreads, 1) void gu_kernel(GuArgs a) {
     const uint32_t wlane[2] = {static_cast<uint32_t>(wrow0) * kbytes + p0 * 16,
                                static_cast<uint32_t>(wrow0) * kbytes + (p0 ^ 4) * 16};
     const bool whi[2] = {p0 >= 4, (p0 ^ 4) >= 4};
-    auto wuni = [&](int q) -> uint32_t {   // wave-uniform part of weight instruction q
-      return wave_on ? static_cast<uint32_t>(8 * (q & 3) + (q >= 4 ? inter : 0)) * kbytes : 0u;
-    };
     uint32_t toff[4] = {0u, 0u, 0u, 0u};
     if (loader) {
 #pragma unroll
@@ -245,43 +318,6 @@ __global__ __launch_bounds__(kGuThreads, 1) void gu_kernel(GuArgs a) {
       }
     }
 
-    // Stage st goes to ring slot st % 3: weights, scales, tokens, issued by
-    // the load wave in four parts (the gate block's weight rows, the up
-    // block's, the token block, the fp8 scales).  In a bf16 half stage (the
-    // last one when K % 64 == 32) the pieces past the row's end load the piece
-    // 64 bytes before (valid memory; the steps that would use them are
-    // skipped).
-    auto issue_part = [&](int st, auto pc) {
-      constexpr int part = decltype(pc)::value;
-      uint8_t *sl = lds + (st % kGuDepth) * C::SLOT;
-      const uint32_t kb = static_cast<uint32_t>(st) * kGuRowBytes;
-      const bool half = DT == kBF16 && kb + kGuRowBytes > static_cast<uint32_t>(kbytes);
-      const uint32_t kb2 = half ? kb - 64 : kb;
-      if constexpr (part < 2) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int q = 4 * part + i;
-          dma16_to_lds(Wb + (wlane[q & 1] + wuni(q) + (whi[q & 1] ? kb2 : kb)), sl + (8 * wave + q) * 1024);
-        }
-
-      } else if constexpr (part == 2) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          dma16_to_lds(Ab + (toff[q] + (whi[q & 1] ? kb2 : kb)),
-                       sl + C::W_BYTES + C::S_BYTES + (4 * wave + q) * 1024);
-      } else {
-        if constexpr (DT == kFP8) {
-          // the next K block's scales too (past the last block: the last
-          // block's again, unused)
-          dma4_to_lds(sbase + (soff + st), sl + C::W_BYTES + 256 * wave);
-          dma4_to_lds(sbase + (soff + min(st + 1, nstage - 1)), sl + C::W_BYTES + 1024 + 256 * wave);
-        }
-      }
-    };
-    auto issue = [&](int st) {
-      static_for<0, 4>([&](auto pc) { issue_part(st, pc); });
-    };
-
     // ---- accumulators: [weight block: 0 gate, 1 up][token block] ----
     f32x16_t acc[2][kGuTBlocks];
 #pragma unroll
@@ -300,56 +336,44 @@ __global__ __launch_bounds__(kGuThreads, 1) void gu_kernel(GuArgs a) {
     // take) but no registers for partials, and each accumulator block's
     // rescale sits between the last MFMAs of the others.
     // One stage: the lane's LDS reads of operand pieces (fp8: after its
-    // token and weight-block scales), issued one piece ahead and waited for
-    // piece by piece, the MFMAs of each piece's steps in between; NT = token
-    // blocks with rows (a template parameter keeps the MFMA sequence free of
-    // branches).
+    // token and weight-block scales), issued one piece ahead, the MFMAs of
+    // each piece's steps in between; NT = token blocks with rows (a template
+    // parameter keeps the MFMA sequence free of branches).
     auto stage = [&](int st, auto ntc) {
       constexpr int NT = decltype(ntc)::value;
       const uint8_t *sl = lds + (st % kGuDepth) * C::SLOT;
-      const uint32_t lw = lds_off(sl + 64 * wave * kGuRowBytes);
-      const uint32_t lt = lds_off(sl + C::W_BYTES + C::S_BYTES);
+      const uint8_t *lw = sl + 64 * wave * kGuRowBytes;
+      const uint8_t *lt = sl + C::W_BYTES + C::S_BYTES;
       const bool half = DT == kBF16 && static_cast<uint32_t>(st + 1) * kGuRowBytes > static_cast<uint32_t>(kbytes);
       u32x4_t wr[4][2], tr[4][NT];
       uint32_t sxr[2][NT];     // [this K block, next][token block]
       u32x2_t swr[2];
       if constexpr (DT == kFP8) {
-        const uint32_t ls = lds_off(sl + C::W_BYTES);
+        const uint8_t *ls = sl + C::W_BYTES;
         static_for<0, NT>([&](auto tc) {
           constexpr int t = decltype(tc)::value;
-          lds_issue_b32<128 * t>(ls + 4 * lr, sxr[0][t]);
-          lds_issue_b32<1024 + 128 * t>(ls + 4 * lr, sxr[1][t]);
+          sxr[0][t] = lds_load<uint32_t>(ls + 4 * lr + 128 * t);
+          sxr[1][t] = lds_load<uint32_t>(ls + 4 * lr + 1024 + 128 * t);
         });
-        lds_issue_b64<512>(ls, swr[0]);
-        lds_issue_b64<1024 + 512>(ls, swr[1]);
+        swr[0] = lds_load<u32x2_t>(ls + 512);
+        swr[1] = lds_load<u32x2_t>(ls + 1024 + 512);
       }
-      auto issue_piece = [&](auto jc) {
+      auto load_piece = [&](auto jc) {
         constexpr int j = decltype(jc)::value;
-        lds_issue<0>(lw + loff[j], wr[j][0]);
-        lds_issue<32 * kGuRowBytes>(lw + loff[j], wr[j][1]);
+        wr[j][0] = lds_load<u32x4_t>(lw + loff[j]);
+        wr[j][1] = lds_load<u32x4_t>(lw + loff[j] + 32 * kGuRowBytes);
         static_for<0, NT>([&](auto tc) {
           constexpr int t = decltype(tc)::value;
-          lds_issue<32 * kGuRowBytes * t>(lt + loff[j], tr[j][t]);
+          tr[j][t] = lds_load<u32x4_t>(lt + loff[j] + 32 * kGuRowBytes * t);
         });
       };
-      issue_piece(std::integral_constant<int, 0>{});
+      load_piece(std::integral_constant<int, 0>{});
       static_for<0, 4>([&](auto jc) {
         constexpr int j = decltype(jc)::value;
-        if constexpr (j + 1 < 4) issue_piece(std::integral_constant<int, j + 1>{});
-        // after piece j + 1 was issued: wait for piece j
-        if constexpr (j < 3) asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(2 + NT) : "memory");
-        else asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        lds_tie(wr[j][0]);
-        lds_tie(wr[j][1]);
-        static_for<0, NT>([&](auto tc) { lds_tie(tr[j][decltype(tc)::value]); });
-        if constexpr (DT == kFP8 && j == 0) {
-          static_for<0, NT>([&](auto tc) {
-            lds_tie_b32(sxr[0][decltype(tc)::value]);
-            lds_tie_b32(sxr[1][decltype(tc)::value]);
-          });
-          lds_tie_b64(swr[0]);
-          lds_tie_b64(swr[1]);
-        }
+        // the reads of piece j + 1 go out before the MFMAs of piece j; the
+        // compiler waits for piece j's values just before their first use
+        if constexpr (j + 1 < 4) load_piece(std::integral_constant<int, j + 1>{});
+        __builtin_amdgcn_sched_barrier(0);
         if constexpr (DT == kBF16) {
           // step j: the piece as 8 bf16 values; a half stage runs steps 0, 1
           if (!(half && j >= 2)) {
@@ -397,30 +421,29 @@ __global__ __launch_bounds__(kGuThreads, 1) void gu_kernel(GuArgs a) {
 
     __syncthreads();   // the previous unit is done with every slot and amax_w
     // ---- the ring: stage st is multiplied from slot st % 3 while stages
-    // st + 1 and st + 2 load.  A load wave issues stages 0 and 1, waits for
-    // stage 0, and at each stage's barrier (every multiplying wave is done
-    // with stage st - 1, whose slot stage st + 2 takes) issues stage st + 2
-    // -- past the end the last stage again, into a free slot no one reads, so
-    // each step leaves exactly OPS operations behind the one awaited -- and
-    // waits until only those are outstanding: stage st + 1 has landed by the
-    // next barrier (in-order completion).  The multiplying waves pass the
-    // same barriers.  Both sides take exactly nstage barriers per unit. ----
-    const int last = nstage - 1;
+    // st + 1 and st + 2 load (gu_load_unit); both sides take exactly nstage
+    // barriers per unit. ----
     if (loader) {
-      issue(0);
-      issue(min(1, last));
-      wait_vm<C::OPS>();
-#pragma unroll 1
-      for (int st = 0; st < nstage; ++st) {
-        __builtin_amdgcn_sched_barrier(0);
-        ring_barrier();
-        issue(min(st + 2, last));
-        wait_vm<C::OPS>();
-      }
+      // buffer extents: the group's w13 rows, the m token rows, the scale
+      // table this wave reads
+      const uint32_t wbytes = static_cast<uint32_t>(2 * inter) * kbytes;
+      const uint32_t abytes = static_cast<uint32_t>(d.m) * kbytes;
+      const uint32_t sbytes = DT != kFP8 ? 4u
+                            : wave < 2 ? static_cast<uint32_t>(d.m) * (d.H / kQBlock) * 4u
+                                       : static_cast<uint32_t>(2 * inter / kQBlock) * (d.H / kQBlock) * 4u;
+      gu_load_unit<DT>(buffer_rsrc(Wb, wbytes), buffer_rsrc(Ab, abytes),
+                       buffer_rsrc(DT == kFP8 ? sbase : a.w.sx, sbytes), wlane[0], wlane[1],
+                       (whi[0] ? 1u : 0u) | (whi[1] ? 2u : 0u),
+                       wave_on ? static_cast<uint32_t>(kbytes) : 0u, static_cast<uint32_t>(inter),
+                       static_cast<uint32_t>(kbytes), toff[0], toff[1], toff[2], toff[3], soff, nstage, wave,
+                       lds_off(lds));
     } else {
       auto run = [&](auto ntc) {
 #pragma unroll 1
         for (int st = 0; st < nstage; ++st) {
+          // every read of the previous stage has landed before the barrier
+          // that hands its slot to the loads
+          wait_lgkm<0>();
           __builtin_amdgcn_sched_barrier(0);   // nothing moves across a stage boundary
           ring_barrier();
           if (wave_on) stage(st, ntc);

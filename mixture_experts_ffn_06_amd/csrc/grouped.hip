@@ -265,6 +265,17 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void grouped_kernel(GroupedArgs a)
       }
     }
 
+    // Buffer resources over the operands (an offset past an extent reads
+    // zeros): the h rows of the group's kind, the group's w2, this wave's
+    // scale table.
+    const __amdgpu_buffer_rsrc_t rA = buffer_rsrc(Ab, static_cast<uint32_t>(shared ? d.m : d.te) * kbytes);
+    const __amdgpu_buffer_rsrc_t rW = buffer_rsrc(Wb, static_cast<uint32_t>(d.H) * kbytes);
+    __amdgpu_buffer_rsrc_t rS = rA;
+    if constexpr (C::SCALED)
+      rS = buffer_rsrc(sbase, wave < C::ROW_WAVES
+                                  ? static_cast<uint32_t>(shared ? d.m : d.te) * (inter / kQBlock) * 4u
+                                  : static_cast<uint32_t>(d.H / kQBlock) * (K / kQBlock) * 4u);
+
     // A of stage st goes to A slot st % DA, B (and the fp8 scales) to B slot
     // st % DEPTH.  A partial last stage (bf16, K % 64 = 32) loads the pieces
     // past the row end from K = 0: valid memory, and compute skips that step
@@ -283,15 +294,15 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void grouped_kernel(GroupedArgs a)
 #pragma unroll
       for (int q = 0; q < C::CPA; ++q)   // m-blocks past the rows are not loaded
         if ((wave * C::CPA + q) / C::BV < nmb)
-          dma16_to_lds(Ab + src_off(coffA[q], cpcA[q], kb), sl + (wave * C::CPA + q) * 1024);
+          buf16_to_lds(rA, src_off(coffA[q], cpcA[q], kb), sl + (wave * C::CPA + q) * 1024);
     };
     auto issue_b = [&](int st, int slot_st) {
       uint8_t *sl = lds + C::DA * C::A_BYTES + (slot_st % DEPTH) * C::B_STAGE;
       const uint32_t kb = static_cast<uint32_t>(st) * C::RB;
 #pragma unroll
       for (int q = 0; q < C::CPB; ++q)
-        dma16_to_lds(Wb + src_off(coffB[q], cpcB[q], kb), sl + (wave * C::CPB + q) * 1024);
-      if constexpr (C::SCALED) dma4_to_lds(sbase + (soff + st), sl + C::B_BYTES + wave * 256);
+        buf16_to_lds(rW, src_off(coffB[q], cpcB[q], kb), sl + (wave * C::CPB + q) * 1024);
+      if constexpr (C::SCALED) buf4_to_lds(rS, 4 * (soff + st), sl + C::B_BYTES + wave * 256);
     };
 
     f32x4_t acc[MBW][NB];
@@ -336,27 +347,20 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void grouped_kernel(GroupedArgs a)
     };
     constexpr int BLK = 16 * C::RB;   // bytes of a stage block
     auto read_stage = [&](int st, Regs &R) {
-      const uint32_t la = lds_off(lds + (st % C::DA) * C::A_BYTES + mb0 * BLK);
-      const uint32_t lb = lds_off(lds + C::DA * C::A_BYTES + (st % DEPTH) * C::B_STAGE + wn * NB * BLK);
+      const uint8_t *la = lds + (st % C::DA) * C::A_BYTES + mb0 * BLK;
+      const uint8_t *lb = lds + C::DA * C::A_BYTES + (st % DEPTH) * C::B_STAGE + wn * NB * BLK;
       // bf16 a[s * MBW + mb] / b[s * NB + j]: piece loff[s] of block mb / j;
       // fp8 a[2 mb + h] / b[2 j + h]: piece loff[h]
       static_for<0, NA>([&](auto ic) {
         constexpr int i = decltype(ic)::value;
         constexpr int o = DT == kBF16 ? i / MBW : i % 2, blk = DT == kBF16 ? i % MBW : i / 2;
-        lds_issue<blk * BLK>(la + loff[o], R.a[i]);
+        R.a[i] = lds_load<u32x4_t>(la + loff[o] + blk * BLK);
       });
       static_for<0, NBR>([&](auto ic) {
         constexpr int i = decltype(ic)::value;
         constexpr int o = DT == kBF16 ? i / NB : i % 2, blk = DT == kBF16 ? i % NB : i / 2;
-        lds_issue<blk * BLK>(lb + loff[o], R.b[i]);
+        R.b[i] = lds_load<u32x4_t>(lb + loff[o] + blk * BLK);
       });
-    };
-    // Wait for the issued reads; the empty statements then "redefine" every
-    // operand register, so no use of one can be scheduled before the wait.
-    auto lds_wait = [&](Regs &R) {
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      static_for<0, NA>([&](auto ic) { lds_tie(R.a[decltype(ic)::value]); });
-      static_for<0, NBR>([&](auto ic) { lds_tie(R.b[decltype(ic)::value]); });
     };
 
     auto compute = [&](int st, const Regs &R) {
@@ -384,43 +388,37 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void grouped_kernel(GroupedArgs a)
       if constexpr (C::SCALED) {
         const uint8_t *sa = lds + (st % C::DA) * C::A_BYTES;
         const uint8_t *sb = lds + C::DA * C::A_BYTES + (st % DEPTH) * C::B_STAGE;
-        const uint32_t la0 = lds_off(sa + wm * BLK) + loff[0];
-        const uint32_t lb0 = lds_off(sb + wn * NB * BLK) + loff[0];
+        const uint8_t *la0 = sa + wm * BLK + loff[0];
+        const uint8_t *lb0 = sb + wn * NB * BLK + loff[0];
         const uint32_t d1 = loff[1] - loff[0];   // the lane's second piece
         const uint8_t *ssc = sb + C::B_BYTES;
         // A pieces, row scales (rows mrow(mb)*16 + 4*kg + i: contiguous
-        // floats) and the weight-block scales of this column group: issued
-        // together, one wait
+        // floats) and the weight-block scales of this column group
         u32x4_t aq[2 * MBW], sv[MBW], sw[NB / 4];
-        const uint32_t lsr = lds_off(ssc + ((wm * 16) + 4 * kg) * 4);
-        const uint32_t lsw = lds_off(ssc + C::ROW_WAVES * 256 + wn * NB * 4);
+        const uint8_t *lsr = ssc + ((wm * 16) + 4 * kg) * 4;
+        const uint8_t *lsw = ssc + C::ROW_WAVES * 256 + wn * NB * 4;
         static_for<0, MBW>([&](auto ic) {
           constexpr int mb = decltype(ic)::value;
           if (mrow(mb) < nmb) {   // m-blocks past the rows are neither read nor multiplied
-            lds_issue<mb * WM * BLK>(la0, aq[2 * mb]);
-            lds_issue<mb * WM * BLK>(la0 + d1, aq[2 * mb + 1]);
-            lds_issue<mb * WM * 64>(lsr, sv[mb]);
+            aq[2 * mb] = lds_load<u32x4_t>(la0 + mb * WM * BLK);
+            aq[2 * mb + 1] = lds_load<u32x4_t>(la0 + d1 + mb * WM * BLK);
+            sv[mb] = lds_load<u32x4_t>(lsr + mb * WM * 64);
           }
         });
         static_for<0, NB / 4>([&](auto ic) {
           constexpr int q = decltype(ic)::value;
-          lds_issue<q * 16>(lsw, sw[q]);
+          sw[q] = lds_load<u32x4_t>(lsw + q * 16);
         });
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        static_for<0, MBW>([&](auto ic) {
-          constexpr int mb = decltype(ic)::value;
-          lds_tie(aq[2 * mb]);
-          lds_tie(aq[2 * mb + 1]);
-          lds_tie(sv[mb]);
-        });
-        static_for<0, NB / 4>([&](auto ic) { lds_tie(sw[decltype(ic)::value]); });
         // weight blocks four at a time
 #pragma unroll
         for (int j0 = 0; j0 < NB; j0 += 4) {
           u32x4_t bq[8];
-          const uint32_t lb = lb0 + j0 * BLK;
-          lds_read4<0, 0, BLK, BLK>(lb, lb + d1, lb, lb + d1, bq[0], bq[1], bq[2], bq[3]);
-          lds_read4<2 * BLK, 2 * BLK, 3 * BLK, 3 * BLK>(lb, lb + d1, lb, lb + d1, bq[4], bq[5], bq[6], bq[7]);
+          const uint8_t *lb = lb0 + j0 * BLK;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            bq[2 * j] = lds_load<u32x4_t>(lb + j * BLK);
+            bq[2 * j + 1] = lds_load<u32x4_t>(lb + d1 + j * BLK);
+          }
 #pragma unroll
           for (int mb = 0; mb < MBW; ++mb) {
             if (mrow(mb) >= nmb) continue;   // no rows in this m-block
@@ -469,7 +467,10 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void grouped_kernel(GroupedArgs a)
           __builtin_amdgcn_sched_barrier(0);
           compute(st, cur);
           __builtin_amdgcn_sched_barrier(0);
-          if (st + 1 < nstage) lds_wait(next);
+          // the reads of stage st + 1 land before the next barrier, which
+          // hands their slots to the loads (unconditional: the compiler then
+          // knows on every path that no read is outstanding)
+          wait_lgkm<0>();
         }
       };
       issue_b(0, 0);
@@ -484,7 +485,7 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void grouped_kernel(GroupedArgs a)
       ring_barrier();   // stage 0 landed
       if (rows_on) {
         read_stage(0, RA);
-        lds_wait(RA);
+        wait_lgkm<0>();
       }
       if (nstage > 1) issue_a(1, 1);
       if (DEPTH - 1 < nstage) issue_b(DEPTH - 1, DEPTH - 1);
@@ -511,6 +512,7 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void grouped_kernel(GroupedArgs a)
       for (int st = 0; st < nstage; ++st) {
         __builtin_amdgcn_sched_barrier(0);   // nothing moves across a stage boundary
         wait_vm<C::LB>();
+        wait_lgkm<0>();   // the previous stage's reads have landed
         ring_barrier();
         issue_a(min(st + 1, last), st + 1);
         issue_b(min(st + 2, last), st + 2);

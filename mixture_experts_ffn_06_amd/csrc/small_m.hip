@@ -321,18 +321,66 @@ struct MxCfg {
   static_assert(WAVE_LDS >= NB * kWave * 16, "partial sums fit the ring");
 };
 
-// LDS reads issued without waiting (the stage's reads are waited for
-// together; mx_tie after that wait keeps every use of a result behind it).
-template <int O>
-__device__ __forceinline__ void mx_issue_b32(uint32_t p, uint32_t &v) {
-  asm volatile("ds_read_b32 %0, %1 offset:%2" : "=v"(v) : "v"(p), "i"(O));
+// One stage's weight and scale reads of an MX item from its ring slot, all
+// issued and then waited for in one statement (NB blocks of 16 rows, block j
+// 16 * kMxRun bytes after block j - 1; its scale bytes 16 * 8 (FP4) or
+// 16 * 4 (FP8) bytes after).  a[i]: the lane's address of step i's weight
+// bytes in block 0; as: of its scale bytes in block 0.
+#define MX_RW(OP, J, I) OP " %[w" #J #I "], %[a" #I "] offset:%[o" #J "]\n\t"
+#define MX_RS(OP, J) OP " %[q" #J "], %[as] offset:%[s" #J "]\n\t"
+#define MX_F4_BLK(J)                                                                                   \
+  MX_RW("ds_read_b32", J, 0) MX_RW("ds_read_b32", J, 1) MX_RW("ds_read_b32", J, 2)                     \
+  MX_RW("ds_read_b32", J, 3) MX_RW("ds_read_b32", J, 4) MX_RW("ds_read_b32", J, 5)                     \
+  MX_RW("ds_read_b32", J, 6) MX_RW("ds_read_b32", J, 7) MX_RS("ds_read_b64", J)
+#define MX_F8_BLK(J)                                                                                   \
+  MX_RW("ds_read_b64", J, 0) MX_RW("ds_read_b64", J, 1) MX_RW("ds_read_b64", J, 2)                     \
+  MX_RW("ds_read_b64", J, 3) MX_RS("ds_read_b32", J)
+#define MX_F4_OUT(J)                                                                                   \
+  [w##J##0] "=&v"(wv[J][0]), [w##J##1] "=&v"(wv[J][1]), [w##J##2] "=&v"(wv[J][2]),                     \
+  [w##J##3] "=&v"(wv[J][3]), [w##J##4] "=&v"(wv[J][4]), [w##J##5] "=&v"(wv[J][5]),                     \
+  [w##J##6] "=&v"(wv[J][6]), [w##J##7] "=&v"(wv[J][7]), [q##J] "=&v"(q[J])
+#define MX_F8_OUT(J)                                                                                   \
+  [w##J##0] "=&v"(wv[J][0]), [w##J##1] "=&v"(wv[J][1]), [w##J##2] "=&v"(wv[J][2]),                     \
+  [w##J##3] "=&v"(wv[J][3]), [q##J] "=&v"(q[J])
+#define MX_A8 [a0] "v"(a[0]), [a1] "v"(a[1]), [a2] "v"(a[2]), [a3] "v"(a[3]), \
+              [a4] "v"(a[4]), [a5] "v"(a[5]), [a6] "v"(a[6]), [a7] "v"(a[7])
+#define MX_A4 [a0] "v"(a[0]), [a1] "v"(a[1]), [a2] "v"(a[2]), [a3] "v"(a[3])
+#define MX_OFFS(SB) [o0] "i"(0), [o1] "i"(16 * kMxRun), [o2] "i"(32 * kMxRun), [o3] "i"(48 * kMxRun), \
+                    [s0] "i"(0), [s1] "i"(16 * (SB)), [s2] "i"(32 * (SB)), [s3] "i"(48 * (SB))
+
+__device__ __forceinline__ void mx_read(const uint32_t (&a)[8], uint32_t as, uint32_t (&wv)[2][8], u32x2_t (&q)[2]) {
+  asm volatile(MX_F4_BLK(0) MX_F4_BLK(1) "s_waitcnt lgkmcnt(0)"
+               : MX_F4_OUT(0), MX_F4_OUT(1)
+               : MX_A8, [as] "v"(as), MX_OFFS(8)
+               : "memory");
 }
-template <int O>
-__device__ __forceinline__ void mx_issue_b64(uint32_t p, u32x2_t &v) {
-  asm volatile("ds_read_b64 %0, %1 offset:%2" : "=v"(v) : "v"(p), "i"(O));
+__device__ __forceinline__ void mx_read(const uint32_t (&a)[8], uint32_t as, uint32_t (&wv)[4][8], u32x2_t (&q)[4]) {
+  asm volatile(MX_F4_BLK(0) MX_F4_BLK(1) MX_F4_BLK(2) MX_F4_BLK(3) "s_waitcnt lgkmcnt(0)"
+               : MX_F4_OUT(0), MX_F4_OUT(1), MX_F4_OUT(2), MX_F4_OUT(3)
+               : MX_A8, [as] "v"(as), MX_OFFS(8)
+               : "memory");
 }
-__device__ __forceinline__ void mx_tie(uint32_t &v) { asm volatile("" : "+v"(v)); }
-__device__ __forceinline__ void mx_tie(u32x2_t &v) { asm volatile("" : "+v"(v)); }
+__device__ __forceinline__ void mx_read(const uint32_t (&a)[4], uint32_t as, u32x2_t (&wv)[2][4], uint32_t (&q)[2]) {
+  asm volatile(MX_F8_BLK(0) MX_F8_BLK(1) "s_waitcnt lgkmcnt(0)"
+               : MX_F8_OUT(0), MX_F8_OUT(1)
+               : MX_A4, [as] "v"(as), MX_OFFS(4)
+               : "memory");
+}
+__device__ __forceinline__ void mx_read(const uint32_t (&a)[4], uint32_t as, u32x2_t (&wv)[4][4], uint32_t (&q)[4]) {
+  asm volatile(MX_F8_BLK(0) MX_F8_BLK(1) MX_F8_BLK(2) MX_F8_BLK(3) "s_waitcnt lgkmcnt(0)"
+               : MX_F8_OUT(0), MX_F8_OUT(1), MX_F8_OUT(2), MX_F8_OUT(3)
+               : MX_A4, [as] "v"(as), MX_OFFS(4)
+               : "memory");
+}
+#undef MX_RW
+#undef MX_RS
+#undef MX_F4_BLK
+#undef MX_F8_BLK
+#undef MX_F4_OUT
+#undef MX_F8_OUT
+#undef MX_A8
+#undef MX_A4
+#undef MX_OFFS
 
 // Eight e2m1 codes (one 32-bit word, the even element in the low nibble of
 // each byte) times 2^(e - 127), as bf16.
@@ -468,20 +516,10 @@ __global__ __launch_bounds__(kSmBlockWaves * kWave, NB == 2 ? 4 : 2) void sm_mx_
       if constexpr (C::F4) {
         uint32_t wv[NB][8];
         u32x2_t q[NB];
-        static_for<0, NB>([&](auto jc) {
-          constexpr int j = decltype(jc)::value;
-          static_for<0, 8>([&](auto ic) {
-            constexpr int i = decltype(ic)::value;
-            mx_issue_b32<j * 16 * kMxRun>(base + boff[i], wv[j][i]);
-          });
-          mx_issue_b64<j * 16 * 8>(base + srd, q[j]);
-        });
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        static_for<0, NB>([&](auto jc) {
-          constexpr int j = decltype(jc)::value;
-          static_for<0, 8>([&](auto ic) { mx_tie(wv[j][decltype(ic)::value]); });
-          mx_tie(q[j]);
-        });
+        uint32_t ad[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ad[i] = base + boff[i];
+        mx_read(ad, base + srd, wv, q);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const bf16x8_t a = __builtin_bit_cast(bf16x8_t, A[i]);
@@ -495,20 +533,10 @@ __global__ __launch_bounds__(kSmBlockWaves * kWave, NB == 2 ? 4 : 2) void sm_mx_
       } else {
         u32x2_t wv[NB][4];
         uint32_t q[NB];
-        static_for<0, NB>([&](auto jc) {
-          constexpr int j = decltype(jc)::value;
-          static_for<0, 4>([&](auto ic) {
-            constexpr int i = decltype(ic)::value;
-            mx_issue_b64<j * 16 * kMxRun>(base + boff[i], wv[j][i]);
-          });
-          mx_issue_b32<j * 16 * 4>(base + srd, q[j]);
-        });
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        static_for<0, NB>([&](auto jc) {
-          constexpr int j = decltype(jc)::value;
-          static_for<0, 4>([&](auto ic) { mx_tie(wv[j][decltype(ic)::value]); });
-          mx_tie(q[j]);
-        });
+        uint32_t ad[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ad[i] = base + boff[i];
+        mx_read(ad, base + srd, wv, q);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const bf16x8_t a = __builtin_bit_cast(bf16x8_t, A[i]);

@@ -1,19 +1,18 @@
-"""Scan gfx950 device assembly for uses of in-flight inline-asm LDS reads.
+"""Scan gfx950 device assembly for inline-asm LDS reads left in flight.
 
-The LDS rings issue their reads with inline asm that does not wait
-(``ds_read_b128`` with an ``=v`` output) and wait later with an
-``s_waitcnt lgkmcnt(N)``: LDS reads complete in issue order, so such a wait
-completes every asm read but the N most recent (other LGKM operations issued
-in between only make the hardware wait longer, so the scan's count is
-conservative).  The compiler takes an asm output as written when
-the asm statement ends, so it may copy, move or reuse such a register before
-the wait, and the late-arriving data then lands in a register that holds
-something else.  This scan walks each function's instructions in text order
-and reports any instruction other than a wait that reads or writes a register
-between an asm LDS read writing it and the wait that completes that read.
+The kernels read LDS with ordinary loads (the compiler places the waits)
+except where a handful of reads must go out together: there an inline-asm
+statement issues them and ends with ``s_waitcnt lgkmcnt(0)``, so no result
+register is still being written when the statement ends.  (The compiler
+takes an asm output as written when the statement ends; a read still in
+flight could land in a register that by then holds something else.)
 
-The scan is linear (no control-flow graph), so it is a guard against the
-common forms of the mistake, not a proof of their absence.
+``asm_blocks`` splits a function's assembly into its inline-asm statements
+(the ``;;#ASMSTART`` / ``;;#ASMEND`` markers); ``unwaited_reads`` returns the
+statements with a ``ds_read`` that no later ``s_waitcnt lgkmcnt(0)`` in the
+same statement completes.  ``scan`` is the older, stricter check of the
+whole text: any instruction touching a register between an asm read writing
+it and the wait that completes the read.
 """
 from __future__ import annotations
 
@@ -34,10 +33,58 @@ def _regs(text: str) -> set:
     return out
 
 
+def _instructions(raw_lines):
+    for raw in raw_lines:
+        text = raw.split(";")[0].strip()
+        if text and not text.startswith(".") and not text.endswith(":"):
+            yield text
+
+
+def asm_blocks(asm: str):
+    """Yield (function, first line number, [instructions]) per inline-asm statement."""
+    fn, block, start = None, None, 0
+    for ln, raw in enumerate(asm.splitlines(), 1):
+        m = _FN.match(raw)
+        if m:
+            fn = m.group(1)
+            continue
+        line = raw.strip()
+        if line.startswith(";;#ASMSTART"):
+            block, start = [], ln
+            continue
+        if line.startswith(";;#ASMEND"):
+            if block is not None:
+                yield fn, start, block
+            block = None
+            continue
+        if block is not None:
+            block.extend(_instructions([raw]))
+
+
+def unwaited_reads(asm: str):
+    """Return (bad statements, statements with LDS reads): a statement is bad
+    if a ds_read in it is not followed, inside it, by s_waitcnt lgkmcnt(0)."""
+    bad, n = [], 0
+    for fn, ln, ins in asm_blocks(asm):
+        reads = [i for i, t in enumerate(ins) if t.startswith("ds_read")]
+        if not reads:
+            continue
+        n += 1
+        waits = [i for i, t in enumerate(ins)
+                 if t.startswith("s_waitcnt") and _LGKM.search(t) and _LGKM.search(t).group(1) == "0"]
+        if not waits or max(waits) < max(reads):
+            bad.append((fn, ln, ins))
+    return bad, n
+
+
 def scan(asm: str):
     """Return (hazards, n_asm_reads, n_functions) for assembly text.
 
-    Each hazard is (function, line number, instruction, register).
+    Each hazard is (function, line number, instruction, register): an
+    instruction other than a wait that reads or writes a register between an
+    asm LDS read writing it and the wait that completes that read (reads
+    complete in issue order, so lgkmcnt(N) completes all but the N most
+    recent).  The scan is linear (no control-flow graph).
     """
     hazards = []
     fn = None
