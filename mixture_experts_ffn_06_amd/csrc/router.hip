@@ -248,7 +248,6 @@ template <int EPL>
 __global__ __launch_bounds__(kFusedThreads) void topk_permute_kernel(Dims d, Inputs in, Work w, int ks,
                                                                      int *topk_idx, float *topk_w) {
   extern __shared__ __align__(16) uint8_t smem[];
-  __shared__ int scan_tmp[kPermWaves];
   __shared__ uint32_t sk[kFusedThreads / kWave][kTopkScratch];
   const int wave = threadIdx.x >> 6;
   const int m = d.m, E = d.E;
@@ -297,9 +296,10 @@ __global__ __launch_bounds__(kFusedThreads) void topk_permute_kernel(Dims d, Inp
                     topk_idx + static_cast<size_t>(wave) * d.k, topk_w + static_cast<size_t>(wave) * d.k,
                     idx_s + wave * d.k, sk[wave]);
   __syncthreads();
-  // ---- stable sort by expert ----
-  permute_block(idx_s, d.te, E, wcnt, scan_tmp, w.counts, w.offsets, w.sorted_pair, w.slot_of_pair,
-                lrank, w.active, w.nactive, w.rboff);
+  // ---- stable sort by expert: the few pairs of a decode batch by one wave ----
+  if (wave == 0)
+    permute_wave(idx_s, d.te, E, wcnt, lrank, w.counts, w.offsets, w.sorted_pair, w.slot_of_pair,
+                 w.active, w.nactive, w.rboff);
 }
 
 hipError_t launch_topk_permute(const Dims &d, const Inputs &in, const Work &w, int *topk_idx,

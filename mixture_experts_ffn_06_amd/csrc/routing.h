@@ -84,14 +84,21 @@ __device__ __forceinline__ void topk_token(const float *lrow, int E, int k, int 
     if (bias) c += valid[i] ? bias[e] : 0.f;
     key[i] = valid[i] ? order_key(c) : 0u;
   }
-  // T = the largest value with at least k keys >= T (the k-th largest key)
+  // T = the largest value with at least k keys >= T (the k-th largest key),
+  // two bits per step: of the candidates T | d << b (d = 3, 2, 1, 0) the
+  // largest that at least k keys reach (d = 0 always does); the three counts
+  // are independent, so the serial chain is 16 steps instead of 32
   uint32_t T = 0;
-  for (int b = 31; b >= 0; --b) {
-    const uint32_t t = T | (1u << b);
-    int cnt = 0;
+  for (int b = 30; b >= 0; b -= 2) {
+    const uint32_t t1 = T | (1u << b), t2 = T | (2u << b), t3 = T | (3u << b);
+    int c1 = 0, c2 = 0, c3 = 0;
 #pragma unroll
-    for (int i = 0; i < EPL; ++i) cnt += __popcll(__ballot(valid[i] && key[i] >= t));
-    if (cnt >= k) T = t;
+    for (int i = 0; i < EPL; ++i) {
+      c1 += __popcll(__ballot(valid[i] && key[i] >= t1));
+      c2 += __popcll(__ballot(valid[i] && key[i] >= t2));
+      c3 += __popcll(__ballot(valid[i] && key[i] >= t3));
+    }
+    T = c3 >= k ? t3 : c2 >= k ? t2 : c1 >= k ? t1 : T;
   }
   int need = k;
 #pragma unroll
@@ -292,6 +299,84 @@ __device__ __forceinline__ int expert_offsets(int tot, int E, int *scan_tmp, int
     rboff[all_active] = all_rb;
   }
   return off;
+}
+
+// The whole sort by one wave, for the few pairs of a decode-sized batch (no
+// block barriers).  Pairs are ranked 64 at a time in pair order (the rank of
+// a pair among the earlier pairs of its expert: running counts in cnt, LDS
+// of E ints), the expert totals are scanned by the wave (lane l takes
+// experts [l P, l P + P), P = ceil(E / 64)), and each pair goes to its
+// expert's start plus its rank: the same stable order as permute_block.
+// lrank: te ints of LDS or global memory.
+__device__ __forceinline__ void permute_wave(
+    const int *topk_idx, int te, int E, int *cnt, int *__restrict__ lrank,
+    int *__restrict__ counts, int *__restrict__ offsets, int *__restrict__ sorted_pair,
+    int *__restrict__ slot_of_pair, int *__restrict__ active, int *__restrict__ nactive,
+    int *__restrict__ rboff) {
+  const int lane = threadIdx.x & 63;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const uint64_t above = (lane == 63) ? 0ull : (~0ull << (lane + 1));
+  for (int e = lane; e < E; e += kWave) cnt[e] = 0;
+  __builtin_amdgcn_wave_barrier();
+  for (int base = 0; base < te; base += kWave) {
+    const int p = base + lane;
+    const bool valid = p < te;
+    const int e = valid ? topk_idx[p] : 0;
+    const uint64_t same = same_expert_mask(e, valid, E);
+    const int r = (valid ? cnt[e] : 0) + __popcll(same & below);
+    if (valid) lrank[p] = r;
+    __builtin_amdgcn_wave_barrier();
+    if (valid && (same & above) == 0) cnt[e] = r + 1;   // last lane of its group
+    __builtin_amdgcn_wave_barrier();
+  }
+  // totals -> starts, the active list and the 16-row block prefix
+  const int per = (E + kWave - 1) / kWave;
+  const int e0 = min(lane * per, E), e1 = min(e0 + per, E);
+  int tot = 0, act = 0, rb = 0;
+  for (int e = e0; e < e1; ++e) {
+    const int c = cnt[e];
+    tot += c;
+    act += c > 0 ? 1 : 0;
+    rb += (c + 15) >> 4;
+  }
+  int itot = tot, iact = act, irb = rb;   // inclusive scans over the lanes
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int a = __shfl_up(itot, o), b = __shfl_up(iact, o), c = __shfl_up(irb, o);
+    if (lane >= o) {
+      itot += a;
+      iact += b;
+      irb += c;
+    }
+  }
+  const int all_pairs = __shfl(itot, kWave - 1), all_active = __shfl(iact, kWave - 1),
+            all_rb = __shfl(irb, kWave - 1);
+  int off = itot - tot, aoff = iact - act, rbo = irb - rb;
+  __builtin_amdgcn_wave_barrier();
+  for (int e = e0; e < e1; ++e) {
+    const int c = cnt[e];
+    counts[e] = c;
+    offsets[e] = off;
+    if (c > 0) {
+      active[aoff] = e;
+      rboff[aoff] = rbo;
+      ++aoff;
+      rbo += (c + 15) >> 4;
+    }
+    cnt[e] = off;   // cnt now holds the expert's first position
+    off += c;
+  }
+  if (lane == 0) {
+    offsets[E] = all_pairs;
+    *nactive = all_active;
+    rboff[all_active] = all_rb;
+  }
+  __builtin_amdgcn_wave_barrier();
+  for (int p = lane; p < te; p += kWave) {
+    const int pos = cnt[topk_idx[p]] + lrank[p];
+    sorted_pair[pos] = p;
+    slot_of_pair[p] = pos;
+  }
 }
 
 // The whole sort in one block.
