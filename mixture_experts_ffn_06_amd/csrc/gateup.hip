@@ -10,25 +10,31 @@
 //
 // Layout on CDNA4:
 //  * A unit is (group, N tile, M tile): 128 h columns (128 gate rows of w1
-//    and the matching 128 up rows of w3) against up to 128 token rows of one
+//    and the matching 128 up rows of w3) against up to 160 token rows of one
 //    group (a routed expert's sorted rows, or the m tokens for the shared
-//    expert, group E).  Consecutive units are the M tiles of one N tile and
-//    run side by side on one XCD, so a tile's weights come from HBM once and
-//    from that XCD's L2 for the other M tiles.
+//    expert, group E).  A group's rows split evenly over ceil(rows / 160) M
+//    tiles, so an expert of up to 160 rows streams its weights once.
+//    Consecutive units are the M tiles of one N tile (else the N tiles of one
+//    group) and run side by side on one XCD, so shared operands come from
+//    that XCD's L2.
 //  * A block is 8 waves, two per SIMD.  Waves 0-3 multiply: wave w owns
 //    weight rows [32 w, 32 w + 32) of the gate half and of the up half of the
-//    tile, as the M side of the MFMA, and multiplies them with all token
-//    blocks (the N side): each lane then holds one token's results, so its
+//    tile, as the M side of the MFMA, and multiplies them with token blocks
+//    0-3 (the N side): each lane then holds one token's results, so its
 //    activation scale is one value per token block and the block-scale
-//    promotion is one FMA per accumulator.  Waves 4-7 only move data: load
-//    wave 4 + w brings wave w's 64 weight rows, token block w and a share of
-//    the fp8 scales.  A load instruction holds the CU's address path for many
-//    cycles once HBM pushes back, and a wave cannot issue past it; kept out
-//    of the multiplying waves, those stalls no longer idle the MFMA.
+//    promotion is one FMA per accumulator.  Waves 4-7 move data -- load wave
+//    4 + w brings wave w's 64 weight rows, token block w, 8 rows of token
+//    block 4 and a share of the fp8 scales -- and, when the tile has rows
+//    past 128, load wave 4 + w multiplies wave w's weight rows with token
+//    block 4 (rows 128-159) on the same SIMD.  A load instruction holds the
+//    CU's address path for many cycles once HBM pushes back, and a wave
+//    cannot issue past it; kept out of the multiplying waves, those stalls no
+//    longer idle the MFMA.
 //  * Per K stage (128 bytes of every row: 64 bf16 or 128 e4m3 elements) the
 //    256 weight rows and the token rows go to LDS by direct buffer->LDS
-//    loads (16-byte pieces XOR-swizzled per row); three slots, two stages in
-//    flight while one is multiplied, one barrier per stage.  The multiplying
+//    loads (16-byte pieces XOR-swizzled per row): weights (and fp8 scales)
+//    in three slots, two stages in flight while one is multiplied; token
+//    rows (from L2) in two slots, one stage ahead; one barrier per stage.  All
 //    waves read LDS with ordinary loads, whose waits the compiler places.
 //  * Lane l multiplies row l % 32 of a block and takes 64 of the stage's
 //    bytes: pieces P(g, j) = 4 (j / 2) + 2 g + j % 2 for lane group g = l / 32,
@@ -46,7 +52,7 @@
 //    fp8 rounding boundaries of h.
 //  * Epilogue: SwiGLU from the gate and up accumulators (the same layout);
 //    bf16 h, or fp8 h quantised per row per 128 columns (the unit's
-//    columns: row amax across the four waves through LDS).
+//    columns: row amax across the four column waves through LDS).
 #include "common.h"
 #include "kernels.h"
 #include "launch.h"
@@ -62,9 +68,11 @@ constexpr int kGuWaves = 4;        // multiplying waves (and as many load waves)
 constexpr int kGuThreads = 2 * kGuWaves * kWave;
 constexpr int kGuRowBytes = 128;   // bytes of a row per stage
 constexpr int kGuWRows = 256;      // weight rows per unit (4 waves x (32 gate + 32 up))
-constexpr int kGuTBlocks = 4;      // token blocks of 32 rows per unit
+constexpr int kGuMBlocks = 4;      // token blocks of the multiplying waves
+constexpr int kGuTBlocks = 5;      // token blocks of 32 rows per unit (block 4 on the load waves)
 constexpr int kGuTRows = 32 * kGuTBlocks;
-constexpr int kGuDepth = 3;        // stages in the LDS ring
+constexpr int kGuDepth = 3;        // weight (and scale) slots
+constexpr int kGuTDepth = 2;       // token slots
 
 template <int DT>
 struct GuCfg {
@@ -72,15 +80,23 @@ struct GuCfg {
   static constexpr int SK = kGuRowBytes / ESZ;              // K elements per stage
   static constexpr int STEPS = SK / 16;                     // MFMA steps per stage
   static constexpr int W_BYTES = kGuWRows * kGuRowBytes;    // 32 KB
-  static constexpr int S_BYTES = DT == kFP8 ? 2048 : 0;     // token and weight-block scales, 2 K blocks
-  static constexpr int T_BYTES = kGuTRows * kGuRowBytes;    // 16 KB
-  static constexpr int SLOT = W_BYTES + S_BYTES + T_BYTES;
-  static constexpr int LDS = kGuDepth * SLOT;
-  // vector-memory operations per load wave per stage: 8 weight + 4 token
-  // loads (+ two 4-byte scale loads for fp8: this K block's and the next one's)
-  static constexpr int OPS = 8 + 4 + (DT == kFP8 ? 2 : 0);
-  static_assert(OPS < 16 && 2 * OPS < 64, "vmcnt range");
-  static_assert(LDS <= 152 * 1024, "LDS");
+  // fp8 scales of two K blocks (this one, at 0, and the next, at 1024): the
+  // 160 token rows' scales at 4 r (loaded by waves 4-6, 64 each) and the
+  // gate / up weight-block scales at 768 / 772 (wave 7)
+  static constexpr int S_BYTES = DT == kFP8 ? 2048 : 0;
+  static constexpr int WS_SLOT = W_BYTES + S_BYTES;
+  static constexpr int T_BYTES = kGuTRows * kGuRowBytes;    // 20 KB
+  static constexpr int T_BASE = kGuDepth * WS_SLOT;         // token slots after the weight slots
+  static constexpr int LDS = T_BASE + kGuTDepth * T_BYTES;
+  // vector-memory operations per load wave per stage: 8 weight loads, 5
+  // token loads, fp8: two 4-byte scale loads (this K block's and the next)
+  static constexpr int NW = 8, NTL = 5, NS = DT == kFP8 ? 2 : 0;
+  static constexpr int OPS = NW + NTL + NS;
+  // left outstanding when a stage's loads have landed: the weight and scale
+  // loads of the stage after it
+  static constexpr int WAIT = NW + NS;
+  static_assert(OPS < 16, "vmcnt range");
+  static_assert(LDS <= 146 * 1024, "LDS (with the static arrays)");
 };
 
 struct GuArgs {
@@ -99,16 +115,17 @@ __device__ __forceinline__ int gu_swz(int r) { return (r >> 1) & 7; }
 // Logical piece of the lane's j-th 16 bytes (lane group g).
 __device__ __forceinline__ int gu_piece(int g, int j) { return 4 * (j >> 1) + 2 * g + (j & 1); }
 
-// The load waves' part of one unit: stage st goes to ring slot st % 3 --
-// the gate block's weight rows, the up block's, the token block and the fp8
-// scales -- by direct loads to LDS.  A load wave issues stages 0 and 1,
-// waits for stage 0, and at each stage's barrier (every multiplying wave is
-// done with stage st - 1, whose slot stage st + 2 takes) issues stage st + 2
-// -- past the end the last stage again, into a free slot no one reads, so
-// each step leaves exactly OPS operations behind the one awaited -- and waits
-// until only those are outstanding: stage st + 1 has landed by the next
-// barrier (in-order completion).  It passes exactly nstage barriers, as the
-// multiplying waves do.
+// The load waves' part of one unit.  Weight stage st (and its fp8 scales)
+// goes to weight slot st % 3, token stage st to token slot st % 2.  A load
+// wave issues weights 0, tokens 0 and weights 1, waits for stage 0, and at
+// each stage's barrier (every wave is done with stage st - 1, whose weight
+// slot stage st + 2 takes and whose token slot stage st + 1 takes) issues
+// tokens st + 1 and weights st + 2 -- past the end the last stage again,
+// into a free slot no one reads, so each step leaves exactly WAIT
+// operations behind the ones awaited -- then runs work(st) (the fifth token
+// block's MFMAs, or nothing) and waits until only the weights st + 2 are
+// outstanding: stage st + 1 has landed by the next barrier (loads complete
+// in order).  It passes exactly nstage barriers, as the multiplying waves do.
 //
 // The loads go through buffer resources (buffer_load ... lds): the compiler
 // counts LDS reads exactly in a function that holds them (with the
@@ -118,59 +135,65 @@ __device__ __forceinline__ int gu_piece(int g, int j) { return 4 * (j >> 1) + 2 
 // Weight instruction q (0..7) moves rows 8 (q % 4) + drow of the gate (q < 4)
 // or up block (wave-uniform offset (8 (q % 4) + (q >= 4 ? inter : 0)) *
 // wstep; wstep = 0 for a wave past the columns: valid memory, never read)
-// from lane offsets wl0 / wl1 (q even / odd); token instruction q from
-// t0..t3.  hi_bits bit b: the lane's piece of lane offset b lies in the
-// second half of the stage's 128 bytes (in a bf16 half stage -- the last one
-// when K % 64 == 32 -- such pieces load the piece 64 bytes before instead:
-// valid memory, and the steps that would use them are skipped).
-template <int DT>
+// from lane offsets wl[q % 2]; token instruction q (0..4) from toff[q].
+// whi / thi: the lane's piece lies in the second half of the stage's 128
+// bytes (in a bf16 half stage -- the last one when K % 64 == 32 -- such
+// pieces load the piece 64 bytes before instead: valid memory, and the steps
+// that would use them are skipped).
+template <int DT, typename F>
 __device__ __forceinline__ void gu_load_unit(
-    __amdgpu_buffer_rsrc_t rW, __amdgpu_buffer_rsrc_t rA, __amdgpu_buffer_rsrc_t rS, uint32_t wl0,
-    uint32_t wl1, uint32_t hi_bits, uint32_t wstep, uint32_t inter, uint32_t kbytes, uint32_t t0, uint32_t t1,
-    uint32_t t2, uint32_t t3, uint32_t soff, int nstage, int wave, uint32_t lds0) {
+    __amdgpu_buffer_rsrc_t rW, __amdgpu_buffer_rsrc_t rA, __amdgpu_buffer_rsrc_t rS, const uint32_t (&wl)[2],
+    const bool (&whi)[2], const uint32_t (&toff)[kGuTBlocks], const bool (&thi)[kGuTBlocks], uint32_t wstep,
+    uint32_t inter, uint32_t kbytes, uint32_t soff, int nstage, int wave, uint32_t lds0, F &&work) {
   using C = GuCfg<DT>;
-  const uint32_t wl[2] = {wl0, wl1};
-  const bool whi[2] = {(hi_bits & 1u) != 0, (hi_bits & 2u) != 0};
-  const uint32_t toff[4] = {t0, t1, t2, t3};
-  // part 0, 1: the gate / up block's weight rows; 2: the token rows; 3: the
-  // fp8 scales of this K block and of the next one (past the last block: the
-  // last block's again, unused)
-  auto issue_part = [&](int st, auto pc) {
-    constexpr int part = decltype(pc)::value;
-    const uint32_t sl = lds0 + (st % kGuDepth) * C::SLOT;
-    const uint32_t kb = static_cast<uint32_t>(st) * kGuRowBytes;
+  auto kbs = [&](int st, uint32_t &kb, uint32_t &kb2) {
+    kb = static_cast<uint32_t>(st) * kGuRowBytes;
     const bool half = DT == kBF16 && kb + kGuRowBytes > kbytes;
-    const uint32_t kb2 = half ? kb - 64 : kb;
-    if constexpr (part < 2) {
+    kb2 = half ? kb - 64 : kb;
+  };
+  // weights (and scales) of stage st into the weight slot of stage slot_st
+  auto issue_w = [&](int st, int slot_st) {
+    const uint32_t sl = lds0 + static_cast<uint32_t>(slot_st % kGuDepth) * C::WS_SLOT;
+    uint32_t kb, kb2;
+    kbs(st, kb, kb2);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int q = 4 * part + i;
-        const uint32_t wu = static_cast<uint32_t>(8 * (q & 3) + (q >= 4 ? inter : 0)) * wstep;
-        buf16_to_lds(rW, wl[q & 1] + wu + (whi[q & 1] ? kb2 : kb), lds_ptr(sl + (8 * wave + q) * 1024));
-      }
-    } else if constexpr (part == 2) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        buf16_to_lds(rA, toff[q] + (whi[q & 1] ? kb2 : kb),
-                     lds_ptr(sl + C::W_BYTES + C::S_BYTES + (4 * wave + q) * 1024));
-    } else {
-      if constexpr (DT == kFP8) {
-        buf4_to_lds(rS, 4 * (soff + st), lds_ptr(sl + C::W_BYTES + 256 * wave));
-        buf4_to_lds(rS, 4 * (soff + min(st + 1, nstage - 1)), lds_ptr(sl + C::W_BYTES + 1024 + 256 * wave));
-      }
+    for (int q = 0; q < C::NW; ++q) {
+      const uint32_t wu = static_cast<uint32_t>(8 * (q & 3) + (q >= 4 ? inter : 0)) * wstep;
+      buf16_to_lds(rW, wl[q & 1] + wu + (whi[q & 1] ? kb2 : kb), lds_ptr(sl + (8 * wave + q) * 1024));
+    }
+    if constexpr (C::NS) {
+      // the next K block's scales too (past the last block: the last
+      // block's again, unused)
+      buf4_to_lds(rS, 4 * (soff + st), lds_ptr(sl + C::W_BYTES + 256 * wave));
+      buf4_to_lds(rS, 4 * (soff + min(st + 1, nstage - 1)), lds_ptr(sl + C::W_BYTES + 1024 + 256 * wave));
     }
   };
-  auto issue = [&](int st) { static_for<0, 4>([&](auto pc) { issue_part(st, pc); }); };
+  // token rows of stage st into the token slot of stage slot_st: block wave
+  // (instructions 0-3), rows 128 + 8 wave .. + 8 of block 4 (instruction 4)
+  auto issue_t = [&](int st, int slot_st) {
+    const uint32_t tl = lds0 + C::T_BASE + static_cast<uint32_t>(slot_st % kGuTDepth) * C::T_BYTES;
+    uint32_t kb, kb2;
+    kbs(st, kb, kb2);
+#pragma unroll
+    for (int q = 0; q < C::NTL; ++q)
+      buf16_to_lds(rA, toff[q] + (thi[q] ? kb2 : kb),
+                   lds_ptr(tl + (q < 4 ? 4 * wave + q : 16 + wave) * 1024));
+  };
   const int last = nstage - 1;
-  issue(0);
-  issue(min(1, last));
-  wait_vm<C::OPS>();
+  issue_w(0, 0);
+  issue_t(0, 0);
+  issue_w(min(1, last), 1);
+  wait_vm<C::WAIT>();
 #pragma unroll 1
   for (int st = 0; st < nstage; ++st) {
+    wait_lgkm<0>();   // work(st - 1)'s reads have landed
     __builtin_amdgcn_sched_barrier(0);
     ring_barrier();
-    issue(min(st + 2, last));
-    wait_vm<C::OPS>();
+    issue_t(min(st + 1, last), st + 1);
+    issue_w(min(st + 2, last), st + 2);
+    work(st);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vm<C::WAIT>();
   }
 }
 
@@ -185,11 +208,11 @@ __global__ __launch_bounds__(kGuThreads, 1) void gu_kernel(GuArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave_id = uniform(tid >> 6);
   const bool loader = wave_id >= kGuWaves;                  // waves 4-7 load, 0-3 multiply
-  const int wave = loader ? wave_id - kGuWaves : wave_id;   // the multiplying wave served / itself
+  const int wave = loader ? wave_id - kGuWaves : wave_id;   // the column wave served / itself
   const int G = d.E + (d.Is > 0 ? 1 : 0);
   const int *offsets = a.w.offsets;
 
-  // ---- unit prefix: units(g) = ceil(rows_g / 128) * ntile_g ----
+  // ---- unit prefix: units(g) = ceil(rows_g / 160) * ntile_g ----
   {
     constexpr int PER = (1025 + kGuThreads - 1) / kGuThreads;
     int loc[PER];
@@ -254,12 +277,12 @@ __global__ __launch_bounds__(kGuThreads, 1) void gu_kernel(GuArgs a) {
     const int nmt = (grows + kGuTRows - 1) / kGuTRows;
     const int local = uu - uniform(uoff[g]);
     const int ntile = local / nmt;
-    // the group's rows split evenly over its nmt M tiles (a 150-row expert
-    // runs two tiles of 75 rows, not 128 + 22)
+    // the group's rows split evenly over its nmt M tiles (a 200-row expert
+    // runs two tiles of 100 rows, not 160 + 40)
     const int trows = (grows + nmt - 1) / nmt;
     const int row0 = (local - ntile * nmt) * trows;
     const int rows = min(trows, grows - row0);
-    const int ntb = (rows + 31) >> 5;                       // token blocks with rows
+    const int ntb = (rows + 31) >> 5;                       // token blocks with rows (1..5)
     const int seg0 = shared ? 0 : uniform(offsets[g]);
     const int inter = shared ? d.Is : d.I;
     const int kbytes = d.H * C::ESZ;
@@ -272,58 +295,13 @@ __global__ __launch_bounds__(kGuThreads, 1) void gu_kernel(GuArgs a) {
     const uint8_t *Ab = DT == kFP8 ? static_cast<const uint8_t *>(a.w.xq)
                                    : static_cast<const uint8_t *>(a.in.x);
 
-    // ---- this wave's load sources (32-bit byte offsets; operands < 2 GiB) ----
-    // Weight instruction q (0..7) moves rows 8 (q % 4) + drow of the gate
-    // (q < 4) or up block to LDS rows 64 wave + 8 q + drow; token instruction
-    // q (0..3) token rows 32 wave + 8 q + drow (past the tile's rows: its last
-    // row again).  The lane fetches logical piece dpiece ^ swz(LDS row); for
-    // these rows that is p0 ^ 4 (q % 2), p0 = dpiece ^ (drow / 2), so the
-    // offsets are two lane values plus a wave-uniform part.  *hi: the piece
-    // lies in the second half of the stage's 128 bytes.
-    const int p0 = dpiece ^ (drow >> 1);
-    const int wrow0 = wave_on ? c0 + drow : 0;             // out of range: read valid memory, store nothing
-    const uint32_t wlane[2] = {static_cast<uint32_t>(wrow0) * kbytes + p0 * 16,
-                               static_cast<uint32_t>(wrow0) * kbytes + (p0 ^ 4) * 16};
-    const bool whi[2] = {p0 >= 4, (p0 ^ 4) >= 4};
-    uint32_t toff[4] = {0u, 0u, 0u, 0u};
-    if (loader) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int rr = min(32 * wave + 8 * q + drow, rows - 1);
-        const int tok = shared ? row0 + rr : a.w.sorted_pair[seg0 + row0 + rr] / d.k;
-        toff[q] = static_cast<uint32_t>(tok) * kbytes + (p0 ^ (4 * (q & 1))) * 16;
-      }
-    }
-    // fp8 scales of the stage's K block and of the next one (a scale area
-    // of 2 x 1 KB per slot): load waves 4, 5 load the token rows' scales (64
-    // each), wave 6 the gate (even lanes) and up (odd lanes) weight-block
-    // scales, wave 7 the same again into a spare area (every load wave issues
-    // two scale loads per stage)
-    const float *sbase = nullptr;
-    uint32_t soff = 0;
-    if constexpr (DT == kFP8) {
-      const int nkb = d.H / kQBlock;
-      if (!loader) {
-        // multiplying waves read the scales from LDS
-      } else if (wave < 2) {
-        const int rr = min(64 * wave + lane, rows - 1);
-        const int tok = shared ? row0 + rr : a.w.sorted_pair[seg0 + row0 + rr] / d.k;
-        sbase = a.w.sx;
-        soff = static_cast<uint32_t>(tok) * nkb;
-      } else {
-        sbase = shared ? a.in.sw13_scale
-                       : a.in.w13_scale + static_cast<size_t>(g) * (2 * d.I / kQBlock) * nkb;
-        const int srow = (lane & 1) ? inter / kQBlock + ntile : ntile;
-        soff = static_cast<uint32_t>(srow) * nkb;
-      }
-    }
-
-    // ---- accumulators: [weight block: 0 gate, 1 up][token block] ----
-    f32x16_t acc[2][kGuTBlocks];
+    // ---- accumulators: [weight block: 0 gate, 1 up][token block]; a load
+    // wave keeps block 4 in [.][0] ----
+    f32x16_t acc[2][kGuMBlocks];
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
-      for (int t = 0; t < kGuTBlocks; ++t)
+      for (int t = 0; t < kGuMBlocks; ++t)
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[b][t][i] = 0.f;
 
@@ -337,26 +315,27 @@ __global__ __launch_bounds__(kGuThreads, 1) void gu_kernel(GuArgs a) {
     // rescale sits between the last MFMAs of the others.
     // One stage: the lane's LDS reads of operand pieces (fp8: after its
     // token and weight-block scales), issued one piece ahead, the MFMAs of
-    // each piece's steps in between; NT = token blocks with rows (a template
-    // parameter keeps the MFMA sequence free of branches).
-    auto stage = [&](int st, auto ntc) {
+    // each piece's steps in between; NT token blocks from block T0 (template
+    // parameters keep the MFMA sequence free of branches).
+    auto stage = [&](int st, auto ntc, auto t0c) {
       constexpr int NT = decltype(ntc)::value;
-      const uint8_t *sl = lds + (st % kGuDepth) * C::SLOT;
-      const uint8_t *lw = sl + 64 * wave * kGuRowBytes;
-      const uint8_t *lt = sl + C::W_BYTES + C::S_BYTES;
+      constexpr int T0 = decltype(t0c)::value;
+      const uint8_t *sw = lds + (st % kGuDepth) * C::WS_SLOT;
+      const uint8_t *lw = sw + 64 * wave * kGuRowBytes;
+      const uint8_t *lt = lds + C::T_BASE + (st % kGuTDepth) * C::T_BYTES + 32 * kGuRowBytes * T0;
       const bool half = DT == kBF16 && static_cast<uint32_t>(st + 1) * kGuRowBytes > static_cast<uint32_t>(kbytes);
       u32x4_t wr[4][2], tr[4][NT];
       uint32_t sxr[2][NT];     // [this K block, next][token block]
       u32x2_t swr[2];
       if constexpr (DT == kFP8) {
-        const uint8_t *ls = sl + C::W_BYTES;
+        const uint8_t *ls = sw + C::W_BYTES;
         static_for<0, NT>([&](auto tc) {
           constexpr int t = decltype(tc)::value;
-          sxr[0][t] = lds_load<uint32_t>(ls + 4 * lr + 128 * t);
-          sxr[1][t] = lds_load<uint32_t>(ls + 4 * lr + 1024 + 128 * t);
+          sxr[0][t] = lds_load<uint32_t>(ls + 4 * lr + 128 * (T0 + t));
+          sxr[1][t] = lds_load<uint32_t>(ls + 4 * lr + 1024 + 128 * (T0 + t));
         });
-        swr[0] = lds_load<u32x2_t>(ls + 512);
-        swr[1] = lds_load<u32x2_t>(ls + 1024 + 512);
+        swr[0] = lds_load<u32x2_t>(ls + 768);
+        swr[1] = lds_load<u32x2_t>(ls + 1024 + 768);
       }
       auto load_piece = [&](auto jc) {
         constexpr int j = decltype(jc)::value;
@@ -420,33 +399,80 @@ __global__ __launch_bounds__(kGuThreads, 1) void gu_kernel(GuArgs a) {
     };
 
     __syncthreads();   // the previous unit is done with every slot and amax_w
-    // ---- the ring: stage st is multiplied from slot st % 3 while stages
-    // st + 1 and st + 2 load (gu_load_unit); both sides take exactly nstage
-    // barriers per unit. ----
+    // ---- the ring: stage st is multiplied from its slots while stages
+    // st + 1 (tokens) and st + 2 (weights) load (gu_load_unit); both sides
+    // take exactly nstage barriers per unit ----
     if (loader) {
+      // ---- this wave's load sources (32-bit byte offsets; operands < 2 GiB) ----
+      // Weight instruction q moves rows 8 (q % 4) + drow of the gate (q < 4)
+      // or up block to LDS rows 64 wave + 8 q + drow; token instruction q
+      // (0..3) token rows 32 wave + 8 q + drow, instruction 4 rows 128 +
+      // 8 wave + drow (past the tile's rows: its last row again).  The lane
+      // fetches logical piece dpiece ^ swz(row in its 32-row block): p0 ^ 4
+      // (q % 2) for instructions 0-3 and weights, p0 ^ 4 (wave % 2) for
+      // instruction 4, p0 = dpiece ^ (drow / 2).
+      const int p0 = dpiece ^ (drow >> 1);
+      const int wrow0 = wave_on ? c0 + drow : 0;           // out of range: read valid memory, store nothing
+      const uint32_t wl[2] = {static_cast<uint32_t>(wrow0) * kbytes + p0 * 16,
+                              static_cast<uint32_t>(wrow0) * kbytes + (p0 ^ 4) * 16};
+      const bool whi[2] = {p0 >= 4, (p0 ^ 4) >= 4};
+      uint32_t toff[kGuTBlocks];
+      bool thi[kGuTBlocks];
+#pragma unroll
+      for (int q = 0; q < kGuTBlocks; ++q) {
+        const int row = q < 4 ? 32 * wave + 8 * q + drow : 128 + 8 * wave + drow;
+        const int rr = min(row, rows - 1);
+        const int tok = shared ? row0 + rr : a.w.sorted_pair[seg0 + row0 + rr] / d.k;
+        const int pc = p0 ^ (4 * ((q < 4 ? q : wave) & 1));
+        toff[q] = static_cast<uint32_t>(tok) * kbytes + pc * 16;
+        thi[q] = pc >= 4;
+      }
+      // fp8 scales: load waves 4-6 the token rows' (64 each, rows past the
+      // tile's rows: its last row again), wave 7 the gate (even lanes) and up
+      // (odd lanes) weight-block scales
+      const float *sbase = a.w.sx;
+      uint32_t soff = 0, sbytes = 4;
+      if constexpr (DT == kFP8) {
+        const int nkb = d.H / kQBlock;
+        if (wave < 3) {
+          const int rr = min(64 * wave + lane, rows - 1);
+          const int tok = shared ? row0 + rr : a.w.sorted_pair[seg0 + row0 + rr] / d.k;
+          soff = static_cast<uint32_t>(tok) * nkb;
+          sbytes = static_cast<uint32_t>(d.m) * nkb * 4u;
+        } else {
+          sbase = shared ? a.in.sw13_scale
+                         : a.in.w13_scale + static_cast<size_t>(g) * (2 * d.I / kQBlock) * nkb;
+          const int srow = (lane & 1) ? inter / kQBlock + ntile : ntile;
+          soff = static_cast<uint32_t>(srow) * nkb;
+          sbytes = static_cast<uint32_t>(2 * inter / kQBlock) * nkb * 4u;
+        }
+      }
       // buffer extents: the group's w13 rows, the m token rows, the scale
       // table this wave reads
-      const uint32_t wbytes = static_cast<uint32_t>(2 * inter) * kbytes;
-      const uint32_t abytes = static_cast<uint32_t>(d.m) * kbytes;
-      const uint32_t sbytes = DT != kFP8 ? 4u
-                            : wave < 2 ? static_cast<uint32_t>(d.m) * (d.H / kQBlock) * 4u
-                                       : static_cast<uint32_t>(2 * inter / kQBlock) * (d.H / kQBlock) * 4u;
-      gu_load_unit<DT>(buffer_rsrc(Wb, wbytes), buffer_rsrc(Ab, abytes),
-                       buffer_rsrc(DT == kFP8 ? sbase : a.w.sx, sbytes), wlane[0], wlane[1],
-                       (whi[0] ? 1u : 0u) | (whi[1] ? 2u : 0u),
-                       wave_on ? static_cast<uint32_t>(kbytes) : 0u, static_cast<uint32_t>(inter),
-                       static_cast<uint32_t>(kbytes), toff[0], toff[1], toff[2], toff[3], soff, nstage, wave,
-                       lds_off(lds));
+      const __amdgpu_buffer_rsrc_t rW = buffer_rsrc(Wb, static_cast<uint32_t>(2 * inter) * kbytes);
+      const __amdgpu_buffer_rsrc_t rA = buffer_rsrc(Ab, static_cast<uint32_t>(d.m) * kbytes);
+      const __amdgpu_buffer_rsrc_t rS = buffer_rsrc(sbase, sbytes);
+      auto load = [&](auto work) {
+        gu_load_unit<DT>(rW, rA, rS, wl, whi, toff, thi, wave_on ? static_cast<uint32_t>(kbytes) : 0u,
+                         static_cast<uint32_t>(inter), static_cast<uint32_t>(kbytes), soff, nstage, wave,
+                         lds_off(lds), work);
+      };
+      if (ntb == kGuTBlocks && wave_on)
+        load([&](int st) {
+          stage(st, std::integral_constant<int, 1>{}, std::integral_constant<int, kGuMBlocks>{});
+        });
+      else
+        load([](int) {});
     } else {
       auto run = [&](auto ntc) {
 #pragma unroll 1
         for (int st = 0; st < nstage; ++st) {
           // every read of the previous stage has landed before the barrier
-          // that hands its slot to the loads
+          // that hands its slots to the loads
           wait_lgkm<0>();
           __builtin_amdgcn_sched_barrier(0);   // nothing moves across a stage boundary
           ring_barrier();
-          if (wave_on) stage(st, ntc);
+          if (wave_on) stage(st, ntc, std::integral_constant<int, 0>{});
         }
       };
       switch (ntb) {
@@ -458,14 +484,17 @@ __global__ __launch_bounds__(kGuThreads, 1) void gu_kernel(GuArgs a) {
     }
     // the trailing loads (the last stage again) land before the slots are
     // refilled: the next unit's first barrier waits for every load
-    // ---- epilogue: lane holds token row 32 t + lr, h columns
+    // ---- epilogue: a multiplying wave's block t (t < 4) and a load wave's
+    // block 4 (in acc[.][0]); lane holds token row 32 t + lr, h columns
     // c0 + 8 (i / 4) + 4 lg + i % 4 for i = 0..15 ----
+    const int nblk = loader ? (ntb == kGuTBlocks ? 1 : 0) : min(ntb, kGuMBlocks);
+    auto row_of = [&](int t) { return loader ? 32 * kGuMBlocks + lr : 32 * t + lr; };
     if constexpr (DT == kBF16) {
       uint16_t *h = static_cast<uint16_t *>(shared ? a.w.h_sh : a.w.h);
 #pragma unroll
-      for (int t = 0; t < kGuTBlocks; ++t) {
-        const int rr = 32 * t + lr;
-        if (loader || !wave_on || rr >= rows) continue;
+      for (int t = 0; t < kGuMBlocks; ++t) {
+        const int rr = row_of(t);
+        if (t >= nblk || !wave_on || rr >= rows) continue;
         uint16_t *hr = h + static_cast<size_t>(seg0 + row0 + rr) * inter + c0 + 4 * lg;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -477,9 +506,11 @@ __global__ __launch_bounds__(kGuThreads, 1) void gu_kernel(GuArgs a) {
         }
       }
     } else {
-      // h per row per 128 columns (this unit's): amax across the 4 waves
+      // h per row per 128 columns (this unit's): amax across the 4 column
+      // waves (rows 0-127: waves 0-3, rows 128-159: waves 4-7)
 #pragma unroll
-      for (int t = 0; t < kGuTBlocks; ++t) {
+      for (int t = 0; t < kGuMBlocks; ++t) {
+        if (t >= nblk) continue;
         float am = 0.f;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -488,15 +519,15 @@ __global__ __launch_bounds__(kGuThreads, 1) void gu_kernel(GuArgs a) {
           am = fmaxf(am, fabsf(hv));
         }
         am = fmaxf(am, __shfl_xor(am, 32));
-        if (!loader && lg == 0) amax_w[wave][32 * t + lr] = am;
+        if (lg == 0) amax_w[wave][row_of(t)] = am;
       }
       __syncthreads();
       uint8_t *h = static_cast<uint8_t *>(shared ? a.w.h_sh : a.w.h);
       float *hs = shared ? a.w.h_sh_scale : a.w.h_scale;
 #pragma unroll
-      for (int t = 0; t < kGuTBlocks; ++t) {
-        const int rr = 32 * t + lr;
-        if (loader || rr >= rows) continue;
+      for (int t = 0; t < kGuMBlocks; ++t) {
+        const int rr = row_of(t);
+        if (t >= nblk || rr >= rows) continue;
         float amax = 0.f;
 #pragma unroll
         for (int w = 0; w < kGuWaves; ++w) amax = fmaxf(amax, amax_w[w][rr]);
