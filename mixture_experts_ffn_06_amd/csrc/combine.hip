@@ -108,12 +108,80 @@ __global__ __launch_bounds__(256) void combine_kernel(
   }
 }
 
+// Without a shared-expert gate (k <= kCombineK): one thread per 8 output
+// columns of one token over a flat grid of m * H / 8 threads (no idle
+// threads past a row's end), and every y row of the token loaded before any
+// is summed, so the k gathers are in flight together.  The sum is the same
+// as combine_kernel's: j ascending, then the shared row.
+constexpr int kCombineK = 8;
+
+template <bool F32>
+__global__ __launch_bounds__(256) void combine_flat_kernel(
+    const float *__restrict__ y, const float *__restrict__ y_sh,
+    const int *__restrict__ slot_of_pair, const float *__restrict__ topk_w,
+    int m, int H, int k, void *__restrict__ out) {
+  const int cpr = H / 8;
+  const long gid = static_cast<long>(blockIdx.x) * 256 + threadIdx.x;
+  if (gid >= static_cast<long>(m) * cpr) return;
+  const int t = static_cast<int>(gid / cpr);
+  const int n0 = static_cast<int>(gid - static_cast<long>(t) * cpr) * 8;
+  size_t row[kCombineK];
+  float wj[kCombineK];
+#pragma unroll
+  for (int j = 0; j < kCombineK; ++j) {
+    row[j] = j < k ? static_cast<size_t>(slot_of_pair[static_cast<size_t>(t) * k + j]) : 0;
+    wj[j] = j < k ? topk_w[static_cast<size_t>(t) * k + j] : 0.f;
+  }
+  float v[kCombineK][8];
+#pragma unroll
+  for (int j = 0; j < kCombineK; ++j)
+    if (j < k) load8<true>(y, row[j] * H + n0, v[j]);
+  float acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+#pragma unroll
+  for (int j = 0; j < kCombineK; ++j)
+    if (j < k) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = fmaf(wj[j], v[j][i], acc[i]);
+    }
+  if (y_sh) {
+    float u[8];
+    load8<true>(y_sh, static_cast<size_t>(t) * H + n0, u);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] += u[i];
+  }
+  if constexpr (F32) {
+    float4 *dst = reinterpret_cast<float4 *>(static_cast<float *>(out) + static_cast<size_t>(t) * H + n0);
+    dst[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    dst[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+  } else {
+    uint4 q;
+    q.x = f32_to_bf16(acc[0]) | (static_cast<uint32_t>(f32_to_bf16(acc[1])) << 16);
+    q.y = f32_to_bf16(acc[2]) | (static_cast<uint32_t>(f32_to_bf16(acc[3])) << 16);
+    q.z = f32_to_bf16(acc[4]) | (static_cast<uint32_t>(f32_to_bf16(acc[5])) << 16);
+    q.w = f32_to_bf16(acc[6]) | (static_cast<uint32_t>(f32_to_bf16(acc[7])) << 16);
+    *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(out) + static_cast<size_t>(t) * H + n0) = q;
+  }
+}
+
 hipError_t launch_combine(const Dims &d, const Inputs &in, const Work &w, const int *topk_idx,
                           const float *topk_w, void *out, hipStream_t s) {
   (void)topk_idx;
-  const dim3 grid((d.H / 8 + 255) / 256, d.m);
   const float *ysh = d.Is > 0 ? w.y_sh : nullptr;
   const void *sg = d.Is > 0 ? in.sgate : nullptr;
+  if (!sg && d.k <= kCombineK) {
+    const long threads = static_cast<long>(d.m) * (d.H / 8);
+    const dim3 fgrid(static_cast<unsigned>((threads + 255) / 256));
+    if (d.wdt == kF32)
+      hipLaunchKernelGGL(combine_flat_kernel<true>, fgrid, dim3(256), 0, s, w.y, ysh, w.slot_of_pair,
+                         topk_w, d.m, d.H, d.k, out);
+    else
+      hipLaunchKernelGGL(combine_flat_kernel<false>, fgrid, dim3(256), 0, s, w.y, ysh, w.slot_of_pair,
+                         topk_w, d.m, d.H, d.k, out);
+    return hipGetLastError();
+  }
+  const dim3 grid((d.H / 8 + 255) / 256, d.m);
   if (d.wdt == kF32)
     hipLaunchKernelGGL(combine_kernel<true>, grid, dim3(256), 0, s, w.y, ysh,
                        w.slot_of_pair, topk_w, in.x, sg, d.m, d.H, d.k, out);

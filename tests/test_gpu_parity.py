@@ -276,6 +276,43 @@ def test_empty_experts_many_tiles():
     assert int((to_np(dbg["counts"]) == 0).sum()) >= 256 - 40
 
 
+# Exact per-expert row counts around the gate/up tile edges (32-row token
+# blocks, 160-row M tiles split evenly: 129 and 159 rows fill five blocks
+# partly, 160 all five, 161 and 321 rows split into two and three tiles).
+# Top-1 routing by construction: router row e is the unit vector at column
+# e and token t carries a clear maximum at its expert's column, so the
+# logits are x[t, :E] and every token's choice is far from a tie.
+TILE_COUNTS = (1, 31, 129, 159, 160, 161, 320, 321, 0)
+
+
+def _counted_inputs(wl, counts, seed):
+    inp = synth.make_inputs(wl, device=DEV)
+    rng = np.random.default_rng(seed)
+    m, H, E = sum(counts), wl.hidden, wl.experts
+    x = rng.standard_normal((m, H)).astype(np.float32)
+    x[:, :E] = np.clip(0.5 * x[:, :E], -2.0, 2.0)
+    owner = np.repeat(np.arange(E), counts)
+    x[np.arange(m), owner] = 4.0
+    rw = np.zeros((E, H), dtype=np.float32)
+    rw[np.arange(E), np.arange(E)] = 1.0
+    inp["x"] = torch.from_numpy(x).to(torch.bfloat16).to(DEV)
+    inp["router_w"] = torch.from_numpy(rw).to(torch.bfloat16).to(DEV)
+    return inp, owner
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("dtype", ["fp8", "bf16"])
+def test_gateup_tile_edges_exact_counts(dtype):
+    m = sum(TILE_COUNTS)
+    wl = synth.Workload(f"tile_edges_{dtype}", m=m, hidden=256, experts=len(TILE_COUNTS), topk=1,
+                        inter=256, shared_inter=128, dtype=dtype, gating="softmax",
+                        routed_scale=1.0, seed=50)
+    inp, owner = _counted_inputs(wl, TILE_COUNTS, seed=51)
+    rep, *_, (out, idx, w, dbg) = run_case(wl, path="grouped", inp=inp)
+    assert (to_np(idx)[:, 0] == owner).all()
+    assert to_np(dbg["counts"]).tolist() == list(TILE_COUNTS)
+
+
 # ------------------------------------------------------ gating variants ---
 # sqrtsoftplus and softmax with a correction bias, no renormalisation, and
 # the sigmoid-gated shared-expert blend (page 3, top-k dispatch and step 8).
