@@ -50,9 +50,10 @@ __global__ __launch_bounds__(256) void router_valu_kernel(
 
 // ---------------------------------------------------------------------------
 // MFMA router for bf16: a block computes 16*MBW tokens x 16*NBW experts with
-// its four waves splitting H; each wave streams its K range of the token and
-// expert rows straight into MFMA operands (16x16x32 bf16, fp32 accumulate)
-// and the four partial tiles are summed through LDS in a fixed order.  Small
+// its NW waves (4, or 8 for the largest tiles) splitting H; each wave
+// streams its K range of the token and expert rows straight into MFMA
+// operands (16x16x32 bf16, fp32 accumulate) and the NW partial tiles are
+// summed through LDS in a fixed order (wave 0's, then 1, 2, ...).  Small
 // tiles keep enough blocks in flight at decode sizes; larger ones cut the
 // re-reads of x and Wr at prefill sizes.
 //
@@ -65,16 +66,28 @@ __global__ __launch_bounds__(256) void router_valu_kernel(
 // scale, an all-zero group gets scale 1).  Each wave's K range is then whole
 // 128-column groups and one batch of four 32-wide steps is one group: the
 // four lanes of a token row hold its 128 values.  Group g is written by the
-// block with blockIdx.x == g % gridDim.x (every expert tile reads the same
+// block of expert tile g % (expert tiles) (every expert tile reads the same
 // x rows), so the quantisation work is spread over all blocks.
-template <int MBW, int NBW, bool SPLIT, bool QUANT = false>
-__global__ __launch_bounds__(256) void router_mfma_kernel(
+template <int MBW, int NBW, bool SPLIT, bool QUANT = false, int NW = 4>
+__global__ __launch_bounds__(NW * 64) void router_mfma_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ wr,
     float *__restrict__ logits, int m, int E, int H,
     uint8_t *__restrict__ xq = nullptr, float *__restrict__ sx = nullptr) {
-  __shared__ f32x4_t part[3][MBW * NBW][kWave];
+  __shared__ f32x4_t part[NW - 1][MBW * NBW][kWave];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int t0 = SPLIT ? 0 : blockIdx.y * 16 * MBW, e0 = blockIdx.x * 16 * NBW;
+  // Without SPLIT the grid is one-dimensional: block b runs on XCD b % 8
+  // (blocks are dealt to the XCDs round-robin), and the ne expert tiles of a
+  // token tile go to consecutive slots of one XCD, so its x rows come from
+  // HBM once and from that XCD's L2 for the other expert tiles.
+  const int ne = SPLIT ? static_cast<int>(gridDim.x) : (E + 16 * NBW - 1) / (16 * NBW);
+  int et = blockIdx.x, tt = SPLIT ? 0 : static_cast<int>(blockIdx.y);
+  if (!SPLIT) {
+    const int j = static_cast<int>(blockIdx.x) >> 3;
+    et = j % ne;
+    tt = (j / ne) * 8 + (static_cast<int>(blockIdx.x) & 7);
+    if (tt * 16 * MBW >= m) return;
+  }
+  const int t0 = SPLIT ? 0 : tt * 16 * MBW, e0 = et * 16 * NBW;
   if (SPLIT) logits += static_cast<size_t>(blockIdx.y) * m * E;
   const int kofs = (lane >> 4) * 8;
   const uint16_t *ap[MBW];
@@ -91,7 +104,7 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(
 #pragma unroll
     for (int j = 0; j < NBW; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const int steps = H / 32;
-  const int parts = SPLIT ? 4 * gridDim.y : 4, part_id = SPLIT ? 4 * blockIdx.y + wave : wave;
+  const int parts = SPLIT ? NW * gridDim.y : NW, part_id = SPLIT ? NW * blockIdx.y + wave : wave;
   const int s0 = steps * part_id / parts, s1 = steps * (part_id + 1) / parts;
   constexpr int BATCH = 4;
   for (int s = s0; s < s1; s += BATCH) {
@@ -118,7 +131,7 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(
               acc[i][j], 0, 0, 0);
     if constexpr (QUANT) {
       const int g = s >> 2;   // this batch's 128-column group
-      if (g % static_cast<int>(gridDim.x) == static_cast<int>(blockIdx.x)) {
+      if (g % ne == et) {
 #pragma unroll
         for (int i = 0; i < MBW; ++i) {
           float v[BATCH][8];
@@ -167,7 +180,7 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(
     for (int j = 0; j < NBW; ++j) {
       f32x4_t v = acc[i][j];
 #pragma unroll
-      for (int w = 0; w < 3; ++w) v += part[w][i * NBW + j][lane];
+      for (int w = 0; w < NW - 1; ++w) v += part[w][i * NBW + j][lane];
       const int e = e0 + 16 * j + (lane & 15);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -177,16 +190,18 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(
     }
 }
 
-template <int MBW, int NBW>
+template <int MBW, int NBW, int NW = 4>
 static hipError_t launch_router_mfma(const Dims &d, const Inputs &in, const Work &w,
                                      hipStream_t s) {
-  const dim3 grid((d.E + 16 * NBW - 1) / (16 * NBW), (d.m + 16 * MBW - 1) / (16 * MBW));
+  // one-dimensional: ne expert tiles x the token tiles rounded up to 8
+  const int ne = (d.E + 16 * NBW - 1) / (16 * NBW), nt = (d.m + 16 * MBW - 1) / (16 * MBW);
+  const dim3 grid(static_cast<unsigned>(ne * ((nt + 7) / 8) * 8));
   if (router_quant_fused(d))
-    hipLaunchKernelGGL((router_mfma_kernel<MBW, NBW, false, true>), grid, dim3(256), 0, s,
+    hipLaunchKernelGGL((router_mfma_kernel<MBW, NBW, false, true, NW>), grid, dim3(NW * 64), 0, s,
                        static_cast<const uint16_t *>(in.x),
                        static_cast<const uint16_t *>(in.router_w), w.logits, d.m, d.E, d.H, w.xq, w.sx);
   else
-    hipLaunchKernelGGL((router_mfma_kernel<MBW, NBW, false>), grid, dim3(256), 0, s,
+    hipLaunchKernelGGL((router_mfma_kernel<MBW, NBW, false, false, NW>), grid, dim3(NW * 64), 0, s,
                        static_cast<const uint16_t *>(in.x),
                        static_cast<const uint16_t *>(in.router_w), w.logits, d.m, d.E, d.H,
                        static_cast<uint8_t *>(nullptr), static_cast<float *>(nullptr));
@@ -208,8 +223,11 @@ hipError_t launch_router(const Dims &d, const Inputs &in, const Work &w,
     // of x and Wr, but four times the blocks), 64 x 64 when those fill them
     const long big_tiles = static_cast<long>((d.E + 63) / 64) * ((d.m + 31) / 32);
     if (big_tiles < 256) return launch_router_mfma<1, 2>(d, in, w, s);
-    // 64 x 64 tiles once they alone fill the CUs: half the re-reads of Wr
-    if (static_cast<long>((d.E + 63) / 64) * ((d.m + 63) / 64) >= 256) return launch_router_mfma<4, 4>(d, in, w, s);
+    // 64 x 64 tiles once they alone fill the CUs: half the re-reads of Wr;
+    // eight waves splitting K where it divides into 1024-column parts (twice
+    // the loads in flight per CU: the loop waits for each batch's loads)
+    if (static_cast<long>((d.E + 63) / 64) * ((d.m + 63) / 64) >= 256)
+      return d.H % 1024 == 0 ? launch_router_mfma<4, 4, 8>(d, in, w, s) : launch_router_mfma<4, 4>(d, in, w, s);
     return launch_router_mfma<2, 4>(d, in, w, s);
   }
   dim3 grid((d.E + kRouterWaves - 1) / kRouterWaves,
