@@ -384,7 +384,11 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void grouped_kernel(GroupedArgs a)
     // again, so the MFMA's short summation (it drops product bits below
     // ~2^-14 of the largest product in each group of eight) stays ~1e-4 of
     // the output.
-    auto compute_fp8 = [&](int st) {
+    // NMB: the wave's first NMB m-blocks (all those with rows), a template
+    // parameter so that reads and MFMAs carry no branches and the compiler's
+    // read waits stay exact.
+    auto compute_fp8 = [&](int st, auto nmbc) {
+      constexpr int NMB = decltype(nmbc)::value;
       if constexpr (C::SCALED) {
         const uint8_t *sa = lds + (st % C::DA) * C::A_BYTES;
         const uint8_t *sb = lds + C::DA * C::A_BYTES + (st % DEPTH) * C::B_STAGE;
@@ -392,54 +396,55 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void grouped_kernel(GroupedArgs a)
         const uint8_t *lb0 = sb + wn * NB * BLK + loff[0];
         const uint32_t d1 = loff[1] - loff[0];   // the lane's second piece
         const uint8_t *ssc = sb + C::B_BYTES;
-        // A pieces, row scales (rows mrow(mb)*16 + 4*kg + i: contiguous
-        // floats) and the weight-block scales of this column group
-        u32x4_t aq[2 * MBW], sv[MBW], sw[NB / 4];
+        // Reads in the order the MFMAs use them -- the weight-block scales
+        // and the wave's weight blocks, then per m-block its A pieces and
+        // row scales (rows mrow(mb)*16 + 4*kg + i: contiguous floats) -- so
+        // the first MFMA waits only for the weights and the first m-block,
+        // not for every read of the stage.
+        u32x4_t aq[2 * MBW], sv[MBW], sw[NB / 4], bq[2 * NB];
         const uint8_t *lsr = ssc + ((wm * 16) + 4 * kg) * 4;
         const uint8_t *lsw = ssc + C::ROW_WAVES * 256 + wn * NB * 4;
-        static_for<0, MBW>([&](auto ic) {
-          constexpr int mb = decltype(ic)::value;
-          if (mrow(mb) < nmb) {   // m-blocks past the rows are neither read nor multiplied
-            aq[2 * mb] = lds_load<u32x4_t>(la0 + mb * WM * BLK);
-            aq[2 * mb + 1] = lds_load<u32x4_t>(la0 + d1 + mb * WM * BLK);
-            sv[mb] = lds_load<u32x4_t>(lsr + mb * WM * 64);
-          }
-        });
         static_for<0, NB / 4>([&](auto ic) {
           constexpr int q = decltype(ic)::value;
           sw[q] = lds_load<u32x4_t>(lsw + q * 16);
         });
-        // weight blocks four at a time
 #pragma unroll
-        for (int j0 = 0; j0 < NB; j0 += 4) {
-          u32x4_t bq[8];
-          const uint8_t *lb = lb0 + j0 * BLK;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            bq[2 * j] = lds_load<u32x4_t>(lb + j * BLK);
-            bq[2 * j + 1] = lds_load<u32x4_t>(lb + d1 + j * BLK);
-          }
-#pragma unroll
-          for (int mb = 0; mb < MBW; ++mb) {
-            if (mrow(mb) >= nmb) continue;   // no rows in this m-block
-            // h row scale x weight-block scale: the wave's blocks are 16 * NB
-            // <= 64 consecutive 16-aligned output columns, inside one
-            // 128-row weight-scale block
-            const float ws = __uint_as_float(sw[0][0]);
-            float sc[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) sc[i] = __uint_as_float(sv[mb][i]) * ws;
-            const i32x8_t av = as_i32x8(aq[2 * mb], aq[2 * mb + 1]);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
-              const f32x4_t p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                  av, as_i32x8(bq[2 * j], bq[2 * j + 1]), z, 0, 0, 0, 127, 0, 127);
-#pragma unroll
-              for (int i = 0; i < 4; ++i) acc[mb][j0 + j][i] = fmaf(p[i], sc[i], acc[mb][j0 + j][i]);
-            }
-          }
+        for (int j = 0; j < NB; ++j) {
+          bq[2 * j] = lds_load<u32x4_t>(lb0 + j * BLK);
+          bq[2 * j + 1] = lds_load<u32x4_t>(lb0 + d1 + j * BLK);
         }
+        __builtin_amdgcn_sched_barrier(0);
+        // m-blocks past the rows are neither read nor multiplied; an
+        // m-block's reads go out two m-blocks ahead of its MFMAs
+        auto load_mb = [&](auto ic) {
+          constexpr int mb = decltype(ic)::value;
+          aq[2 * mb] = lds_load<u32x4_t>(la0 + mb * WM * BLK);
+          aq[2 * mb + 1] = lds_load<u32x4_t>(la0 + d1 + mb * WM * BLK);
+          sv[mb] = lds_load<u32x4_t>(lsr + mb * WM * 64);
+          __builtin_amdgcn_sched_barrier(0);
+        };
+        static_for<0, (NMB < 2 ? NMB : 2)>([&](auto ic) { load_mb(ic); });
+        static_for<0, NMB>([&](auto ic) {
+          constexpr int mb = decltype(ic)::value;
+          if constexpr (mb + 2 < NMB) load_mb(std::integral_constant<int, mb + 2>{});
+          // h row scale x weight-block scale: the wave's blocks are 16 * NB
+          // <= 64 consecutive 16-aligned output columns, inside one
+          // 128-row weight-scale block
+          const float ws = __uint_as_float(sw[0][0]);
+          float sc[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sc[i] = __uint_as_float(sv[mb][i]) * ws;
+          const i32x8_t av = as_i32x8(aq[2 * mb], aq[2 * mb + 1]);
+#pragma unroll
+          for (int j = 0; j < NB; ++j) {
+            const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+            const f32x4_t p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                av, as_i32x8(bq[2 * j], bq[2 * j + 1]), z, 0, 0, 0, 127, 0, 127);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[mb][j][i] = fmaf(p[i], sc[i], acc[mb][j][i]);
+          }
+          __builtin_amdgcn_sched_barrier(0);   // m-block by m-block, as the reads arrive
+        });
       }
     };
 
@@ -505,19 +510,30 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void grouped_kernel(GroupedArgs a)
       // free slots), so the count is the same along every path and the loop
       // has no branch around its loads. ----
       const int last = nstage - 1;
-      issue_b(0, 0);
-      issue_a(0, 0);
-      issue_b(min(1, last), 1);
+      auto run_fp8 = [&](auto nmbc) {
+        issue_b(0, 0);
+        issue_a(0, 0);
+        issue_b(min(1, last), 1);
 #pragma unroll 1
-      for (int st = 0; st < nstage; ++st) {
-        __builtin_amdgcn_sched_barrier(0);   // nothing moves across a stage boundary
-        wait_vm<C::LB>();
-        wait_lgkm<0>();   // the previous stage's reads have landed
-        ring_barrier();
-        issue_a(min(st + 1, last), st + 1);
-        issue_b(min(st + 2, last), st + 2);
-        if (rows_on) compute_fp8(st);
-      }
+        for (int st = 0; st < nstage; ++st) {
+          __builtin_amdgcn_sched_barrier(0);   // nothing moves across a stage boundary
+          wait_vm<C::LB>();
+          wait_lgkm<0>();   // the previous stage's reads have landed
+          ring_barrier();
+          issue_a(min(st + 1, last), st + 1);
+          issue_b(min(st + 2, last), st + 2);
+          if constexpr (decltype(nmbc)::value > 0) compute_fp8(st, nmbc);
+        }
+      };
+      // the wave's m-blocks with rows: mrow(mb) = mfirst + WM mb < nmb.
+      // Four loop variants (more cost registers): all MBW, MBW - 1, up to
+      // MBW - 2 (the m-blocks past the rows are then read and multiplied
+      // but not stored: their rows lie past the tile's), none.
+      const int nmbw = rows_on ? min(MBW, (nmb - mfirst + WM - 1) / WM) : 0;
+      if (nmbw == MBW) run_fp8(std::integral_constant<int, MBW>{});
+      else if (nmbw == MBW - 1) run_fp8(std::integral_constant<int, MBW - 1>{});
+      else if (nmbw > 0) run_fp8(std::integral_constant<int, MBW - 2>{});
+      else run_fp8(std::integral_constant<int, 0>{});
     }
     __syncthreads();
 
