@@ -313,8 +313,8 @@ __global__ __launch_bounds__(kGuThreads, 1) void gu_kernel(GuArgs a) {
     // operation per accumulator and K block (as a separate partial sum would
     // take) but no registers for partials, and each accumulator block's
     // rescale sits between the last MFMAs of the others.
-    // One stage: the lane's LDS reads of operand pieces (fp8: after its
-    // token and weight-block scales), issued one piece ahead, the MFMAs of
+    // One stage: the lane's LDS reads of operand pieces (fp8: its token and
+    // weight-block scales after piece 0), issued one piece ahead, the MFMAs of
     // each piece's steps in between; NT token blocks from block T0 (template
     // parameters keep the MFMA sequence free of branches).
     auto stage = [&](int st, auto ntc, auto t0c) {
@@ -327,6 +327,17 @@ __global__ __launch_bounds__(kGuThreads, 1) void gu_kernel(GuArgs a) {
       u32x4_t wr[4][2], tr[4][NT];
       uint32_t sxr[2][NT];     // [this K block, next][token block]
       u32x2_t swr[2];
+      auto load_piece = [&](auto jc) {
+        constexpr int j = decltype(jc)::value;
+        wr[j][0] = lds_load<u32x4_t>(lw + loff[j]);
+        wr[j][1] = lds_load<u32x4_t>(lw + loff[j] + 32 * kGuRowBytes);
+        static_for<0, NT>([&](auto tc) {
+          constexpr int t = decltype(tc)::value;
+          tr[j][t] = lds_load<u32x4_t>(lt + loff[j] + 32 * kGuRowBytes * t);
+        });
+      };
+      // piece 0 first: the scales are needed only after piece 3
+      load_piece(std::integral_constant<int, 0>{});
       if constexpr (DT == kFP8) {
         const uint8_t *ls = sw + C::W_BYTES;
         static_for<0, NT>([&](auto tc) {
@@ -337,16 +348,6 @@ __global__ __launch_bounds__(kGuThreads, 1) void gu_kernel(GuArgs a) {
         swr[0] = lds_load<u32x2_t>(ls + 768);
         swr[1] = lds_load<u32x2_t>(ls + 1024 + 768);
       }
-      auto load_piece = [&](auto jc) {
-        constexpr int j = decltype(jc)::value;
-        wr[j][0] = lds_load<u32x4_t>(lw + loff[j]);
-        wr[j][1] = lds_load<u32x4_t>(lw + loff[j] + 32 * kGuRowBytes);
-        static_for<0, NT>([&](auto tc) {
-          constexpr int t = decltype(tc)::value;
-          tr[j][t] = lds_load<u32x4_t>(lt + loff[j] + 32 * kGuRowBytes * t);
-        });
-      };
-      load_piece(std::integral_constant<int, 0>{});
       static_for<0, 4>([&](auto jc) {
         constexpr int j = decltype(jc)::value;
         // the reads of piece j + 1 go out before the MFMAs of piece j; the
