@@ -73,6 +73,7 @@ constexpr int kGuTBlocks = 5;      // token blocks of 32 rows per unit (block 4 
 constexpr int kGuTRows = 32 * kGuTBlocks;
 constexpr int kGuDepth = 3;        // weight (and scale) slots
 constexpr int kGuTDepth = 2;       // token slots
+constexpr int kGuFewRounds = 4;    // unit rounds up to which the shared expert's units run first
 
 template <int DT>
 struct GuCfg {
@@ -263,8 +264,16 @@ __global__ __launch_bounds__(kGuThreads, 1) void gu_kernel(GuArgs a) {
 
 #pragma unroll 1
   for (int r = 0; r * P < total; ++r) {
-    const int uu = r * P + xcd * per_xcd + slot_id;
-    if (uu >= total) continue;
+    const int u = r * P + xcd * per_xcd + slot_id;
+    if (u >= total) continue;
+    // Position u runs unit uu.  When the units fill at most kGuFewRounds
+    // rounds of the grid, the last, partly filled round is a large share of
+    // the launch: the shared expert's S units (last in group order, the
+    // fullest tiles) then run first, so that lighter routed units form that
+    // round.  (With many rounds the order was neutral to slightly slower.)
+    const int S = d.Is > 0 ? total - uoff[d.E] : 0;
+    const bool shared_first = S > 0 && S < total && total <= kGuFewRounds * P;
+    const int uu = shared_first ? (u < S ? total - S + u : u - S) : u;
     // ---- decode the unit (block-uniform) ----
     int lo = 0, hi = G - 1;
     while (lo < hi) {
