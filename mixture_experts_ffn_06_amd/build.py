@@ -32,8 +32,13 @@ FLAGS = [
 
 # Per-file additions: the gate/up kernel keeps its accumulators in VGPRs
 # (its fp8 path rescales them with VALU multiplies, which cannot read AGPRs),
-# so its MFMAs take the VGPR form.
-FILE_FLAGS = {"gateup.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# so its MFMAs take the VGPR form.  The persistent GEMMs fetch their next
+# unit ticket with a one-lane atomic whose result is used only when the unit
+# ends; the atomic optimizer would rewrite it into a wave-wide form that
+# waits for the result at once.
+_NO_ATOMIC_OPT = ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]
+FILE_FLAGS = {"gateup.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", *_NO_ATOMIC_OPT],
+              "grouped.hip": _NO_ATOMIC_OPT}
 
 
 def file_flags(src: str) -> list:

@@ -73,7 +73,8 @@ constexpr int kGuTBlocks = 5;      // token blocks of 32 rows per unit (block 4 
 constexpr int kGuTRows = 32 * kGuTBlocks;
 constexpr int kGuDepth = 3;        // weight (and scale) slots
 constexpr int kGuTDepth = 2;       // token slots
-constexpr int kGuFewRounds = 4;    // unit rounds up to which the shared expert's units run first
+constexpr int kGuFewRounds = 4;    // unit rounds of the grid up to which a launch counts as short
+constexpr int kGuFewChunk = 8;     // units per XCD chunk in a short launch
 
 template <int DT>
 struct GuCfg {
@@ -212,6 +213,11 @@ __global__ __launch_bounds__(kGuThreads, 1) void gu_kernel(GuArgs a) {
   const int wave = loader ? wave_id - kGuWaves : wave_id;   // the column wave served / itself
   const int G = d.E + (d.Is > 0 ? 1 : 0);
   const int *offsets = a.w.offsets;
+  // this block's next ticket from its XCD's unit queue (the prefix's
+  // barriers publish the first one)
+  __shared__ int tk_next;
+  int *const queue = a.w.queue + kQueueStride * (blockIdx.x & 7);
+  if (tid == 0) tk_next = atomicAdd(queue, 1);
 
   // ---- unit prefix: units(g) = ceil(rows_g / 160) * ntile_g ----
   {
@@ -251,8 +257,20 @@ __global__ __launch_bounds__(kGuThreads, 1) void gu_kernel(GuArgs a) {
   }
   const int total = uoff[G];
   const int P = gridDim.x;
-  const int per_xcd = P / 8;
-  const int xcd = blockIdx.x & 7, slot_id = blockIdx.x >> 3;
+  const int xcd = blockIdx.x & 7;
+  // Units go to the XCDs in chunks of consecutive units (chunk c to XCD
+  // c % 8: the M tiles of an N tile, or the N tiles of a group, run side by
+  // side on one L2), and each XCD's blocks take its units in order, one
+  // ticket of the XCD's counter each, so a block that finishes early takes
+  // the next unit.  A short launch (units for at most kGuFewRounds rounds of
+  // the grid) deals chunks of kGuFewChunk units, spreading heavy units over
+  // the XCDs, and runs the shared expert's S units (last in group order,
+  // the fullest tiles) first, so that lighter routed units come last.  (In
+  // long launches shared-first measured neutral to slightly slower.)
+  const bool few = total <= kGuFewRounds * P;
+  const int chunk = few ? kGuFewChunk : P / 8;
+  const int S = d.Is > 0 ? total - uoff[d.E] : 0;
+  const bool shared_first = few && S > 0 && S < total;
 
   const int lg = lane >> 5, lr = lane & 31;   // lane group, row inside a block
   // the lane's read offsets inside a 32-row block, pieces j = 0..3
@@ -263,16 +281,11 @@ __global__ __launch_bounds__(kGuThreads, 1) void gu_kernel(GuArgs a) {
   const int drow = lane >> 3, dpiece = lane & 7;
 
 #pragma unroll 1
-  for (int r = 0; r * P < total; ++r) {
-    const int u = r * P + xcd * per_xcd + slot_id;
-    if (u >= total) continue;
-    // Position u runs unit uu.  When the units fill at most kGuFewRounds
-    // rounds of the grid, the last, partly filled round is a large share of
-    // the launch: the shared expert's S units (last in group order, the
-    // fullest tiles) then run first, so that lighter routed units form that
-    // round.  (With many rounds the order was neutral to slightly slower.)
-    const int S = d.Is > 0 ? total - uoff[d.E] : 0;
-    const bool shared_first = S > 0 && S < total && total <= kGuFewRounds * P;
+  for (;;) {
+    __syncthreads();   // tk_next holds this block's ticket
+    const int tk = tk_next;
+    const int u = (tk / chunk) * (8 * chunk) + xcd * chunk + tk % chunk;   // increasing in tk
+    if (u >= total) break;
     const int uu = shared_first ? (u < S ? total - S + u : u - S) : u;
     // ---- decode the unit (block-uniform) ----
     int lo = 0, hi = G - 1;
@@ -408,7 +421,11 @@ __global__ __launch_bounds__(kGuThreads, 1) void gu_kernel(GuArgs a) {
       });
     };
 
-    __syncthreads();   // the previous unit is done with every slot and amax_w
+    __syncthreads();   // every wave has read its ticket (tk_next is refilled at the unit's end)
+    // the ticket after this one, fetched while the unit runs (issued after
+    // the unit's own global loads above: loads complete in order)
+    int tk_new = 0;
+    if (tid == 0) tk_new = atomicAdd(queue, 1);
     // ---- the ring: stage st is multiplied from its slots while stages
     // st + 1 (tokens) and st + 2 (weights) load (gu_load_unit); both sides
     // take exactly nstage barriers per unit ----
@@ -554,6 +571,8 @@ __global__ __launch_bounds__(kGuThreads, 1) void gu_kernel(GuArgs a) {
         }
       }
     }
+    // every wave has read tk_next (the barrier before the ring)
+    if (tid == 0) tk_next = tk_new;
   }
 }
 

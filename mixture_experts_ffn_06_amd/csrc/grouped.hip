@@ -101,6 +101,11 @@ struct GroupedArgs {
   int order;          // kOrderGroups or kOrderSharedFirst (bf16)
 };
 
+// A launch with units for at most kFewRounds rounds of the grid deals them to
+// the XCDs in chunks of kFewChunk units (else one chunk per block of an XCD).
+constexpr int kFewRounds = 8;
+constexpr int kFewChunk = 8;
+
 // Order in which the persistent blocks take the units.
 enum : int {
   kOrderGroups = 0,       // routed experts in order, then the shared expert
@@ -119,6 +124,11 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void grouped_kernel(GroupedArgs a)
   const int wn = wave % WN, wm = wave / WN;
   const int G = d.E + (d.Is > 0 ? 1 : 0);
   const int *offsets = a.w.offsets;
+  // this block's next ticket from its XCD's unit queue (the prefix's
+  // barriers publish the first one)
+  __shared__ int tk_next;
+  int *const queue = a.w.queue + kQueueStride * (8 + (blockIdx.x & 7));
+  if (tid == 0) tk_next = atomicAdd(queue, 1);
 
   // ---- unit prefix: units(g) = ceil(rows_g / BM) * ntile_g ----
   {
@@ -158,8 +168,14 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void grouped_kernel(GroupedArgs a)
   }
   const int total = uoff[G];
   const int P = gridDim.x;
-  const int per_xcd = P / 8;
-  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int xcd = blockIdx.x & 7;
+  // Units go to the XCDs in chunks of consecutive units (chunk c to XCD
+  // c % 8: units of one expert run side by side on one L2), and each XCD's
+  // blocks take its units in order, one ticket of the XCD's counter each, so
+  // a block that finishes early takes the next unit.  A short launch (units
+  // for at most kFewRounds rounds of the grid) deals chunks of kFewChunk
+  // units, which spreads long units over the XCDs.
+  const int chunk = total <= kFewRounds * P ? kFewChunk : P / 8;
 
   // Piece position p of row r inside a step block holds the row's 16-byte
   // piece p ^ swz(r).
@@ -167,12 +183,11 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void grouped_kernel(GroupedArgs a)
   const int lrow = lane / C::CPR;                    // row of this lane in a load instruction
   const int lpiece = lane % C::CPR;
 
-  for (int r = 0; r * P < total; ++r) {
-    // Consecutive units go to consecutive slots of one XCD (block ids are
-    // dealt to the 8 XCDs round-robin), so units of one expert run side by
-    // side on one L2.
-    const int u = r * P + xcd * per_xcd + slot;
-    if (u >= total) continue;
+  for (;;) {
+    __syncthreads();   // tk_next holds this block's ticket
+    const int tk = tk_next;
+    const int u = (tk / chunk) * (8 * chunk) + xcd * chunk + tk % chunk;   // increasing in tk
+    if (u >= total) break;
     // Position u runs unit uu.  The S shared-expert units are last in group
     // order; kOrderSharedFirst runs them first, so that longer units (K = I_s
     // > I) do not form the tail.  (fp8 kernels: compiled out.)
@@ -448,7 +463,11 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void grouped_kernel(GroupedArgs a)
       }
     };
 
-    __syncthreads();   // the previous unit is done with every slot
+    __syncthreads();   // every wave has read its ticket (tk_next is refilled at the unit's end)
+    // the ticket after this one, fetched while the unit runs (issued after
+    // the unit's own global loads above: loads complete in order)
+    int tk_new = 0;
+    if (tid == 0) tk_new = atomicAdd(queue, 1);
     if constexpr (DT == kBF16) {
       // ---- bf16: split ring (A 2 slots, B DEPTH slots), one barrier per
       // stage, operands read into registers one stage ahead.  Issue order:
@@ -555,6 +574,8 @@ __global__ __launch_bounds__(WN * WM * 64, 1) void grouped_kernel(GroupedArgs a)
         }
       }
     }
+    // every wave has read tk_next (the barrier before the ring)
+    if (tid == 0) tk_next = tk_new;
   }
 }
 

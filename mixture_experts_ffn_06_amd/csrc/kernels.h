@@ -60,7 +60,14 @@ struct Work {
   float *h_sh_scale;    // [m,Is/128]
   float *y;             // [te,H]  routed down output (sorted rows), fp32
   float *y_sh;          // [m,H]   shared down output, fp32
+  int *queue;           // [kQueueInts] per-XCD unit tickets of the persistent
+                        // GEMMs (gate/up: XCD x at kQueueStride x, down: at
+                        // kQueueStride (8 + x)), zeroed by the routing sort
 };
+
+// Unit queues: one counter per XCD and GEMM, each on its own 128-byte line.
+constexpr int kQueueStride = 32;
+constexpr int kQueueInts = 16 * kQueueStride;
 
 // permute.hip: one block below kPermMultiMin pairs, else chunks of
 // perm_chunk(te) pairs, about eight of them (needs Work::perm_blk of

@@ -71,7 +71,7 @@ int resolve_path(const moe_config_t &c, int m) {
 struct Layout {
   enum {
     kLogits, kRpart, kCounts, kOffsets, kSorted, kSlot, kLrank, kActive, kNactive, kRbOff, kPermBlk, kXq,
-    kSx, kH, kHs, kHsh, kHshs, kY, kYsh, kN
+    kSx, kH, kHs, kHsh, kHshs, kY, kYsh, kQueue, kN
   };
   size_t size[kN];
   size_t off[kN];
@@ -105,6 +105,7 @@ Layout layout(const moe_plan_s &p, int m) {
   L.size[Layout::kHshs] = fp8 ? m * (Is / 128) * 4 : 0;
   L.size[Layout::kY] = te * H * yb;
   L.size[Layout::kYsh] = Is > 0 ? m * H * yb : 0;
+  L.size[Layout::kQueue] = moe::kQueueInts * 4;
   size_t o = 0;
   for (int i = 0; i < Layout::kN; ++i) {
     L.off[i] = o;
@@ -137,6 +138,7 @@ moe::Work carve(const Layout &L, void *ws) {
   w.h_sh_scale = static_cast<float *>(at(Layout::kHshs));
   w.y = static_cast<float *>(at(Layout::kY));
   w.y_sh = static_cast<float *>(at(Layout::kYsh));
+  w.queue = static_cast<int *>(at(Layout::kQueue));
   return w;
 }
 

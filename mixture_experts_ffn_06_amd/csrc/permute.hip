@@ -27,11 +27,12 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
     const int *__restrict__ topk_idx, int te, int E,
     int *__restrict__ counts, int *__restrict__ offsets,
     int *__restrict__ sorted_pair, int *__restrict__ slot_of_pair,
-    int *__restrict__ lrank, int *__restrict__ active, int *__restrict__ nactive, int *__restrict__ rboff) {
+    int *__restrict__ lrank, int *__restrict__ active, int *__restrict__ nactive, int *__restrict__ rboff,
+    int *__restrict__ queue) {
   extern __shared__ int wcnt[];          // [kPermWaves][E]
   __shared__ int scan_tmp[kPermWaves];
   permute_block(topk_idx, te, E, wcnt, scan_tmp, counts, offsets, sorted_pair, slot_of_pair,
-                lrank, active, nactive, rboff);
+                lrank, active, nactive, rboff, queue);
 }
 
 // ---------------------------------------------------------------------------
@@ -59,13 +60,13 @@ __global__ __launch_bounds__(kPermThreads) void permute_hist_kernel(const int *_
 __global__ __launch_bounds__(kPermThreads) void permute_scan_kernel(int nblk, int E, int *__restrict__ blk,
                                                                     int *__restrict__ counts, int *__restrict__ offsets,
                                                                     int *__restrict__ active, int *__restrict__ nactive,
-                                                                    int *__restrict__ rboff) {
+                                                                    int *__restrict__ rboff, int *__restrict__ queue) {
   __shared__ int scan_tmp[kPermWaves];
   const int x = threadIdx.x;
   int tot = 0;
   if (x < E)
     for (int b = 0; b < nblk; ++b) tot += blk[static_cast<size_t>(b) * E + x];
-  const int off = expert_offsets(tot, E, scan_tmp, counts, offsets, active, nactive, rboff);
+  const int off = expert_offsets(tot, E, scan_tmp, counts, offsets, active, nactive, rboff, queue);
   if (x < E) {
     int run = off;
     for (int b = 0; b < nblk; ++b) {
@@ -103,13 +104,13 @@ hipError_t launch_permute(const Dims &d, const int *topk_idx, const Work &w,
   if (nblk == 0) {
     hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(kPermThreads), lds, s, topk_idx,
                        d.te, d.E, w.counts, w.offsets, w.sorted_pair, w.slot_of_pair,
-                       w.lrank, w.active, w.nactive, w.rboff);
+                       w.lrank, w.active, w.nactive, w.rboff, w.queue);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(permute_hist_kernel, dim3(nblk), dim3(kPermThreads), d.E * sizeof(int), s,
                      topk_idx, d.te, d.E, chunk, w.perm_blk);
   hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(kPermThreads), 0, s, nblk, d.E, w.perm_blk,
-                     w.counts, w.offsets, w.active, w.nactive, w.rboff);
+                     w.counts, w.offsets, w.active, w.nactive, w.rboff, w.queue);
   hipLaunchKernelGGL(permute_scatter_kernel, dim3(nblk), dim3(kPermThreads), lds, s, topk_idx, d.te, d.E,
                      chunk, w.perm_blk, w.sorted_pair, w.slot_of_pair, w.lrank);
   return hipGetLastError();

@@ -317,7 +317,7 @@ __global__ __launch_bounds__(kFusedThreads) void topk_permute_kernel(Dims d, Inp
   // ---- stable sort by expert: the few pairs of a decode batch by one wave ----
   if (wave == 0)
     permute_wave(idx_s, d.te, E, wcnt, lrank, w.counts, w.offsets, w.sorted_pair, w.slot_of_pair,
-                 w.active, w.nactive, w.rboff);
+                 w.active, w.nactive, w.rboff, w.queue);
 }
 
 hipError_t launch_topk_permute(const Dims &d, const Inputs &in, const Work &w, int *topk_idx,

@@ -2,6 +2,7 @@
 // their own kernels and by the fused single-block routing kernel.
 #pragma once
 #include "common.h"
+#include "kernels.h"
 
 namespace moe {
 
@@ -275,12 +276,14 @@ __device__ __forceinline__ void chunk_scatter(const int *topk_idx, int c0, int c
 // Expert totals -> counts, offsets, the active list and, per active slot,
 // the prefix of its 16-row blocks (rboff[s] = sum over the active slots
 // before s of ceil(rows / 16), rboff[nactive] = their total: the
-// small-batch kernels' items); returns offsets[x] for thread x
-// (E <= kPermThreads).
+// small-batch kernels' items), and zeroes the GEMMs' unit queues; returns
+// offsets[x] for thread x (E <= kPermThreads).
 __device__ __forceinline__ int expert_offsets(int tot, int E, int *scan_tmp, int *__restrict__ counts,
                                               int *__restrict__ offsets, int *__restrict__ active,
-                                              int *__restrict__ nactive, int *__restrict__ rboff) {
+                                              int *__restrict__ nactive, int *__restrict__ rboff,
+                                              int *__restrict__ queue) {
   const int x = threadIdx.x;
+  if (x < kQueueInts / kQueueStride) queue[kQueueStride * x] = 0;
   int all_pairs, all_active, all_rb;
   const int off = block_exclusive_scan(x < E ? tot : 0, scan_tmp, &all_pairs);
   const int aoff = block_exclusive_scan(x < E && tot > 0 ? 1 : 0, scan_tmp, &all_active);
@@ -307,13 +310,15 @@ __device__ __forceinline__ int expert_offsets(int tot, int E, int *scan_tmp, int
 // of E ints), the expert totals are scanned by the wave (lane l takes
 // experts [l P, l P + P), P = ceil(E / 64)), and each pair goes to its
 // expert's start plus its rank: the same stable order as permute_block.
-// lrank: te ints of LDS or global memory.
+// lrank: te ints of LDS or global memory.  Also zeroes the GEMMs' unit
+// queues.
 __device__ __forceinline__ void permute_wave(
     const int *topk_idx, int te, int E, int *cnt, int *__restrict__ lrank,
     int *__restrict__ counts, int *__restrict__ offsets, int *__restrict__ sorted_pair,
     int *__restrict__ slot_of_pair, int *__restrict__ active, int *__restrict__ nactive,
-    int *__restrict__ rboff) {
+    int *__restrict__ rboff, int *__restrict__ queue) {
   const int lane = threadIdx.x & 63;
+  if (lane < kQueueInts / kQueueStride) queue[kQueueStride * lane] = 0;
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   const uint64_t above = (lane == 63) ? 0ull : (~0ull << (lane + 1));
   for (int e = lane; e < E; e += kWave) cnt[e] = 0;
@@ -384,13 +389,14 @@ __device__ __forceinline__ void permute_block(
     const int *topk_idx, int te, int E, int *wcnt, int *scan_tmp,
     int *__restrict__ counts, int *__restrict__ offsets,
     int *__restrict__ sorted_pair, int *__restrict__ slot_of_pair,
-    int *__restrict__ lrank, int *__restrict__ active, int *__restrict__ nactive, int *__restrict__ rboff) {
+    int *__restrict__ lrank, int *__restrict__ active, int *__restrict__ nactive, int *__restrict__ rboff,
+    int *__restrict__ queue) {
   chunk_ranks(topk_idx, 0, te, E, wcnt, lrank);
   const int x = threadIdx.x;
   int tot = 0;
   if (x < E)
     for (int w = 0; w < kPermWaves; ++w) tot += wcnt[w * E + x];
-  const int off = expert_offsets(tot, E, scan_tmp, counts, offsets, active, nactive, rboff);
+  const int off = expert_offsets(tot, E, scan_tmp, counts, offsets, active, nactive, rboff, queue);
   chunk_bases(E, wcnt, off);
   chunk_scatter(topk_idx, 0, te, E, wcnt, lrank, sorted_pair, slot_of_pair);
 }
