@@ -407,15 +407,28 @@ __global__ __launch_bounds__(kGuThreads, 1) void gu_kernel(GuArgs a) {
             // the K block is done: to the next block's scale (after the last
             // block, to its own scale: acc becomes the sum itself)
             const bool last = st + 1 == nstage;
+            if constexpr (NT >= 2) {
+              // ratio = (token ratio) x (weight-block ratio): NT + 2
+              // reciprocals instead of 2 NT
+              float tq[NT], wq[2];
 #pragma unroll
-            for (int t = 0; t < NT; ++t)
+              for (int t = 0; t < NT; ++t)
+                tq[t] = __uint_as_float(sxr[0][t]) * __builtin_amdgcn_rcpf(last ? 1.0f : __uint_as_float(sxr[1][t]));
+#pragma unroll
+              for (int b = 0; b < 2; ++b)
+                wq[b] = __uint_as_float(swr[0][b]) * __builtin_amdgcn_rcpf(last ? 1.0f : __uint_as_float(swr[1][b]));
+#pragma unroll
+              for (int t = 0; t < NT; ++t)
+#pragma unroll
+                for (int b = 0; b < 2; ++b) acc[b][t] *= tq[t] * wq[b];
+            } else {
 #pragma unroll
               for (int b = 0; b < 2; ++b) {
-                const float s0 = __uint_as_float(sxr[0][t]) * __uint_as_float(swr[0][b]);
-                const float s1 = __uint_as_float(sxr[1][t]) * __uint_as_float(swr[1][b]);
-                const float r = last ? s0 : s0 * __builtin_amdgcn_rcpf(s1);
-                acc[b][t] *= r;
+                const float s0 = __uint_as_float(sxr[0][0]) * __uint_as_float(swr[0][b]);
+                const float s1 = __uint_as_float(sxr[1][0]) * __uint_as_float(swr[1][b]);
+                acc[b][0] *= last ? s0 : s0 * __builtin_amdgcn_rcpf(s1);
               }
+            }
           }
         }
       });
