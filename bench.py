@@ -222,9 +222,12 @@ CPU_SAMPLE = {"decode_bf16": (16, 3), "decode_mxfp4": (16, 3), "decode_mxfp8": (
               "dense_bf16": (8, 1), "dense_fp8": (2, 1), "tiny_f32": (4, 3)}
 
 
-def measure(wl, m, args, launch, cpu):
+def measure(wl, m, args, launch, cpu, min_warm_s=0.0):
     """One workload: K timed layer forwards (inputs resident in HBM), the
-    dominant kernel against its roofline and, if ``cpu``, the CPU oracle."""
+    dominant kernel against its roofline and, if ``cpu``, the CPU oracle.
+    ``min_warm_s``: after the W warm-up steps, more untimed steps until that
+    much time has passed (entries that follow another entry's host-only CPU
+    leg, when the GPU sat idle, and whose timed region is a few ms)."""
     import numpy as np
     import torch
     import synth
@@ -298,6 +301,15 @@ def measure(wl, m, args, launch, cpu):
             graphs[i % copies].replay()
     else:
         kev = [dom_events() for _ in range(args.steps)] if args.kernel_events == "timed" else None
+    torch.cuda.synchronize()
+    t_warm = time.perf_counter()
+    while time.perf_counter() - t_warm < min_warm_s:
+        for i in range(8):
+            if graphs is not None:
+                graphs[i % copies].replay()
+            else:
+                step(i)
+        torch.cuda.synchronize()
     bounds = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     for ev in bounds:
         _event_handle(ev)
@@ -420,7 +432,7 @@ def main():
                 continue
             print(f"bench: {name} m={mm} ({launch})", file=sys.stderr, flush=True)
             entries.append(measure(synth.WORKLOADS[name], mm, args, launch,
-                                   not args.no_cpu_baseline))
+                                   not args.no_cpu_baseline, min_warm_s=0.2))
         result["configs"] = entries
     print(json.dumps(result), flush=True)
 
