@@ -194,8 +194,10 @@ int moe_plan(const moe_config_t *cfg, moe_plan_t *plan_out);
  * of logits, expert ids, weights and quantised h buffers; forward_prefill.rs,
  * page 3, step 2: the top-k indices and weights in the shared scratch).  The
  * workspace holds logits, the permutation, the list of experts with rows and
- * their row-block prefix, quantised activations, the sorted intermediates
- * and, for calls of <= 16 tokens, the router's partial sums. */
+ * their row-block prefix, quantised activations, the sorted intermediates,
+ * the expert GEMMs' unit-queue counters (set by each call before use, so the
+ * contents need not be initialised) and, for calls of <= 16 tokens, the
+ * router's partial sums. */
 size_t moe_workspace_bytes(moe_plan_t plan, int32_t m);
 
 /* Forward of the layer for m tokens (page 2, MoeV41::forward: x, m and a
