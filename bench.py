@@ -218,7 +218,7 @@ CONFIG_RUNS = (("decode_bf16", 1, "graph"), ("decode_bf16", 4, "graph"),
                ("skew_fp8", 2048, "eager"))
 # CPU-oracle sample (tokens) and repeats per workload: about 10-30 s of host work
 CPU_SAMPLE = {"decode_bf16": (16, 3), "decode_mxfp4": (16, 3), "decode_mxfp8": (16, 3),
-              "prefill_bf16": (32, 3), "large_fp8": (4, 1), "skew_fp8": (4, 1),
+              "prefill_bf16": (32, 3), "large_fp8": (4, 1), "skew_fp8": (4, 1), "skew_head_fp8": (4, 1),
               "dense_bf16": (8, 1), "dense_fp8": (2, 1), "tiny_f32": (4, 3)}
 
 

@@ -88,12 +88,20 @@ class Workload:
         return "f32" if self.dtype == "f32" else "bf16"
 
 
-# The router sub-seed of the prefill workload and the bias strength of the
-# skewed workload are found by tests/golden/make_workload_params.py (which
+# The router sub-seed of the prefill workload and the bias strengths of the
+# skewed workloads are found by tests/golden/make_workload_params.py (which
 # runs the fp64 oracle's gating) and re-checked by the CPU test suite.
+# skew_fp8: a pure Zipf(1.2) bias whose strength leaves 20 experts without a
+# token (the middle of the range of strengths that do; at its edges one
+# top-k near-tie decides an expert's only token); its busiest expert then
+# takes 3.4 % of the assignments (the > 10 % asked alongside cannot hold
+# with 20 idle experts under a pure Zipf bias).  skew_head_fp8
+# (supplementary): the same bias with a gap below the most popular expert,
+# which gives both (20 idle, top expert > 10 %).
 PREFILL_ROUTER_SUBSEED = 31
-SKEW_ZIPF_HEAD = 0.7
-SKEW_ZIPF_ALPHA = 0.04081156828387305
+SKEW_ZIPF_ALPHA = 0.04326865809483731
+SKEW_HEAD_ZIPF_HEAD = 0.7
+SKEW_HEAD_ZIPF_ALPHA = 0.04088530535399924
 
 WORKLOADS: dict[str, Workload] = {
     # Tiny fp32 layer, softmax top-2 renormalised, no shared expert.
@@ -133,8 +141,13 @@ WORKLOADS: dict[str, Workload] = {
     "skew_fp8": Workload("skew_fp8", m=2048, hidden=7168, experts=256,
                          topk=8, inter=2048, shared_inter=2048, dtype="fp8",
                          gating="sigmoid", routed_scale=2.5, seed=5,
-                         zipf_alpha=SKEW_ZIPF_ALPHA,
-                         zipf_head=SKEW_ZIPF_HEAD),
+                         zipf_alpha=SKEW_ZIPF_ALPHA),
+    # The skewed layer with a hot expert (supplementary load-imbalance case).
+    "skew_head_fp8": Workload("skew_head_fp8", m=2048, hidden=7168, experts=256,
+                              topk=8, inter=2048, shared_inter=2048, dtype="fp8",
+                              gating="sigmoid", routed_scale=2.5, seed=5,
+                              zipf_alpha=SKEW_HEAD_ZIPF_ALPHA,
+                              zipf_head=SKEW_HEAD_ZIPF_HEAD),
 }
 
 

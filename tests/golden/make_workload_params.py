@@ -5,10 +5,12 @@ Runs the fp64 oracle's gating only (no GPU, no HIP library) and prints:
 * the router sub-seed of ``prefill_bf16``: the first r = 0, 1, 2, ... for
   which every expert's token count lies within +-30 % of m*k/E (for m=1024,
   k=8, E=128: [45, 83]);
-* the Zipf bias strength ``alpha`` of ``skew_fp8`` (with its fixed head gap):
-  bisection so that the number of experts receiving no token is as close to
-  20 as the sample allows, then reports the top expert's share of the m*k
-  assignments (required > 10 %).
+* the Zipf bias strength ``alpha`` of ``skew_fp8`` (a pure Zipf(1.2) bias)
+  and of ``skew_head_fp8`` (the same with a fixed gap below the most popular
+  expert): bisection so that the number of experts receiving no token is as
+  close to 20 as the sample allows, then the top expert's share of the m*k
+  assignments (asked > 10 %: skew_fp8 does not reach it, skew_head_fp8
+  does).
 
 The chosen values are written into ``synth/__init__.py`` by hand and
 re-checked by ``tests/test_workloads.py``.
@@ -57,21 +59,29 @@ def prefill_subseed():
     raise SystemExit("no sub-seed found")
 
 
-def skew_alpha():
-    wl = synth.WORKLOADS["skew_fp8"]
+def skew_alpha(name):
+    """The middle of the range of alpha that leaves 20 experts idle (at its
+    edges a near-tie of the top-k decides one expert's only token)."""
+    wl = synth.WORKLOADS[name]
     _, logits = counts_for(wl.replace(zipf_alpha=0.0))
     zeros = lambda a: int((counts_for(wl, alpha=a, logits=logits)[0] == 0).sum())
-    lo, hi = 1e-4, 10.0
-    for _ in range(60):
-        mid = 0.5 * (lo + hi)
-        if zeros(mid) < 20:
-            lo = mid
-        else:
-            hi = mid
-    best = min((abs(zeros(a) - 20), a) for a in (lo, hi))[1]
+
+    def edge(target):   # smallest alpha with at least `target` idle experts
+        lo, hi = 1e-4, 10.0
+        for _ in range(60):
+            mid = 0.5 * (lo + hi)
+            if zeros(mid) < target:
+                lo = mid
+            else:
+                hi = mid
+        return hi
+
+    a20, a21 = edge(20), edge(21)
+    best = 0.5 * (a20 + a21)
+    print(f"{name}: 20 idle experts for alpha in [{a20!r}, {a21!r})")
     c, _ = counts_for(wl, alpha=best, logits=logits)
     share = c.max() / c.sum()
-    print(f"skew_fp8: alpha={best!r} zero-token experts={int((c == 0).sum())} "
+    print(f"{name}: alpha={best!r} zero-token experts={int((c == 0).sum())} "
           f"top share={share:.4f} (top count {c.max()} of {c.sum()})")
     print("histogram (descending):", sorted(c.tolist(), reverse=True))
     return best
@@ -79,4 +89,5 @@ def skew_alpha():
 
 if __name__ == "__main__":
     prefill_subseed()
-    skew_alpha()
+    skew_alpha("skew_fp8")        # pure Zipf(1.2) bias
+    skew_alpha("skew_head_fp8")   # with the head gap

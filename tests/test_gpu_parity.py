@@ -138,20 +138,22 @@ def test_large_fp8_sampled(shard):
 
 @pytest.mark.timeout(600)
 @pytest.mark.parametrize("shard", range(SHARDS))
-def test_skew_fp8_sampled(shard):
-    """Skewed routing: every active expert reached over the shards, and in
-    each shard 16 further tokens of the busiest expert (its rows span several
-    M tiles)."""
-    wl, inp, out, idx, w, dbg = _full_size_run("skew_fp8")
+@pytest.mark.parametrize("name", ["skew_fp8", "skew_head_fp8"])
+def test_skew_fp8_sampled(name, shard):
+    """Skewed routing (pure Zipf, and with a hot expert): every active expert
+    reached over the shards, and in each shard 16 further tokens of the
+    busiest expert (its rows span several M tiles)."""
+    wl, inp, out, idx, w, dbg = _full_size_run(name)
     counts = to_np(dbg["counts"])
     hot = int(np.argmax(counts))
     g_idx = to_np(idx)
     on_hot = np.nonzero((g_idx == hot).any(axis=1))[0]
     rng = np.random.default_rng(100 + shard)
     extra = rng.choice(on_hot, size=min(16, len(on_hot)), replace=False).tolist()
-    _sampled_shard("skew_fp8", shard, extra=extra)
+    _sampled_shard(name, shard, extra=extra)
     assert int((counts == 0).sum()) == 20
-    assert counts.max() / counts.sum() > 0.10
+    if name == "skew_head_fp8":
+        assert counts.max() / counts.sum() > 0.10
 
 
 @pytest.mark.parametrize("name", ["dense_bf16", "dense_fp8"])
